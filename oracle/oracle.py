@@ -1,0 +1,180 @@
+"""ctypes binding of the C oracle (test infrastructure only).
+
+Arrays are numpy; bf16 tensors are passed as their raw uint16 bits.  Every
+function mirrors one in ``fp4_oracle.c`` and returns freshly allocated numpy
+outputs.
+"""
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "fp4_oracle.c")
+LIB = os.path.join(HERE, "libfp4oracle.so")
+
+F32, BF16 = 0, 1
+MX, NV = 0, 1
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force=True):
+    """Compile the oracle with gcc (IEEE semantics: no contraction, no fast-math)."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+            lib = C.CDLL(LIB)
+            i64, i32, u64, vp, dp = C.c_int64, C.c_int, C.c_uint64, C.c_void_p, C.c_double
+            lib.oracle_e2m1_value.argtypes = [i32]; lib.oracle_e2m1_value.restype = dp
+            lib.oracle_e8m0_value.argtypes = [i32]; lib.oracle_e8m0_value.restype = dp
+            lib.oracle_e4m3_value.argtypes = [i32]; lib.oracle_e4m3_value.restype = dp
+            lib.oracle_e4m3_encode.argtypes = [dp]; lib.oracle_e4m3_encode.restype = i32
+            lib.oracle_e2m1_round.argtypes = [dp, i32, C.c_uint, C.POINTER(C.c_int)]
+            lib.oracle_e2m1_round.restype = i32
+            lib.oracle_mx_exponent.argtypes = [dp]; lib.oracle_mx_exponent.restype = i32
+            lib.oracle_philox4x32_10.argtypes = [vp, vp, vp]; lib.oracle_philox4x32_10.restype = None
+            lib.oracle_sr_draw.argtypes = [u64, u64]; lib.oracle_sr_draw.restype = C.c_uint
+            lib.oracle_rht_sign_negative.argtypes = [u64, i64]; lib.oracle_rht_sign_negative.restype = i32
+            lib.oracle_quantize_mx.argtypes = [i64, i64, i64, i32, vp, i32, i32, i32, u64, vp, vp, vp]
+            lib.oracle_quantize_mx.restype = i32
+            lib.oracle_quantize_nv.argtypes = [i64, i64, i64, i32, vp, i32, i32, u64, vp, vp, vp, vp, vp, vp]
+            lib.oracle_quantize_nv.restype = i32
+            lib.oracle_fwht.argtypes = [i64, i64, i64, i32, vp, vp, i64, i32, u64]
+            lib.oracle_fwht.restype = i32
+            lib.oracle_dequantize.argtypes = [i32, i64, i64, i32, vp, vp, vp, i32, vp]
+            lib.oracle_dequantize.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _as_input(x):
+    """Return (array, dtype code) for an fp32 array or a uint16 array of bf16 bits."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16:
+        return x, BF16
+    raise TypeError("oracle input must be float32 or uint16 (bf16 bits), got %s" % x.dtype)
+
+
+def e2m1_value(code):
+    return load().oracle_e2m1_value(int(code))
+
+
+def e8m0_value(b):
+    return load().oracle_e8m0_value(int(b))
+
+
+def e4m3_value(b):
+    return load().oracle_e4m3_value(int(b))
+
+
+def e4m3_encode(t):
+    return load().oracle_e4m3_encode(float(t))
+
+
+def e2m1_round(q, rounding=0, u=0):
+    sat = C.c_int(0)
+    code = load().oracle_e2m1_round(float(q), int(rounding), int(u), C.byref(sat))
+    return code, sat.value
+
+
+def mx_exponent(amax):
+    return load().oracle_mx_exponent(float(amax))
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.zeros(4, np.uint32)
+    load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_draw(seed, i):
+    return load().oracle_sr_draw(int(seed), int(i))
+
+
+def rht_sign_negative(seed, j):
+    return load().oracle_rht_sign_negative(int(seed), int(j))
+
+
+def quantize_mx(x, policy=0, manual_exponent=0, rounding=0, seed=0, cols=None):
+    """x: [rows, stride] float32 or uint16 (bf16 bits); the first ``cols`` columns are quantized."""
+    x, dt = _as_input(x)
+    rows, stride = x.shape
+    cols = stride if cols is None else cols
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    counters = np.zeros(3, np.uint64)
+    rc = load().oracle_quantize_mx(rows, cols, stride, dt, _ptr(x), policy, manual_exponent, rounding,
+                                   seed, _ptr(codes), _ptr(scales), _ptr(counters))
+    if rc != 0:
+        raise ValueError("oracle_quantize_mx rejected the arguments")
+    return codes, scales, counters
+
+
+def quantize_nv(x, policy=2, rounding=0, seed=0, global_amax=None, cols=None):
+    """x: [rows, stride] float32 or uint16 (bf16 bits); the first ``cols`` columns are quantized."""
+    x, dt = _as_input(x)
+    rows, stride = x.shape
+    cols = stride if cols is None else cols
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    gs = np.zeros(1, np.float32)
+    nblk = rows * (cols // 16)
+    choice = np.zeros((nblk + 7) // 8, np.uint8) if policy == 3 else None
+    counters = np.zeros(3, np.uint64)
+    ga = None if global_amax is None else np.array([global_amax], np.float32)
+    rc = load().oracle_quantize_nv(rows, cols, stride, dt, _ptr(x), policy, rounding, seed, _ptr(ga),
+                                   _ptr(codes), _ptr(scales), _ptr(gs), _ptr(choice), _ptr(counters))
+    if rc != 0:
+        raise ValueError("oracle_quantize_nv rejected the arguments")
+    return codes, scales, gs[0], choice, counters
+
+
+def fwht(x, t=None, random_signs=False, seed=0):
+    """Normalised Walsh-Hadamard transform of each t-chunk of each row (fp64 out)."""
+    x, dt = _as_input(x)
+    rows, d = x.shape
+    t = d if t is None else t
+    y = np.zeros((rows, d), np.float64)
+    rc = load().oracle_fwht(rows, d, d, dt, _ptr(x), _ptr(y), t, int(bool(random_signs)), seed)
+    if rc != 0:
+        raise ValueError("oracle_fwht rejected the arguments")
+    return y
+
+
+def dequantize(fmt, codes, scales, global_scale=None, out_dtype=F32):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    cols = codes.shape[1] * 2
+    block = 32 if fmt == MX else 16
+    gs = None if global_scale is None else np.array([global_scale], np.float32)
+    out = np.zeros((rows, cols), np.float32 if out_dtype == F32 else np.uint16)
+    rc = load().oracle_dequantize(fmt, rows, cols, block, _ptr(codes), _ptr(scales), _ptr(gs),
+                                  out_dtype, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_dequantize rejected the arguments")
+    return out

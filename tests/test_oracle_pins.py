@@ -1,0 +1,529 @@
+"""Pins for the CPU oracle: each test checks the oracle against something
+other than itself -- values the pages print (tests/golden), library
+routines (torch float8 decodes and casts, scipy's Hadamard matrix, rocRAND's
+Philox), closed forms, invariants, and an exact-rational brute force."""
+import math
+import os
+import shutil
+import subprocess
+from fractions import Fraction as Fr
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_ref as X
+from conftest import golden
+from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+
+
+def codes_of(packed):
+    return X.unpack_codes(packed)
+
+
+# ---------------------------------------------------------------- formats
+def test_e2m1_lattice_matches_page():
+    g = golden("e2m1_lattice.json")
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    assert vals[:8] == g["magnitudes"]
+    for c in range(8):
+        assert vals[8 + c] == -g["magnitudes"][c]
+        assert math.copysign(1.0, vals[8 + c]) == -1.0   # signed zero included
+    assert len(set((v, math.copysign(1, v)) for v in vals)) == g["finite_codes"]
+    assert oracle.e2m1_value(1) == g["subnormal_point"]
+
+
+def test_exec_bit_identity_all_codes():
+    """metrale 'hardware::exec': the masked shift maps every E2M1 code to an
+    E4M3 byte worth value * 2^-6 (torch decodes the E4M3 bytes)."""
+    g = golden("exec_e2m1_to_e4m3.json")
+    for base in range(0, 16, 4):
+        codes = [base + i for i in range(4)]
+        q = 0
+        for i, c in enumerate(codes):
+            q |= (c << 4) << (8 * i)
+        w = (q & g["sign_mask"]) | ((q & g["magnitude_mask"]) >> g["shift"])
+        b = torch.tensor([(w >> (8 * i)) & 0xFF for i in range(4)], dtype=torch.uint8)
+        dec = b.view(torch.float8_e4m3fn).double().tolist()
+        for c, d in zip(codes, dec):
+            want = oracle.e2m1_value(c) * 2.0 ** g["value_factor_log2"]
+            assert d == want and math.copysign(1, d) == math.copysign(1, want), (c, d, want)
+
+
+def test_e8m0_decode_and_limits():
+    g = golden("e8m0_limits.json")
+    t = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).double()
+    for b in range(255):
+        assert oracle.e8m0_value(b) == t[b].item() == 2.0 ** (b - g["bias"])
+    assert math.isnan(oracle.e8m0_value(g["nan_byte"]))
+    assert oracle.mx_exponent(3.0e38) <= g["exponent_max"]
+    assert oracle.mx_exponent(2.0 ** -140) == g["exponent_min"]
+    for e, byte in ((g["exponent_min"], g["byte_of_min"]), (g["exponent_max"], g["byte_of_max"])):
+        x = np.zeros((1, 32), np.float32)
+        _, s, _ = oracle.quantize_mx(x, policy=1, manual_exponent=e)
+        assert int(s[0, 0]) == byte
+
+
+def test_mx_never_produces_nan_scale_for_finite_input():
+    rng = np.random.default_rng(7)
+    e = rng.integers(-149, 128, size=(64, 256))
+    m = rng.uniform(1, 2, size=(64, 256)) * rng.choice([-1, 1], size=(64, 256))
+    x = np.ldexp(m, e).astype(np.float32)
+    x[~np.isfinite(x)] = 1.0
+    _, s, _ = oracle.quantize_mx(x)
+    assert s.max() <= 254
+
+
+def test_bits_per_value_closed_form():
+    g = golden("bits_per_value.json")
+    assert g["block_size"] * g["element_bits"] + g["scale_bits"] == g["block_bits"]
+    x = np.ones((4, 256), np.float32)
+    c, s, _ = oracle.quantize_mx(x)
+    assert (c.nbytes + s.nbytes) * 8 / x.size == g["bits_per_value"]
+    c, s, gs, _, _ = oracle.quantize_nv(x)
+    assert (c.nbytes + s.nbytes) * 8 / x.size == 4.5   # 16 x 4 + 8 bits per 16 values
+
+
+# ---------------------------------------------------------------- page fixtures
+def test_worked_block():
+    g = golden("mx_worked_block.json")
+    x = np.zeros((1, 32), np.float32)
+    for i, el in enumerate(g["elements"]):
+        x[0, i] = el["source"]
+    c, s, cnt = oracle.quantize_mx(x)
+    assert int(s[0, 0]) - 127 == g["exponent"]
+    assert oracle.e8m0_value(int(s[0, 0])) == g["scale"]
+    d = oracle.dequantize(oracle.MX, c, s)
+    codes = codes_of(c)
+    for i, el in enumerate(g["elements"]):
+        assert d[0, i] == el["reconstructed"]
+        assert oracle.e2m1_value(codes[0, i]) == pytest.approx(el["normalised"], abs=0.5) or el["saturated"]
+    assert cnt[0] == sum(el["saturated"] for el in g["elements"])
+    assert cnt[1] == sum(el["underflowed"] for el in g["elements"])
+
+
+def test_outlier_fixtures():
+    g = golden("mx_outlier_fixtures.json")
+    for fx in g["fixtures"]:
+        vals = (g["pattern"] * 4)[:31] + [fx["last"]]
+        x = np.array([vals], np.float32)
+        c, s, cnt = oracle.quantize_mx(x)
+        d = oracle.dequantize(oracle.MX, c, s).astype(np.float64)
+        err = d - x
+        assert int(s[0, 0]) - 127 == fx["exponent"]
+        assert d[0, -1] == fx["last_reconstructed"]
+        assert int((d == 0).sum()) == fx["zeros"]
+        assert np.abs(err).max() == fx["max_abs_error"]
+        assert round(float(np.sqrt((err ** 2).mean())), g["rmse_printed_decimals"]) == fx["rmse"]
+
+
+# ---------------------------------------------------------------- OCP exponent
+def test_ocp_exponent_matches_integer_search():
+    rng = np.random.default_rng(11)
+    amaxes = [0.0, 4.0, 4.0 * (1 - 2 ** -24), 8.0, 13.0, 6.0, 2.0 ** -149, 2.0 ** -126, 3.4e38,
+              2.0 ** -125, 2.0 ** -124 * 1.5, 2.0 ** 127, 2.0 ** 128 * (1 - 2 ** -24)]
+    amaxes += [float(np.float32(v)) for v in np.ldexp(rng.uniform(1, 2, 300), rng.integers(-149, 128, 300))]
+    for k in range(-130, 130, 3):
+        for f in (1.0, 1.0 - 2 ** -24, 1.0 + 2 ** -23):
+            v = 4.0 * 2.0 ** k * f
+            if 2.0 ** -149 <= v < 3.4e38 and float(np.float32(v)) == v:
+                amaxes.append(v)
+    for a in amaxes:
+        assert oracle.mx_exponent(a) == X.ocp_exponent(a), a
+
+
+# ---------------------------------------------------------------- MX brute force
+def _mx_cases():
+    rng = np.random.default_rng(5)
+    blocks = []
+    # random t-distributed, various magnitudes
+    for sc in (1e-3, 1.0, 37.0, 1e5):
+        blocks.append(rng.standard_t(3, 32) * sc)
+    # exact ties and lattice points at several exponents
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 6.5, 7.0, 0.5, 4.0]
+    for e in (-3, 0, 2, 9):
+        b = np.array([m * 2.0 ** e * s for m in mids for s in (1, -1)] + [0.0] * 8)
+        b[-1] = 7.9 * 2.0 ** e  # sets amax so that the exponent is e
+        blocks.append(b)
+    # signed zeros and underflows
+    b = np.zeros(32); b[0] = 100.0; b[1] = -0.0; b[2] = -0.3; b[3] = 0.3; b[4] = 1e-30
+    blocks.append(b)
+    # subnormal and tiny blocks (exponent clamps at -127)
+    blocks.append(np.ldexp(rng.uniform(-1, 1, 32), -140))
+    blocks.append(np.ldexp(rng.uniform(-1, 1, 32), -127))
+    # huge block
+    blocks.append(np.ldexp(rng.uniform(-1, 1, 32), 127))
+    x = np.stack(blocks).astype(np.float32)
+    return x.reshape(-1, 64) if len(blocks) % 2 == 0 else x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_quantize_matches_exact_bruteforce(dtype):
+    x32 = _mx_cases()
+    xin = f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+    xv = bf16_bits_to_f32(xin).astype(np.float64) if dtype == "bf16" else x32.astype(np.float64)
+    c, s, cnt = oracle.quantize_mx(xin)
+    rc, rs, rcnt = X.mx_quantize(xv)
+    assert np.array_equal(codes_of(c), rc)
+    assert np.array_equal(s.astype(np.int64), rs)
+    assert [int(cnt[0]), int(cnt[1])] == rcnt
+
+
+def test_mx_stochastic_matches_exact_bruteforce():
+    x = _mx_cases()
+    seed = 0x1234_5678_9ABC
+    draws = np.array([[oracle.sr_draw(seed, r * x.shape[1] + i) for i in range(x.shape[1])]
+                      for r in range(x.shape[0])])
+    c, s, cnt = oracle.quantize_mx(x, rounding=1, seed=seed)
+    rc, rs, rcnt = X.mx_quantize(x.astype(np.float64), rounding=1, draws=draws)
+    assert np.array_equal(codes_of(c), rc)
+    assert np.array_equal(s.astype(np.int64), rs)
+    assert [int(cnt[0]), int(cnt[1])] == rcnt
+
+
+def test_mx_strided_input():
+    x = np.random.default_rng(3).standard_normal((5, 96)).astype(np.float32)
+    c, s, _ = oracle.quantize_mx(x, cols=64)
+    c2, s2, _ = oracle.quantize_mx(np.ascontiguousarray(x[:, :64]))
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+# ---------------------------------------------------------------- E4M3 scale
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(9)
+    ts = list(np.ldexp(rng.uniform(1, 2, 4000), rng.integers(-12, 9, 4000)).astype(np.float32))
+    for b in range(0x7E):   # every midpoint between neighbouring codes, and neighbours of it
+        lo, hi = X.e4m3_byte_value(b), X.e4m3_byte_value(b + 1)
+        m = np.float32((lo + hi) / 2)
+        ts += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9)), np.float32(lo)]
+    ts += [np.float32(0), np.float32(2 ** -10), np.float32(448)]
+    ts = [t for t in ts if 0 <= t <= 448]
+    tt = torch.tensor(np.array(ts, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    for t, want in zip(ts, tt.tolist()):
+        assert oracle.e4m3_encode(float(t)) == want, t
+    for t in (448.0001, 460.0, 464.0, 500.0, 1e30):
+        assert oracle.e4m3_encode(t) == 0x7E          # saturation (reading R-11)
+    for b in range(256):
+        want = X.e4m3_byte_value(b)
+        got = oracle.e4m3_value(b)
+        assert (math.isnan(want) and math.isnan(got)) or want == got
+
+
+# ---------------------------------------------------------------- NV brute force
+def _nv_cases():
+    rng = np.random.default_rng(21)
+    rows = []
+    # amax 2688 makes g = 1 exactly; the block max 9 gives s = 1.5, then
+    # elements at M * 1.5 are exact nearest-even ties.
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
+    r0 = np.zeros(64)
+    r0[0] = 2688.0
+    r0[16:32] = [9.0] + [m * 1.5 for m in mids] + [-m * 1.5 for m in mids[:7]]
+    r0[32:48] = rng.standard_t(4, 16) * 3
+    r0[48:64] = rng.standard_t(4, 16) * 1e-4      # tiny block: subnormal / zero E4M3 scale
+    rows.append(r0)
+    for sc in (1.0, 1e-3, 50.0):
+        rows.append(rng.standard_t(4, 64) * sc)
+    r = rng.standard_normal(64)
+    r[5] = -0.0
+    rows.append(r)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nv_quantize_matches_exact_bruteforce(dtype):
+    x32 = _nv_cases()
+    xin = f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+    xv = bf16_bits_to_f32(xin).astype(np.float64) if dtype == "bf16" else x32.astype(np.float64)
+    c, s, g, _, cnt = oracle.quantize_nv(xin)
+    rc, rs, rg, rcnt = X.nv_quantize(xv)
+    assert g == rg
+    assert np.array_equal(s.astype(np.int64), rs)
+    assert np.array_equal(codes_of(c), rc)
+    assert [int(cnt[0]), int(cnt[1])] == rcnt
+
+
+def test_nv_exact_ties_resolve_to_even():
+    x = _nv_cases()[:1]
+    c, s, g, _, _ = oracle.quantize_nv(x)
+    assert g == 1.0 and oracle.e4m3_value(int(s[0, 1])) == 1.5
+    got = codes_of(c)[0, 17:25]
+    # M -> lower even code for 0.25, 1.25, 2.5, 5; upper for 0.75, 1.75, 3.5; 6 exact
+    assert list(got) == [0, 2, 2, 4, 4, 6, 6, 7]
+
+
+def test_nv_caller_amax_and_saturation():
+    x = _nv_cases()
+    c, s, g, _, cnt = oracle.quantize_nv(x, global_amax=1.0)
+    rcodes, rs, rg, rcnt = X.nv_quantize(x.astype(np.float64), divisor=2688)  # for shape only
+    assert g == np.float32(1.0) / np.float32(2688)
+    assert s.max() == 0x7E and cnt[0] > 0
+
+
+def test_nv_stochastic_matches_exact_bruteforce():
+    x = _nv_cases()
+    seed = 0x5EED
+    draws = np.array([[oracle.sr_draw(seed, r * x.shape[1] + i) for i in range(x.shape[1])]
+                      for r in range(x.shape[0])])
+    c, s, g, _, cnt = oracle.quantize_nv(x, rounding=1, seed=seed)
+    rc, rs, rg, rcnt = X.nv_quantize(x.astype(np.float64), rounding=1, draws=draws)
+    assert np.array_equal(s.astype(np.int64), rs)
+    assert np.array_equal(codes_of(c), rc)
+    assert [int(cnt[0]), int(cnt[1])] == rcnt
+
+
+def test_nv_invariants_on_heavy_tailed_tensor():
+    x = (2 * np.random.default_rng(2).standard_t(4, (64, 512))).astype(np.float32)
+    c, s, g, _, _ = oracle.quantize_nv(x)
+    codes = codes_of(c).reshape(64, 32, 16)
+    xb = np.abs(x).reshape(64, 32, 16)
+    amax = np.abs(x).max()
+    assert g == np.float32(amax) / np.float32(2688)
+    # the block holding the tensor max gets the largest scale byte 0x7E (448)
+    r, b = np.unravel_index(np.argmax(xb.max(axis=2)), xb.shape[:2])
+    assert s[r, b] == 0x7E
+    # with a normal E4M3 scale the block max lands in (5, 6.4] -> magnitude code 7
+    for r in range(64):
+        for b in range(32):
+            if s[r, b] >= 8:
+                k = int(np.argmax(xb[r, b]))
+                assert codes[r, b, k] & 7 == 7
+
+
+# ---------------------------------------------------------------- Four Over Six
+def _exact_sse(xs, codes, sb, g):
+    sc = Fr(X.e4m3_byte_value(sb)) * Fr(float(g))
+    return sum((Fr(float(v)) - X.E2M1[c] * sc) ** 2 for v, c in zip(xs, codes))
+
+
+def test_four_over_six_choice_and_invariants():
+    rng = np.random.default_rng(4)
+    x = rng.normal(0, 0.02, (8, 256))
+    x.reshape(-1)[rng.choice(x.size, 3, replace=False)] *= 20
+    x[0, :16] = 0.0                                  # all-zero block keeps max->6
+    x = bf16_bits_to_f32(f32_to_bf16_bits(x.astype(np.float32)))
+    c, s, g, choice, cnt = oracle.quantize_nv(x, policy=3)
+    assert g == np.float32(np.abs(x).max()) / np.float32(1792)
+    bits = np.unpackbits(choice, bitorder="little")[: x.size // 16].reshape(8, 16)
+    assert bits[0, 0] == 0
+    codes = codes_of(c)
+    agree = 0
+    for r in range(8):
+        for b in range(16):
+            xs = x[r, b * 16:(b + 1) * 16].astype(np.float64)
+            bam = Fr(float(np.abs(xs).max()))
+            s6 = X.e4m3_nearest(bam / (6 * Fr(float(g))))
+            s4 = X.e4m3_nearest(bam / (4 * Fr(float(g))))
+            c6 = [X.nearest_code(v, Fr(X.e4m3_byte_value(s6)) * Fr(float(g)))[0] if s6 else (8 if np.signbit(v) else 0) for v in xs]
+            c4 = [X.nearest_code(v, Fr(X.e4m3_byte_value(s4)) * Fr(float(g)))[0] if s4 else (8 if np.signbit(v) else 0) for v in xs]
+            e6, e4 = _exact_sse(xs, c6, s6, g), _exact_sse(xs, c4, s4, g)
+            got = list(codes[r, b * 16:(b + 1) * 16])
+            if bits[r, b]:
+                assert got == c4 and s[r, b] == s4
+                if s4 >= 8:
+                    assert max(cc & 7 for cc in got) <= 6   # max->4 never emits +-6
+            else:
+                assert got == c6 and s[r, b] == s6
+            if e6 == e4 or abs(e6 - e4) <= Fr(1, 10 ** 5) * max(e6, e4):
+                continue                             # near-tie: the frozen fp32 order decides
+            assert bool(bits[r, b]) == (e4 < e6)
+            agree += 1
+    assert agree > 100
+
+
+# ---------------------------------------------------------------- FWHT / RHT
+def test_fwht_matches_dense_hadamard():
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(8)
+    for d in (2, 4, 16, 64, 256, 1024):
+        x = rng.standard_normal((3, d)).astype(np.float32)
+        y = oracle.fwht(x)
+        want = x.astype(np.float64) @ hadamard(d).astype(np.float64) / np.sqrt(d)
+        np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x.astype(np.float64), axis=1), rtol=1e-12)
+        z = oracle.fwht(y.astype(np.float32))           # (H/sqrt d)^2 = I
+        np.testing.assert_allclose(z, x, rtol=1e-6, atol=1e-6)
+    # per-16 chunks = block-diagonal H16 / 4
+    x = rng.standard_normal((2, 64)).astype(np.float32)
+    y = oracle.fwht(x, t=16)
+    H = hadamard(16).astype(np.float64) / 4.0
+    for k in range(4):
+        np.testing.assert_allclose(y[:, 16 * k:16 * k + 16], x[:, 16 * k:16 * k + 16] @ H, rtol=1e-13, atol=1e-13)
+
+
+def test_fwht_orthogonal_invariance():
+    rng = np.random.default_rng(10)
+    Xm = rng.standard_normal((4, 128)).astype(np.float32)
+    W = rng.standard_normal((6, 128)).astype(np.float32)
+    lhs = oracle.fwht(Xm) @ oracle.fwht(W).T
+    np.testing.assert_allclose(lhs, Xm.astype(np.float64) @ W.astype(np.float64).T, rtol=1e-10, atol=1e-10)
+
+
+def test_fwht_spike_damping():
+    from scipy.linalg import hadamard
+    g = golden("fwht_spike.json")
+    d = g["d"]
+    k = 3001
+    x = np.zeros((1, d), np.float32)
+    x[0, k] = g["spike"]
+    y = oracle.fwht(x)
+    assert np.allclose(np.abs(y), g["spike"] / math.sqrt(d), rtol=1e-14)
+    assert round(g["spike"] / np.abs(y).max(), g["damping_printed_decimals"]) == g["damping"]
+    row = hadamard(d, dtype=np.int8)[k]
+    assert np.array_equal(np.sign(y[0]).astype(np.int8), row)
+
+
+def test_rht16_matches_dense():
+    from scipy.linalg import hadamard
+    seed = 0x5EED
+    sig = np.array([-1.0 if oracle.rht_sign_negative(seed, j) else 1.0 for j in range(16)])
+    assert 0 < (sig < 0).sum() < 16
+    x = np.random.default_rng(12).laplace(0, 1e-3, (4, 64)).astype(np.float32)
+    y = oracle.fwht(x, t=16, random_signs=True, seed=seed)
+    M = np.diag(sig) @ hadamard(16).astype(np.float64) / 4.0
+    for k in range(4):
+        np.testing.assert_allclose(y[:, 16 * k:16 * k + 16], x[:, 16 * k:16 * k + 16].astype(np.float64) @ M,
+                                   rtol=1e-13, atol=1e-20)
+        np.testing.assert_allclose(np.linalg.norm(y[:, 16 * k:16 * k + 16], axis=1),
+                                   np.linalg.norm(x[:, 16 * k:16 * k + 16].astype(np.float64), axis=1), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- Philox / SR
+ROCRAND_PROBE = r"""
+#include <cstdio>
+#include <cstdlib>
+#include <rocrand/rocrand_philox4x32_10.h>
+struct eng : rocrand_device::philox4x32_10_engine {
+  uint4 run(uint4 c, uint2 k) { return ten_rounds(c, k); }
+};
+int main(int argc, char** argv) {
+  eng e; uint4 c; uint2 k;
+  c.x = strtoul(argv[1], 0, 0); c.y = strtoul(argv[2], 0, 0); c.z = strtoul(argv[3], 0, 0); c.w = strtoul(argv[4], 0, 0);
+  k.x = strtoul(argv[5], 0, 0); k.y = strtoul(argv[6], 0, 0);
+  uint4 r = e.run(c, k);
+  printf("%u %u %u %u\n", r.x, r.y, r.z, r.w);
+  return 0;
+}
+"""
+
+
+def test_philox_matches_rocrand(tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"):
+        pytest.skip("rocRAND header / hipcc not available")
+    src = tmp_path / "p.cpp"
+    src.write_text(ROCRAND_PROBE)
+    exe = tmp_path / "p"
+    subprocess.run([hipcc, "-x", "hip", "--offload-arch=gfx950", "-O1", str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    cases = [((0, 0, 0, 0), (0, 0)), ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2),
+             ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0)),
+             ((7, 0, 0, 0), (0x5EED, 0)), ((0, 0, 1, 0), (0x5EED, 0)), ((123456, 1, 0, 0), (0xDEADBEEF, 0x12345))]
+    for ctr, key in cases:
+        out = subprocess.run([str(exe)] + [str(v) for v in ctr + key], check=True, capture_output=True, text=True)
+        want = [int(v) for v in out.stdout.split()]
+        assert list(oracle.philox4x32_10(ctr, key)) == want, (ctr, key)
+
+
+def test_sr_draw_layout():
+    seed = 0x0123456789ABCDEF
+    for g in (0, 1, 77, 2 ** 33 + 5):
+        out = oracle.philox4x32_10((g & 0xFFFFFFFF, g >> 32, 0, 0), (seed & 0xFFFFFFFF, seed >> 32))
+        for f in range(8):
+            assert oracle.sr_draw(seed, 8 * g + f) == (int(out[f >> 1]) >> (16 * (f & 1))) & 0xFFFF
+    out = oracle.philox4x32_10((0, 0, 1, 0), (seed & 0xFFFFFFFF, seed >> 32))
+    for j in range(16):
+        assert oracle.rht_sign_negative(seed, j) == (int(out[0]) >> j) & 1
+
+
+def test_sr_unbiased_and_lattice_fixed():
+    seed = 99
+    for q in (0.1, 0.3, 0.9, 1.3, 2.2, 3.7, 5.5):
+        n = 20000
+        vals = []
+        for i in range(n):
+            c, _ = oracle.e2m1_round(q, 1, oracle.sr_draw(seed, i))
+            vals.append(oracle.e2m1_value(c))
+        vals = np.array(vals)
+        lo, hi = vals.min(), vals.max()
+        p = (q - lo) / (hi - lo)
+        sigma = (hi - lo) * math.sqrt(p * (1 - p) / n)
+        assert abs(vals.mean() - q) < 4 * sigma + (hi - lo) * 2 ** -16
+    for k in range(16):
+        v = oracle.e2m1_value(k)
+        for u in (0, 1, 32767, 65535):
+            assert oracle.e2m1_round(v, 1, u)[0] == k
+    assert oracle.e2m1_round(6.5, 1, 0) == (7, 1)
+    assert oracle.e2m1_round(-1.3, 1, 0)[0] == 8 | 3
+
+
+# ---------------------------------------------------------------- dequantize
+def test_dequantize_mx_exact():
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 256, (4, 32), dtype=np.uint8)
+    scales = rng.integers(0, 255, (4, 2), dtype=np.uint8)
+    scales[0, 0] = 0; scales[0, 1] = 254; scales[1, 0] = 255
+    for od in (oracle.F32, oracle.BF16):
+        out = oracle.dequantize(oracle.MX, codes, scales, out_dtype=od)
+        outf = out if od == oracle.F32 else bf16_bits_to_f32(out)
+        cc = codes_of(codes)
+        for r in range(4):
+            for i in range(64):
+                sb = int(scales[r, i // 32])
+                if sb == 255:
+                    assert np.isnan(outf[r, i])
+                    continue
+                want = X.E2M1[cc[r, i]] * Fr(2) ** (sb - 127)
+                got = outf[r, i]
+                if abs(want) > Fr(3.4028234663852886e38):
+                    assert np.isinf(got)
+                else:
+                    assert Fr(float(got)) == want
+                    assert np.signbit(got) == bool(cc[r, i] & 8)
+
+
+def test_dequantize_nv_single_rounding():
+    rng = np.random.default_rng(14)
+    codes = rng.integers(0, 256, (6, 32), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (6, 4), dtype=np.uint8)
+    scales[0, 0] = 0x7F
+    for g in (np.float32(0.0123456), np.float32(1.0) / np.float32(2688), np.float32(3.3e-20)):
+        o32 = oracle.dequantize(oracle.NV, codes, scales, global_scale=g, out_dtype=oracle.F32)
+        o16 = bf16_bits_to_f32(oracle.dequantize(oracle.NV, codes, scales, global_scale=g, out_dtype=oracle.BF16))
+        cc = codes_of(codes)
+        for r in range(6):
+            for i in range(64):
+                sb = int(scales[r, i // 16])
+                if sb == 0x7F:
+                    assert np.isnan(o32[r, i]) and np.isnan(o16[r, i])
+                    continue
+                exact = X.E2M1[cc[r, i]] * Fr(X.e4m3_byte_value(sb)) * Fr(float(g))
+                assert o32[r, i] == np.float32(float(exact))   # exact fits in fp64: one rounding
+                assert Fr(float(o16[r, i])) == X.round_to_bf16_exact(exact)
+
+
+# ---------------------------------------------------------------- non-finite
+def test_nonfinite_blocks():
+    x = np.random.default_rng(15).standard_normal((2, 64)).astype(np.float32)
+    x[0, 3] = np.nan
+    x[1, 40] = np.inf
+    x[1, 41] = -np.inf
+    c, s, cnt = oracle.quantize_mx(x)
+    assert s[0, 0] == 0xFF and s[1, 1] == 0xFF and s[0, 1] != 0xFF
+    assert codes_of(c)[0, :32].max() == 0 and codes_of(c)[1, 32:].max() == 0
+    assert cnt[2] == 3
+    c, s, g, _, cnt = oracle.quantize_nv(x)
+    assert s[0, 0] == 0x7F and s[1, 2] == 0x7F and cnt[2] == 3
+    finite = x[np.isfinite(x)]
+    assert g == np.float32(np.abs(finite).max()) / np.float32(2688)
+    d = oracle.dequantize(oracle.NV, c, s, global_scale=g)
+    assert np.isnan(d[0, :16]).all() and np.isfinite(d[0, 16:]).all()
+
+
+# ---------------------------------------------------------------- inputs
+def test_bf16_cast_matches_torch():
+    x = np.random.default_rng(16).standard_normal(100000).astype(np.float32) * 1e3
+    x[:4] = [np.inf, -np.inf, 3.4e38, -0.0]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(f32_to_bf16_bits(x), want)
