@@ -1,0 +1,128 @@
+// fp4q_dequant.hip -- reconstruction of MXFP4 / NVFP4 tensors on gfx950.
+//
+// "MXFP4 Quantization: Audit the 4.25-Bit Blocks", "Encode one MXFP4 block
+// step by step": a code reconstructs as its lattice value times the block
+// scale.  MX: value * 2^(b-127), exact in fp32 and bf16 -- done by the gfx950
+// scaled FP4 -> fp32/bf16 conversions, whose scale operand is the E8M0 byte.
+// NV ("Sub-4-Bit Microscaling", section 2): value * s * g.  value * s is exact
+// in fp32; the product with g is rounded once: for fp32 output by the fp32
+// multiply, for bf16 output by rounding the fp32 product to nearest-even and,
+// when that product sits exactly on a bf16 rounding boundary, deciding with
+// the exact fp64 product (value * s * g has <= 31 significant bits).
+#include "fp4q_flat.h"
+
+namespace fp4q {
+namespace {
+
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ uint32_t bf16_of_product(float vs, float g) {
+  const float a = fabsf(vs) * g;
+  const uint32_t b = as_u(a);
+  uint32_t r;
+  if ((b & 0xFFFFu) == 0x8000u) {
+    const double ex = (double)fabsf(vs) * (double)g;
+    const double ad = (double)a;
+    const uint32_t hi = b >> 16;
+    r = (ex > ad) ? hi + 1u : (ex < ad) ? hi : hi + (hi & 1u);
+  } else {
+    r = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  }
+  return r | ((as_u(vs) >> 31) << 15);
+}
+
+template <int FMT, int OUT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int64_t nslots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t ntiles = (nslots + 63) >> 6;
+  float g = 1.0f;
+  if constexpr (FMT == 1) g = *d.global_scale;
+  const float one = e8m0_operand(127u);
+  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+    uint32_t cw[kUnroll], sb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
+      const bool act = (t0 + u * nwaves) < ntiles && s < nslots;
+      cw[u] = act ? *reinterpret_cast<const uint32_t*>(d.codes + (s << 2)) : 0u;
+      sb[u] = act ? (uint32_t)d.scales[FMT == 0 ? (s >> 2) : (s >> 1)] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t t = t0 + u * nwaves;
+      if (t >= ntiles) break;
+      const int64_t s = (t << 6) + lane;
+      if (s >= nslots) continue;
+      if constexpr (FMT == 0) {
+        const bool nan = sb[u] == 255u;
+        const float sc = e8m0_operand(sb[u]);
+        if constexpr (OUT == kF32) {
+          float o[8];
+          float2_t p;
+          p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], sc, 0); o[0] = p.x; o[1] = p.y;
+          p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], sc, 1); o[2] = p.x; o[3] = p.y;
+          p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], sc, 2); o[4] = p.x; o[5] = p.y;
+          p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], sc, 3); o[6] = p.x; o[7] = p.y;
+          if (nan) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = as_f(0x7FC00000u);
+          }
+          store_rotated(static_cast<float*>(d.out), s, o);
+        } else {
+          uint4 o;
+          o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 0));
+          o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 1));
+          o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 2));
+          o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 3));
+          if (nan) o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + (s << 3)) = o;
+        }
+      } else {
+        const bool nan = sb[u] == 0x7Fu || sb[u] == 0xFFu;
+        const float sd = e4m3_value(sb[u] & 0x7Fu);
+        float val[8];
+        float2_t p;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], one, 0); val[0] = p.x; val[1] = p.y;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], one, 1); val[2] = p.x; val[3] = p.y;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], one, 2); val[4] = p.x; val[5] = p.y;
+        p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], one, 3); val[6] = p.x; val[7] = p.y;
+        if constexpr (OUT == kF32) {
+          float o[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = nan ? as_f(0x7FC00000u) : (val[i] * sd) * g;
+          store_rotated(static_cast<float*>(d.out), s, o);
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) h[i] = nan ? 0x7FC0u : bf16_of_product(val[i] * sd, g);
+          const uint4 o = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                     h[6] | (h[7] << 16));
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + (s << 3)) = o;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int OUT>
+hipError_t launch_t(const DequantLaunch& d, hipStream_t st) {
+  const int64_t nslots = d.rows * d.cols / 8;
+  const int64_t ntiles = (nslots + 63) >> 6;
+  const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+  hipLaunchKernelGGL((dequant_kernel<FMT, OUT>), dim3(grid), dim3(kThreads), 0, st, d, nslots);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const DequantLaunch& d, hipStream_t st) {
+  if (d.rows == 0 || d.cols == 0) return hipSuccess;
+  if (d.format == 0) return d.out_dtype == kF32 ? launch_t<0, kF32>(d, st) : launch_t<0, kBF16>(d, st);
+  return d.out_dtype == kF32 ? launch_t<1, kF32>(d, st) : launch_t<1, kBF16>(d, st);
+}
+
+}  // namespace fp4q

@@ -1,0 +1,163 @@
+// fp4q_flat.h -- slot loading and the 16-point random Hadamard transform for
+// the flat (elementwise) kernels.  A slot is 8 consecutive elements of one
+// row; slot s covers flat elements 8s .. 8s+7 (flat index r*cols + c).  Lane
+// l of a wave works on slot 64*t + l of wave-tile t, so a 16-block spans a
+// lane pair and a 32-block a lane quad.
+#pragma once
+
+#include "fp4q_common.h"
+#include "fp4q_internal.h"
+
+namespace fp4q {
+
+template <int IN>
+struct SlotRaw {
+  uint32_t w[IN == kF32 ? 8 : 4];
+};
+
+template <bool CONTIG>
+__device__ __forceinline__ int64_t slot_in_offset(int64_t s, int64_t cols, int64_t stride) {
+  const int64_t f = s << 3;
+  if (CONTIG) return f;
+  const int64_t r = f / cols;
+  return r * stride + (f - r * cols);
+}
+
+template <int IN, bool CONTIG>
+__device__ __forceinline__ void load_slot(const QuantLaunch& q, int64_t s, bool active, SlotRaw<IN>& r) {
+  if (!active) {
+#pragma unroll
+    for (int i = 0; i < (IN == kF32 ? 8 : 4); ++i) r.w[i] = 0u;
+    return;
+  }
+  const int64_t off = slot_in_offset<CONTIG>(s, q.cols, q.stride);
+  if constexpr (IN == kF32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(q.x) + off);
+    const uint4 a = p[0], b = p[1];
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + off);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  }
+}
+
+template <int IN>
+__device__ __forceinline__ void widen_slot(const SlotRaw<IN>& r, float v[8]) {
+  if constexpr (IN == kF32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = as_f(r.w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf_lo(r.w[i]);
+      v[2 * i + 1] = bf_hi(r.w[i]);
+    }
+  }
+}
+
+// 16-point random Hadamard transform of the 16-block held by a lane pair:
+// y = (sigma * x) H16 / 4, natural order.  Butterfly stages h = 1, 2, 4 run in
+// registers, h = 8 between the two lanes (the even lane holds positions 0..7).
+// Sign flips and the final x0.25 are exact.
+__device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool odd_lane) {
+  const uint32_t sg = odd_lane ? (signs16 >> 8) : signs16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = as_f(as_u(v[i]) ^ (((sg >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = dpp_xor1_f(v[i]);
+    v[i] = odd_lane ? (p - v[i]) : (v[i] + p);
+    v[i] *= 0.25f;
+  }
+}
+
+__device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float v[8]) {
+  float4* p = reinterpret_cast<float4*>(rot + (s << 3));
+  p[0] = make_float4(v[0], v[1], v[2], v[3]);
+  p[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ void flush_counters(unsigned long long* c, uint32_t sat, uint32_t und, uint32_t nf) {
+  const unsigned long long a = wave_sum_u64(sat), b = wave_sum_u64(und), d = wave_sum_u64(nf);
+  if ((threadIdx.x & 63) == 0) {
+    if (a) atomicAdd(c + 0, a);
+    if (b) atomicAdd(c + 1, b);
+    if (d) atomicAdd(c + 2, d);
+  }
+}
+
+}  // namespace fp4q
+
+namespace fp4q {
+
+// MXFP4 encoding of one slot of fp32 values v[8] at flat slot index s; the
+// lane quad (lanes 4k..4k+3, slots 4k..4k+3 of a 32-block) must be executing
+// together.  Writes the code word, the scale byte (first lane of the quad)
+// and accumulates counters.  Audit page, "Encode one MXFP4 block step by step".
+template <bool SR, bool COUNT, bool MANUAL>
+__device__ __forceinline__ void mx_encode_slot(const float v[8], int64_t s, bool active, int lane,
+                                               int manual_e, uint64_t seed, uint8_t* codes_out,
+                                               uint8_t* scales_out, uint32_t& n_sat, uint32_t& n_und,
+                                               uint32_t& n_nf) {
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = max(amax, as_u(v[i]) & 0x7FFFFFFFu);
+  amax = max(amax, dpp_u32<kQuadXor1>(amax));
+  amax = max(amax, dpp_u32<kQuadXor2>(amax));
+  const bool nonfinite = amax >= 0x7F800000u;
+  int e;
+  if constexpr (MANUAL) {
+    e = manual_e;
+  } else {
+    e = (amax == 0u) ? 0 : max((int)(amax >> 23) - 129, -127);
+  }
+  uint32_t codes = 0u;
+  if constexpr (!SR) {
+    const float sc = e8m0_operand((uint32_t)(e + 127));
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[0], v[1], sc, 0);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[2], v[3], sc, 1);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[4], v[5], sc, 2);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[6], v[7], sc, 3);
+  } else {
+    const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
+    const U4 rnd = philox4x32_10(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float qv = ldexpf(v[i], -e);
+      const uint32_t mag = e2m1_sr_mag_f32(fabsf(qv), draw16(rnd, i), v[i] != 0.0f);
+      codes |= (mag | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+    }
+  }
+  if (nonfinite) codes = 0u;
+  if constexpr (COUNT) {
+    if (active) {
+      if (nonfinite) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) n_nf += ((as_u(v[i]) & 0x7FFFFFFFu) >= 0x7F800000u) ? 1u : 0u;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          n_sat += (fabsf(ldexpf(v[i], -e)) > 6.0f) ? 1u : 0u;
+          n_und += (v[i] != 0.0f && ((codes >> (4 * i)) & 7u) == 0u) ? 1u : 0u;
+        }
+      }
+    }
+  }
+  if (active) {
+    *reinterpret_cast<uint32_t*>(codes_out + (s << 2)) = codes;
+    if ((lane & 3) == 0) scales_out[s >> 2] = (uint8_t)(nonfinite ? 0xFFu : (uint32_t)(e + 127));
+  }
+}
+
+}  // namespace fp4q

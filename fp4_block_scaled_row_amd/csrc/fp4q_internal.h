@@ -1,0 +1,73 @@
+// fp4q_internal.h -- launch interface between the C ABI (fp4q_api.hip) and
+// the kernel translation units.  Host-side only declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+// Flat elementwise quantizers: a "slot" is 8 consecutive elements of a row.
+struct QuantLaunch {
+  const void* x;
+  int64_t rows, cols, stride;
+  int64_t nslots;            // rows * cols / 8
+  int in_dtype;              // kF32 / kBF16
+  int rotation;              // kRotNone / kRotRht16
+  int stochastic;            // 0 / 1
+  int manual;                // MX: manual exponent policy
+  int manual_e;
+  int four_over_six;         // NV
+  uint64_t seed;
+  uint32_t rht_signs;        // 16-bit sign mask of the RHT diagonal
+  uint8_t* codes;
+  uint8_t* scales;
+  float* global_scale;
+  uint8_t* choice_bits;
+  float* rotated;
+  unsigned long long* counters;
+  const float* global_amax;  // NV: caller-supplied amax (device) or null
+  uint32_t* partials;        // NV: per-workgroup amax partials (workspace)
+};
+
+constexpr int kAmaxPartialsMax = 1024;  // workgroups of the NV amax pass
+
+hipError_t launch_zero_counters(unsigned long long* counters, hipStream_t s);
+hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t s);
+hipError_t launch_nv_quant(const QuantLaunch& q, hipStream_t s);
+
+// Row Walsh-Hadamard transform of rows of length d (fp32 out), optionally
+// fused with MXFP4 quantization of the rotated row.
+struct FwhtLaunch {
+  const void* x;
+  int64_t rows, d, stride;
+  int in_dtype;
+  int t;                     // transform size (power of two, divides d)
+  int random_signs;
+  uint64_t seed;
+  float* y;                  // fp32 output (may be null when quantizing)
+  // fused MXFP4 quantization (quantize != 0)
+  int quantize;
+  int stochastic;
+  int manual;
+  int manual_e;
+  uint8_t* codes;
+  uint8_t* scales;
+  unsigned long long* counters;
+};
+hipError_t launch_fwht(const FwhtLaunch& f, hipStream_t s);
+
+struct DequantLaunch {
+  int format;                // 0 MX, 1 NV
+  int64_t rows, cols;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* global_scale;
+  int out_dtype;             // kF32 / kBF16
+  void* out;
+};
+hipError_t launch_dequant(const DequantLaunch& d, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace fp4q

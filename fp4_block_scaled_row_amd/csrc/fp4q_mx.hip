@@ -1,0 +1,139 @@
+// fp4q_mx.hip -- MXFP4 quantization kernel for gfx950.
+//
+// "MXFP4 Quantization: Audit the 4.25-Bit Blocks", sections "Read the shared
+// E8M0 scale" and "Encode one MXFP4 block step by step": per 32-block of a
+// row, e = floor(log2(amax/4)) clamped to [-127, 127] (all-zero block: 0),
+// scale byte e + 127, every element divided by 2^e and rounded onto the E2M1
+// lattice with ties to the even code, |v| > 6 clamped to 6; two nibbles per
+// byte, element 2k low.
+//
+// One pass, HBM-bound.  A lane owns 8 elements (one 16-byte bf16 load), a lane
+// quad owns a 32-block; the block amax is an integer max of the abs bit
+// patterns reduced across the quad with DPP.  Element rounding uses the
+// gfx950 scaled FP4 conversion (v_cvt_scalef32_pk_fp4_*), which divides by
+// 2^(b-127) for the E8M0 byte b held in the exponent field of its scale
+// operand and rounds to nearest-even with saturation at +-6 -- exactly the
+// rule above, so the power-of-two division is exact and nothing else rounds.
+#include "fp4q_flat.h"
+
+namespace fp4q {
+namespace {
+
+constexpr int kUnroll = 4;
+
+template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL>
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(QuantLaunch q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  uint32_t n_sat = 0, n_und = 0, n_nf = 0;
+
+  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+    SlotRaw<IN> raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
+      load_slot<IN, CONTIG>(q, s, (t0 + u * nwaves) < ntiles && s < q.nslots, raw[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t t = t0 + u * nwaves;
+      if (t >= ntiles) break;                       // wave-uniform
+      const int64_t s = (t << 6) + lane;
+      const bool active = s < q.nslots;
+      const int64_t f = s << 3;
+
+      constexpr bool kPackedBf16 = (IN == kBF16 && ROT == kRotNone && !SR && !COUNT);
+      if constexpr (!kPackedBf16) {
+        float v[8];
+        widen_slot<IN>(raw[u], v);
+        if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
+        mx_encode_slot<SR, COUNT, MANUAL>(v, s, active, lane, q.manual_e, q.seed, q.codes, q.scales,
+                                          n_sat, n_und, n_nf);
+        if constexpr (ROT != kRotNone) {
+          if (active && q.rotated) store_rotated(q.rotated, s, v);
+        }
+      } else {
+        // bf16 fast path: packed 16-bit max of |x|, conversion straight from bf16
+        ushort2_t m = __builtin_bit_cast(ushort2_t, raw[u].w[0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+          m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, raw[u].w[i] & 0x7FFF7FFFu));
+        uint32_t amax = m.x > m.y ? m.x : m.y;
+        amax = max(amax, dpp_u32<kQuadXor1>(amax));
+        amax = max(amax, dpp_u32<kQuadXor2>(amax));
+        const bool nonfinite = amax >= 0x7F80u;
+        int e;
+        if constexpr (MANUAL) {
+          e = q.manual_e;
+        } else {
+          e = (amax == 0u) ? 0 : max((int)(amax >> 7) - 129, -127);
+        }
+        const float sc = e8m0_operand((uint32_t)(e + 127));
+        uint32_t codes = 0u;
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, raw[u].w[0]), sc, 0);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, raw[u].w[1]), sc, 1);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, raw[u].w[2]), sc, 2);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, raw[u].w[3]), sc, 3);
+        if (nonfinite) codes = 0u;
+        if (active) {
+          *reinterpret_cast<uint32_t*>(q.codes + (f >> 1)) = codes;
+          if ((lane & 3) == 0) q.scales[f >> 5] = (uint8_t)(nonfinite ? 0xFFu : (uint32_t)(e + 127));
+        }
+      }
+    }
+  }
+  if constexpr (COUNT) flush_counters(q.counters, n_sat, n_und, n_nf);
+}
+
+__global__ void zero_counters_kernel(unsigned long long* c) {
+  if (threadIdx.x < 3) c[threadIdx.x] = 0ull;
+}
+
+template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL>
+hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+  hipLaunchKernelGGL((mx_quant_kernel<IN, ROT, SR, COUNT, CONTIG, MANUAL>), dim3(grid), dim3(kThreads), 0, st, q);
+  return hipGetLastError();
+}
+
+template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG>
+hipError_t dispatch_manual(const QuantLaunch& q, hipStream_t st) {
+  return q.manual ? launch_t<IN, ROT, SR, COUNT, CONTIG, true>(q, st)
+                  : launch_t<IN, ROT, SR, COUNT, CONTIG, false>(q, st);
+}
+template <int IN, int ROT, bool SR, bool COUNT>
+hipError_t dispatch_contig(const QuantLaunch& q, hipStream_t st) {
+  return (q.stride == q.cols) ? dispatch_manual<IN, ROT, SR, COUNT, true>(q, st)
+                              : dispatch_manual<IN, ROT, SR, COUNT, false>(q, st);
+}
+template <int IN, int ROT, bool SR>
+hipError_t dispatch_count(const QuantLaunch& q, hipStream_t st) {
+  return q.counters ? dispatch_contig<IN, ROT, SR, true>(q, st) : dispatch_contig<IN, ROT, SR, false>(q, st);
+}
+template <int IN, int ROT>
+hipError_t dispatch_sr(const QuantLaunch& q, hipStream_t st) {
+  return q.stochastic ? dispatch_count<IN, ROT, true>(q, st) : dispatch_count<IN, ROT, false>(q, st);
+}
+template <int IN>
+hipError_t dispatch_rot(const QuantLaunch& q, hipStream_t st) {
+  return q.rotation == kRotRht16 ? dispatch_sr<IN, kRotRht16>(q, st) : dispatch_sr<IN, kRotNone>(q, st);
+}
+
+}  // namespace
+
+hipError_t launch_zero_counters(unsigned long long* counters, hipStream_t st) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, st, counters);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t st) {
+  if (q.nslots == 0) return hipSuccess;
+  return q.in_dtype == kF32 ? dispatch_rot<kF32>(q, st) : dispatch_rot<kBF16>(q, st);
+}
+
+}  // namespace fp4q

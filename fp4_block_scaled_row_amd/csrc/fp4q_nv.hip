@@ -1,0 +1,418 @@
+// fp4q_nv.hip -- NVFP4 and Four-Over-Six quantization kernels for gfx950.
+//
+// "Sub-4-Bit Microscaling (NVFP4, MXFP4 & Walsh-Hadamard Rotation)", section
+// 2: E2M1 elements in 16-blocks, an unsigned E4M3 scale per block and one
+// fp32 scale per tensor, g = amax / (6 * 448), s = RNE_E4M3(bamax / (6 g)),
+// code = RNE_E2M1(x / (s g)).  "Adaptive Block-Scaled Data Types" transcript,
+// cue 10 (Four Over Six): g = amax / (4 * 448) and each block also tries
+// s4 = RNE_E4M3(bamax / (4 g)), keeping the scaling with the lower block SSE
+// (ties keep max->6).  Cue 8: optional random Hadamard transform before
+// quantization and stochastic rounding.
+//
+// Two passes because every block scale depends on the tensor amax:
+//  1. nv_amax_kernel: max of the finite |x| (after rotation) per workgroup
+//     into the workspace (no atomics, no memset needed).
+//  2. nv_quant_kernel: every workgroup reduces those partials to the same g,
+//     then streams the tensor again (mostly served by the Infinity Cache).
+//
+// Exactness.  The quotient x / (s g) is decided exactly without a division
+// per element: with 1/(s g) rounded down and up by 2^-22 (a per-code table in
+// LDS), the two fp32 products bracket the exact quotient, and the gfx950
+// scaled FP4 conversion (scale operand 1.0) rounds each to nearest-even.  The
+// rounding is monotone, so when both brackets give the same code that code is
+// the rounding of the exact quotient.  The rare element whose brackets
+// disagree is recomputed from the correctly rounded fp64 quotient, which is
+// decision-exact (x has <= 24 significant bits and s g <= 28, so a non-tie
+// quotient is at least 2^-47 away, relatively, from any decision point).
+// E4M3 scales are encoded in fp64 with an exact residual check of ties.  For
+// tensors with g < 2^-100 every element takes the fp64 path.
+#include "fp4q_flat.h"
+
+namespace fp4q {
+namespace {
+
+constexpr int kUnroll = 4;
+
+template <int IN, int ROT, bool CONTIG>
+__device__ __forceinline__ void load_values(const QuantLaunch& q, const SlotRaw<IN>& r, int lane, float v[8]) {
+  widen_slot<IN>(r, v);
+  if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
+}
+
+// ---------------------------------------------------------------- pass 1
+template <int IN, int ROT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
+  __shared__ uint32_t s_red[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  uint32_t acc = 0u;  // fp32 abs bit pattern of the running finite max
+  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+    SlotRaw<IN> raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
+      load_slot<IN, CONTIG>(q, s, (t0 + u * nwaves) < ntiles && s < q.nslots, raw[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t0 + u * nwaves >= ntiles) break;
+      if constexpr (IN == kBF16 && ROT == kRotNone) {
+        ushort2_t m = __builtin_bit_cast(ushort2_t, raw[u].w[0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+          m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, raw[u].w[i] & 0x7FFF7FFFu));
+        uint32_t mx = m.x > m.y ? m.x : m.y;
+        if (mx >= 0x7F80u) {   // a non-finite value is present: take the finite max only
+          mx = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = raw[u].w[i] & 0x7FFFu, hi = (raw[u].w[i] >> 16) & 0x7FFFu;
+            if (lo < 0x7F80u) mx = max(mx, lo);
+            if (hi < 0x7F80u) mx = max(mx, hi);
+          }
+        }
+        acc = max(acc, mx << 16);
+      } else {
+        float v[8];
+        load_values<IN, ROT, CONTIG>(q, raw[u], lane, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t a = as_u(v[i]) & 0x7FFFFFFFu;
+          acc = max(acc, a < 0x7F800000u ? a : 0u);
+        }
+      }
+    }
+  }
+  acc = wave_max_u32(acc);
+  if (lane == 0) s_red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, s_red[w]);
+    q.partials[blockIdx.x] = m;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 3 && q.counters) q.counters[threadIdx.x] = 0ull;
+}
+
+// ---------------------------------------------------------------- pass 2
+struct NvCtx {
+  float g;
+  double g64;
+  double mg6, inv6;   // 6 g and 1 / (6 g)
+  double mg4, inv4;   // 4 g and 1 / (4 g)
+  bool exact_all;
+};
+
+// Codes of the 8 elements of a lane for E4M3 scale byte c.
+template <bool SR, bool COUNT>
+__device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, const NvCtx& cx,
+                                              const float2* s_inv, const U4& rnd, uint32_t& satmask) {
+  const float2 iv = s_inv[c];
+  uint32_t ca = 0u, cb = 0u, sa = 0u, sb = 0u;
+  if constexpr (!SR) {
+    const float one = e8m0_operand(127u);
+    float qa[8], qb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qa[i] = v[i] * iv.x;
+      qb[i] = v[i] * iv.y;
+    }
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[0], qa[1], one, 0);
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[2], qa[3], one, 1);
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[4], qa[5], one, 2);
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[6], qa[7], one, 3);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[0], qb[1], one, 0);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[2], qb[3], one, 1);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[4], qb[5], one, 2);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[6], qb[7], one, 3);
+    if constexpr (COUNT) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sa |= (fabsf(qa[i]) > 6.0f ? 1u : 0u) << i;
+        sb |= (fabsf(qb[i]) > 6.0f ? 1u : 0u) << i;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = fabsf(v[i] * iv.x), b = fabsf(v[i] * iv.y);
+      const bool nz = (v[i] != 0.0f) && (c != 0u);
+      const uint32_t u = draw16(rnd, i);
+      const uint32_t sg = (as_u(v[i]) >> 31) << 3;
+      ca |= (e2m1_sr_mag_f32(a, u, nz) | sg) << (4 * i);
+      cb |= (e2m1_sr_mag_f32(b, u, nz) | sg) << (4 * i);
+      if constexpr (COUNT) {
+        sa |= (a > 6.0f ? 1u : 0u) << i;
+        sb |= (b > 6.0f ? 1u : 0u) << i;
+      }
+    }
+  }
+  uint32_t codes = ca, sat = sa;
+  if (ca != cb || sa != sb || cx.exact_all) {
+    // exact path: correctly rounded fp64 quotient
+    const double den = (double)e4m3_value(c) * cx.g64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t nib_diff = ((ca ^ cb) >> (4 * i)) & 0xFu;
+      const uint32_t sat_diff = ((sa ^ sb) >> i) & 1u;
+      if (cx.exact_all || nib_diff || sat_diff) {
+        uint32_t mag = 0u, st = 0u;
+        if (c != 0u) {
+          const double qd = fabs((double)v[i]) / den;
+          mag = SR ? e2m1_sr_mag_f64(qd, draw16(rnd, i)) : e2m1_rne_mag_f64(qd);
+          st = qd > 6.0 ? 1u : 0u;
+        }
+        const uint32_t sg = (as_u(v[i]) >> 31) << 3;
+        codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));
+        sat = (sat & ~(1u << i)) | (st << i);
+      }
+    }
+  }
+  satmask = sat;
+  return codes;
+}
+
+// Half of a block's sum of squared reconstruction errors, in the fixed fp32
+// order (no contraction): dq = (value * s) * g, d = x - dq, acc += d * d.
+__device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint32_t c, float g) {
+#pragma clang fp contract(off)
+  const float one = e8m0_operand(127u);
+  const float sd = e4m3_value(c);
+  float val[8];
+  float2_t p;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0); val[0] = p.x; val[1] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1); val[2] = p.x; val[3] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2); val[4] = p.x; val[5] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3); val[6] = p.x; val[7] = p.y;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float vs = val[i] * sd;
+    const float dq = vs * g;
+    const float d = v[i] - dq;
+    const float sq = d * d;
+    acc = acc + sq;
+  }
+  return acc;
+}
+
+template <int IN, int ROT, bool SR, bool FOS, bool COUNT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int npartials) {
+  __shared__ float2 s_inv[128];
+  __shared__ uint32_t s_red[kWaves];
+  const int lane = threadIdx.x & 63;
+
+  // ---- tensor scale (identical in every workgroup)
+  uint32_t amax_bits;
+  if (q.global_amax) {
+    amax_bits = as_u(fabsf(*q.global_amax));
+  } else {
+    uint32_t m = 0u;
+    for (int i = threadIdx.x; i < npartials; i += kThreads) m = max(m, q.partials[i]);
+    m = wave_max_u32(m);
+    if (lane == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, s_red[w]);
+    amax_bits = m;
+  }
+  const float amax = as_f(amax_bits);
+  NvCtx cx;
+  // amax / 2688 (or / 1792) in fp64 then to fp32: the quotient of a 24-bit
+  // integer by 21 (or 7) times a power of two never lies within 2^-53 of an
+  // fp32 rounding boundary unless exact, so this is the correctly rounded
+  // fp32 division.
+  float g = (amax == 0.0f) ? 1.0f : (float)((double)amax / (FOS ? 1792.0 : 2688.0));
+  if (g == 0.0f) g = 0x1p-149f;
+  cx.g = g;
+  cx.g64 = (double)g;
+  cx.mg6 = 6.0 * cx.g64;
+  cx.inv6 = 1.0 / cx.mg6;
+  cx.mg4 = 4.0 * cx.g64;
+  cx.inv4 = 1.0 / cx.mg4;
+  cx.exact_all = !(g >= 0x1p-100f);
+  for (int c = threadIdx.x; c < 128; c += kThreads) {
+    float2 e = make_float2(0.0f, 0.0f);
+    if (c != 0 && c != 127) {
+      const double inv = 1.0 / ((double)e4m3_value((uint32_t)c) * cx.g64);
+      e.x = (float)(inv * (1.0 - 0x1p-22));
+      e.y = (float)(inv * (1.0 + 0x1p-22));
+    }
+    s_inv[c] = e;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = g;
+  __syncthreads();
+
+  // ---- stream the tensor
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  uint32_t n_sat = 0, n_und = 0, n_nf = 0;
+  const bool odd = (lane & 1) != 0;
+  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+    SlotRaw<IN> raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
+      load_slot<IN, CONTIG>(q, s, (t0 + u * nwaves) < ntiles && s < q.nslots, raw[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t t = t0 + u * nwaves;
+      if (t >= ntiles) break;
+      const int64_t s = (t << 6) + lane;
+      const bool active = s < q.nslots;
+      const int64_t f = s << 3;
+      float v[8];
+      load_values<IN, ROT, CONTIG>(q, raw[u], lane, v);
+
+      uint32_t bm = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bm = max(bm, as_u(v[i]) & 0x7FFFFFFFu);
+      bm = max(bm, dpp_u32<kQuadXor1>(bm));
+      const bool nonfinite = bm >= 0x7F800000u;
+      const float bamax = as_f(bm);
+
+      U4 rnd = {0u, 0u, 0u, 0u};
+      if constexpr (SR) {
+        const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
+        rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
+      }
+      uint32_t c6 = e4m3_encode_exact(bamax, (double)bamax * cx.inv6, cx.mg6);
+      if (nonfinite) c6 = 0u;
+      uint32_t sat6;
+      uint32_t codes = nv_encode<SR, COUNT>(v, c6, cx, s_inv, rnd, sat6);
+      uint32_t sbyte = c6, satm = sat6;
+      bool pick4 = false;
+      if constexpr (FOS) {
+        uint32_t c4 = e4m3_encode_exact(bamax, (double)bamax * cx.inv4, cx.mg4);
+        if (nonfinite) c4 = 0u;
+        uint32_t sat4;
+        const uint32_t codes4 = nv_encode<SR, COUNT>(v, c4, cx, s_inv, rnd, sat4);
+        float e6 = half_sse(v, codes, c6, cx.g);
+        float e4 = half_sse(v, codes4, c4, cx.g);
+        const float p6 = dpp_xor1_f(e6), p4 = dpp_xor1_f(e4);
+        // S_lo (even lane, elements 0..7) + S_hi (odd lane, 8..15); fp32
+        // addition is commutative so both lanes get the same sum.
+        e6 = odd ? (p6 + e6) : (e6 + p6);
+        e4 = odd ? (p4 + e4) : (e4 + p4);
+        pick4 = (e4 < e6) && !nonfinite;
+        if (pick4) {
+          codes = codes4;
+          sbyte = c4;
+          satm = sat4;
+        }
+        // choice bits: block k of this wave-tile is lane pair (2k, 2k+1)
+        uint64_t bal = __ballot(pick4 && !odd && active);
+        bal &= 0x5555555555555555ull;
+        bal = (bal | (bal >> 1)) & 0x3333333333333333ull;
+        bal = (bal | (bal >> 2)) & 0x0F0F0F0F0F0F0F0Full;
+        bal = (bal | (bal >> 4)) & 0x00FF00FF00FF00FFull;
+        bal = (bal | (bal >> 8)) & 0x0000FFFF0000FFFFull;
+        bal = (bal | (bal >> 16)) & 0x00000000FFFFFFFFull;
+        if (lane == 0) {
+          const int64_t nblk = q.nslots >> 1;           // 16-blocks in the tensor
+          const int64_t b0 = t << 5;                    // first block of this tile
+          const int64_t nb = (nblk - b0) < 32 ? (nblk - b0) : 32;
+          uint8_t* dst = q.choice_bits + (b0 >> 3);
+          if (nb == 32) {
+            *reinterpret_cast<uint32_t*>(dst) = (uint32_t)bal;
+          } else {
+            for (int k = 0; k < (int)((nb + 7) >> 3); ++k) dst[k] = (uint8_t)(bal >> (8 * k));
+          }
+        }
+      }
+      if (nonfinite) {
+        codes = 0u;
+        sbyte = 0x7Fu;
+        satm = 0u;
+      }
+      if constexpr (COUNT) {
+        if (active) {
+          if (nonfinite) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) n_nf += ((as_u(v[i]) & 0x7FFFFFFFu) >= 0x7F800000u) ? 1u : 0u;
+          } else {
+            n_sat += __popc(satm);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) n_und += (v[i] != 0.0f && ((codes >> (4 * i)) & 7u) == 0u) ? 1u : 0u;
+          }
+        }
+      }
+      if (active) {
+        *reinterpret_cast<uint32_t*>(q.codes + (f >> 1)) = codes;
+        if (!odd) q.scales[f >> 4] = (uint8_t)sbyte;
+        if constexpr (ROT != kRotNone) {
+          if (q.rotated) store_rotated(q.rotated, s, v);
+        }
+      }
+    }
+  }
+  if constexpr (COUNT) flush_counters(q.counters, n_sat, n_und, n_nf);
+}
+
+int amax_grid(int64_t nslots) {
+  const int64_t ntiles = (nslots + 63) >> 6;
+  int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
+  int64_t cap = (int64_t)device_cu_count() * 4;
+  if (cap > kAmaxPartialsMax) cap = kAmaxPartialsMax;
+  return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+template <int IN, int ROT, bool SR, bool FOS, bool COUNT, bool CONTIG>
+hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
+  int np = 0;
+  if (!q.global_amax) {
+    np = amax_grid(q.nslots);
+    hipLaunchKernelGGL((nv_amax_kernel<IN, ROT, CONTIG>), dim3(np), dim3(kThreads), 0, st, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (q.counters) {
+    hipError_t e = launch_zero_counters(q.counters, st);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+  hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, FOS, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
+  return hipGetLastError();
+}
+
+template <int IN, int ROT, bool SR, bool FOS, bool COUNT>
+hipError_t d_contig(const QuantLaunch& q, hipStream_t st) {
+  return q.stride == q.cols ? launch_t<IN, ROT, SR, FOS, COUNT, true>(q, st)
+                            : launch_t<IN, ROT, SR, FOS, COUNT, false>(q, st);
+}
+template <int IN, int ROT, bool SR, bool FOS>
+hipError_t d_count(const QuantLaunch& q, hipStream_t st) {
+  return q.counters ? d_contig<IN, ROT, SR, FOS, true>(q, st) : d_contig<IN, ROT, SR, FOS, false>(q, st);
+}
+template <int IN, int ROT, bool SR>
+hipError_t d_fos(const QuantLaunch& q, hipStream_t st) {
+  return q.four_over_six ? d_count<IN, ROT, SR, true>(q, st) : d_count<IN, ROT, SR, false>(q, st);
+}
+template <int IN, int ROT>
+hipError_t d_sr(const QuantLaunch& q, hipStream_t st) {
+  return q.stochastic ? d_fos<IN, ROT, true>(q, st) : d_fos<IN, ROT, false>(q, st);
+}
+template <int IN>
+hipError_t d_rot(const QuantLaunch& q, hipStream_t st) {
+  return q.rotation == kRotRht16 ? d_sr<IN, kRotRht16>(q, st) : d_sr<IN, kRotNone>(q, st);
+}
+
+}  // namespace
+
+hipError_t launch_nv_quant(const QuantLaunch& q, hipStream_t st) {
+  if (q.nslots == 0) {
+    // empty tensor: still report g (amax 0 -> 1) and zero the counters
+    return q.in_dtype == kF32 ? d_rot<kF32>(q, st) : d_rot<kBF16>(q, st);
+  }
+  return q.in_dtype == kF32 ? d_rot<kF32>(q, st) : d_rot<kBF16>(q, st);
+}
+
+}  // namespace fp4q

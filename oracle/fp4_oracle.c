@@ -293,6 +293,20 @@ int oracle_quantize_mx(int64_t rows, int64_t cols, int64_t stride, int dtype, co
     return OR_OK;
 }
 
+/* Largest finite |x| of a tensor (the NVFP4 per-tensor amax, reading R-10:
+ * non-finite values are excluded). */
+float oracle_tensor_amax(int64_t rows, int64_t cols, int64_t stride, int dtype, const void *x)
+{
+    int64_t r, i;
+    float amax = 0.0f;
+    for (r = 0; r < rows; r++)
+        for (i = 0; i < cols; i++) {
+            float f = load_elem_f32(x, dtype, r * stride + i);
+            if (isfinite(f) && fabsf(f) > amax) amax = fabsf(f);
+        }
+    return amax;
+}
+
 /* ------------------------------------------------------------------ */
 /* NVFP4 quantize (two-level) and Four-Over-Six                        */
 /* ------------------------------------------------------------------ */
@@ -369,15 +383,7 @@ int oracle_quantize_nv(int64_t rows, int64_t cols, int64_t stride, int dtype, co
     counters_zero(counters);
     memset(codes, 0, (size_t)(rows * cols / 2));
     if (fos) memset(choice_bits, 0, (size_t)((rows * nb + 7) / 8));
-    if (global_amax) {
-        amax = *global_amax;
-    } else {
-        for (r = 0; r < rows; r++)
-            for (i = 0; i < cols; i++) {
-                float f = load_elem_f32(x, dtype, r * stride + i);
-                if (isfinite(f) && fabsf(f) > amax) amax = fabsf(f);
-            }
-    }
+    amax = global_amax ? *global_amax : oracle_tensor_amax(rows, cols, stride, dtype, x);
     denom_mult = fos ? 4.0f : 6.0f;
     if (amax == 0.0f) {
         g = 1.0f;

@@ -59,6 +59,8 @@ def load():
             lib.oracle_fwht.restype = i32
             lib.oracle_dequantize.argtypes = [i32, i64, i64, i32, vp, vp, vp, i32, vp]
             lib.oracle_dequantize.restype = i32
+            lib.oracle_tensor_amax.argtypes = [i64, i64, i64, i32, vp]
+            lib.oracle_tensor_amax.restype = C.c_float
             _lib = lib
     return _lib
 
@@ -151,6 +153,13 @@ def quantize_nv(x, policy=2, rounding=0, seed=0, global_amax=None, cols=None):
     if rc != 0:
         raise ValueError("oracle_quantize_nv rejected the arguments")
     return codes, scales, gs[0], choice, counters
+
+
+def tensor_amax(x):
+    """Largest finite |x| (the NVFP4 per-tensor amax)."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    return np.float32(load().oracle_tensor_amax(rows, cols, cols, dt, _ptr(x)))
 
 
 def fwht(x, t=None, random_signs=False, seed=0):

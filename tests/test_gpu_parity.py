@@ -1,0 +1,380 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Codes, scale bytes, global scales, choice bits, counters
+and dequantized values must be bit-identical; rotations are checked against
+the fp64 oracle transform at relative L2 <= 1e-5, and the oracle quantizer is
+applied to the GPU's rotated fp32 values."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import f32_to_bf16_bits, bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp4_block_scaled_row_amd")
+
+RTOL_ROT = 1e-5
+_cache = {}
+
+
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(gpu()).view(torch.bfloat16)
+    return torch.from_numpy(a).to(gpu())
+
+
+def host(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def workload(name):
+    if name not in _cache:
+        _cache.clear()
+        _cache[name] = workloads.make(name)
+    return _cache[name]
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+def assert_same(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.nonzero(got.reshape(-1) != want.reshape(-1))[0]
+    assert bad.size == 0, "%s: %d mismatches, first at %s: got %s want %s" % (
+        what, bad.size, bad[:5], got.reshape(-1)[bad[:5]], want.reshape(-1)[bad[:5]])
+
+
+def rel_l2(got, want):
+    got = got.astype(np.float64)
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+
+
+def choice_bits_rows(choice, r0, r1, blocks_per_row):
+    allbits = np.unpackbits(choice, bitorder="little")
+    return allbits[r0 * blocks_per_row:r1 * blocks_per_row]
+
+
+# ------------------------------------------------------------------ full-size workloads
+def test_mx_fp32_1024_quant_dequant_counts():
+    x = workload("mx_f32_1024")
+    r = fq.quantize_mxfp4(to_dev(x), counters=True)
+    c, s, cnt = oracle.quantize_mx(x)
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    d32 = fq.dequantize("mxfp4", r.codes, r.scales, out_dtype=torch.float32)
+    assert_same(bits(host(d32)), bits(oracle.dequantize(oracle.MX, c, s)), "dequant fp32")
+    d16 = fq.dequantize("mxfp4", r.codes, r.scales, out_dtype=torch.bfloat16)
+    assert_same(host(d16), oracle.dequantize(oracle.MX, c, s, out_dtype=oracle.BF16), "dequant bf16")
+
+
+def test_mx_bf16_8192_headline():
+    x = workload("act_bf16_8192")
+    xd = to_dev(x)
+    r = fq.quantize_mxfp4(xd)
+    c, s, cnt = oracle.quantize_mx(x)
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.scales), s, "scales")
+    r2 = fq.quantize_mxfp4(xd, counters=True)            # counting variant: same codes
+    assert_same(host(r2.codes), c, "codes (counting kernel)")
+    assert_same(host(r2.counters).astype(np.uint64), cnt, "counters")
+
+
+def test_nv_bf16_8192_headline_and_dequant():
+    x = workload("act_bf16_8192")
+    xd = to_dev(x)
+    r = fq.quantize_nvfp4(xd, counters=True)
+    c, s, g, _, cnt = oracle.quantize_nv(x)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    d16 = fq.dequantize("nvfp4", r.codes, r.scales, r.global_scale, out_dtype=torch.bfloat16)
+    assert_same(host(d16), oracle.dequantize(oracle.NV, c, s, g, out_dtype=oracle.BF16), "dequant bf16")
+    r2 = fq.quantize_nvfp4(xd)
+    assert_same(host(r2.codes), c, "codes (second call, no counters)")
+
+
+def test_fwht_mx_swiglu_16384x8192():
+    x = workload("swiglu_bf16_16384x8192")
+    xd = to_dev(x)
+    r = fq.quantize_mxfp4(xd, rotation="fwht_row", return_rotated=True)
+    rot = host(r.rotated)
+    c, s, _ = oracle.quantize_mx(rot)
+    assert_same(host(r.codes), c, "codes of the rotated values")
+    assert_same(host(r.scales), s, "scales of the rotated values")
+    r2 = fq.quantize_mxfp4(xd, rotation="fwht_row")       # no rotated store: identical codes
+    assert_same(host(r2.codes), c, "codes without the rotated hook")
+    rows = np.random.default_rng(0).choice(x.shape[0], 64, replace=False)
+    ref = oracle.fwht(x[rows])
+    assert rel_l2(rot[rows], ref) <= RTOL_ROT
+
+
+def test_four_over_six_weight_8192x28672_sampled_rows():
+    x = workload("weight_bf16_8192x28672")
+    r = fq.quantize_nvfp4(to_dev(x), policy="four_over_six", counters=True)
+    amax = oracle.tensor_amax(x)
+    g_ref = np.float32(amax) / np.float32(1792)
+    assert host(r.global_scale)[0] == g_ref
+    codes, scales, choice = host(r.codes), host(r.scales), host(r.choice_bits)
+    nbr = x.shape[1] // 16
+    for r0 in (0, 4095, 8192 - 160):
+        r1 = r0 + 160
+        c, s, g, ch, _ = oracle.quantize_nv(x[r0:r1], policy=3, global_amax=amax)
+        assert g == g_ref
+        assert_same(codes[r0:r1], c, "codes rows %d-%d" % (r0, r1))
+        assert_same(scales[r0:r1], s, "scales rows %d-%d" % (r0, r1))
+        assert_same(choice_bits_rows(choice, r0, r1, nbr), np.unpackbits(ch, bitorder="little")[:(r1 - r0) * nbr],
+                    "choice bits rows %d-%d" % (r0, r1))
+    assert host(r.counters)[2] == 0
+
+
+def test_rht_sr_grad_8192():
+    x = workload("grad_bf16_8192")
+    xd = to_dev(x)
+    seed = workloads.SR_SEED
+    r = fq.quantize_nvfp4(xd, rotation="rht16", rounding="stochastic", seed=seed, return_rotated=True,
+                          counters=True)
+    rot = host(r.rotated)
+    c, s, g, _, cnt = oracle.quantize_nv(rot, rounding=1, seed=seed)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    ref = oracle.fwht(x[:512], t=16, random_signs=True, seed=seed)
+    assert rel_l2(rot[:512], ref) <= RTOL_ROT
+    r2 = fq.quantize_nvfp4(xd, rotation="rht16", rounding="stochastic", seed=seed)
+    assert_same(host(r2.codes), c, "codes without the rotated hook")
+
+
+# ------------------------------------------------------------------ small and ragged shapes
+SHAPES = [(1, 32), (3, 64), (17, 96), (5, 160), (64, 256), (7, 1024), (33, 544)]
+
+
+def make_input(rows, cols, dtype, seed, dist="t", pad=0):
+    full = workloads.random_tensor(rows, cols + pad, dtype, seed, scale=3.0, dist=dist)
+    return full
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rounding", ["rne", "stochastic"])
+@pytest.mark.parametrize("rotation", [None, "rht16"])
+def test_mx_small(rows, cols, dtype, rounding, rotation):
+    pad = 32 if rows % 2 else 0
+    full = make_input(rows, cols, dtype, rows * 1000 + cols, pad=pad)
+    xd = to_dev(full)[:, :cols]
+    r = fq.quantize_mxfp4(xd, rounding=rounding, seed=77, rotation=rotation, counters=True,
+                          return_rotated=rotation is not None)
+    if rotation is None:
+        c, s, cnt = oracle.quantize_mx(full, cols=cols, rounding=int(rounding != "rne"), seed=77)
+    else:
+        rot = host(r.rotated)
+        ref = oracle.fwht(np.ascontiguousarray(full[:, :cols]), t=16, random_signs=True, seed=77)
+        assert rel_l2(rot, ref) <= RTOL_ROT
+        c, s, cnt = oracle.quantize_mx(rot, rounding=int(rounding != "rne"), seed=77)
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("policy", ["max6", "four_over_six"])
+@pytest.mark.parametrize("rounding", ["rne", "stochastic"])
+def test_nv_small(rows, cols, dtype, policy, rounding):
+    pad = 16 if rows % 2 else 0
+    full = make_input(rows, cols, dtype, rows * 7 + cols, pad=pad)
+    xd = to_dev(full)[:, :cols]
+    r = fq.quantize_nvfp4(xd, policy=policy, rounding=rounding, seed=123, counters=True)
+    c, s, g, ch, cnt = oracle.quantize_nv(full, cols=cols, policy=3 if policy == "four_over_six" else 2,
+                                         rounding=int(rounding != "rne"), seed=123)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    if ch is not None:
+        assert_same(host(r.choice_bits), ch, "choice bits")
+
+
+@pytest.mark.parametrize("rows,cols", [(4, 64), (9, 4096), (3, 8192), (2, 16384), (5, 32), (6, 2048)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwht_row_mx_small(rows, cols, dtype):
+    full = make_input(rows, cols, dtype, cols + rows, dist="normal")
+    xd = to_dev(full)
+    for rounding in ("rne", "stochastic"):
+        r = fq.quantize_mxfp4(xd, rotation="fwht_row", return_rotated=True, counters=True, rounding=rounding,
+                              seed=9)
+        rot = host(r.rotated)
+        assert rel_l2(rot, oracle.fwht(full)) <= RTOL_ROT
+        c, s, cnt = oracle.quantize_mx(rot, rounding=int(rounding != "rne"), seed=9)
+        assert_same(host(r.codes), c, "codes")
+        assert_same(host(r.scales), s, "scales")
+        assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+
+
+@pytest.mark.parametrize("t", [2, 4, 8, 16, 32, 64, 256, 1024, 4096, 8192, 16384])
+@pytest.mark.parametrize("signs", [False, True])
+def test_fwht_standalone(t, signs):
+    rows = 3
+    d = max(t, 64)
+    full = make_input(rows, d, "bf16", t, dist="normal", pad=64)
+    xd = to_dev(full)[:, :d]
+    y = host(fq.fwht(xd, transform_size=t, random_signs=signs, seed=0xABC))
+    ref = oracle.fwht(np.ascontiguousarray(full[:, :d]), t=t, random_signs=signs, seed=0xABC)
+    assert rel_l2(y, ref) <= RTOL_ROT
+
+
+# ------------------------------------------------------------------ edge cases
+def test_empty_inputs():
+    dev = gpu()
+    for dtype in (torch.float32, torch.bfloat16):
+        x = torch.empty((0, 64), dtype=dtype, device=dev)
+        r = fq.quantize_mxfp4(x, counters=True)
+        assert r.codes.numel() == 0 and host(r.counters).tolist() == [0, 0, 0]
+        n = fq.quantize_nvfp4(x, counters=True)
+        assert host(n.global_scale)[0] == 1.0 and host(n.counters).tolist() == [0, 0, 0]
+        n = fq.quantize_nvfp4(x, policy="four_over_six")
+        assert host(n.global_scale)[0] == 1.0
+        assert fq.fwht(x).numel() == 0
+        assert fq.dequantize("mxfp4", torch.empty((0, 32), dtype=torch.uint8, device=dev),
+                             torch.empty((0, 2), dtype=torch.uint8, device=dev)).numel() == 0
+
+
+def _special_tensor(dtype):
+    rng = np.random.default_rng(42)
+    x = (rng.standard_t(3, (6, 128)) * 2).astype(np.float32)
+    x[0, 3] = np.nan
+    x[1, 40] = np.inf
+    x[1, 41] = -np.inf
+    x[2, :32] = 0.0
+    x[2, 32:48] = -0.0
+    x[3, :] = np.ldexp(rng.uniform(-1, 1, 128), -130).astype(np.float32)   # subnormal block
+    x[4, :] *= 1e30
+    x[5, 0] = -0.0
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nonfinite_zero_subnormal_huge(dtype):
+    x = _special_tensor(dtype)
+    xd = to_dev(x)
+    r = fq.quantize_mxfp4(xd, counters=True)
+    c, s, cnt = oracle.quantize_mx(x)
+    assert_same(host(r.codes), c, "mx codes")
+    assert_same(host(r.scales), s, "mx scales")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "mx counters")
+    for pol, p in (("max6", 2), ("four_over_six", 3)):
+        n = fq.quantize_nvfp4(xd, policy=pol, counters=True)
+        c, s, g, ch, cnt = oracle.quantize_nv(x, policy=p)
+        assert host(n.global_scale)[0] == g
+        assert_same(host(n.scales), s, "nv scales")
+        assert_same(host(n.codes), c, "nv codes")
+        assert_same(host(n.counters).astype(np.uint64), cnt, "nv counters")
+        if ch is not None:
+            assert_same(host(n.choice_bits), ch, "choice")
+    with pytest.raises(fq.Fp4qError):
+        fq.check_counters(n.counters)
+
+
+@pytest.mark.parametrize("scale_exp", [-140, -120, -101, -60, 0, 100, 120])
+def test_nv_tiny_and_huge_tensors(scale_exp):
+    """Tensors whose global scale is tiny take the all-fp64 path (g < 2^-100)."""
+    rng = np.random.default_rng(scale_exp + 500)
+    x = np.ldexp(rng.standard_t(4, (8, 64)), scale_exp).astype(np.float32)
+    for rounding in (0, 1):
+        n = fq.quantize_nvfp4(to_dev(x), rounding=("stochastic" if rounding else "rne"), seed=3, counters=True)
+        c, s, g, _, cnt = oracle.quantize_nv(x, rounding=rounding, seed=3)
+        assert host(n.global_scale)[0] == g
+        assert_same(host(n.scales), s, "scales")
+        assert_same(host(n.codes), c, "codes")
+        assert_same(host(n.counters).astype(np.uint64), cnt, "counters")
+        d = fq.dequantize("nvfp4", n.codes, n.scales, n.global_scale, out_dtype=torch.bfloat16)
+        assert_same(host(d), oracle.dequantize(oracle.NV, c, s, g, out_dtype=oracle.BF16), "dequant bf16")
+        d = fq.dequantize("nvfp4", n.codes, n.scales, n.global_scale, out_dtype=torch.float32)
+        assert_same(bits(host(d)), bits(oracle.dequantize(oracle.NV, c, s, g)), "dequant fp32")
+
+
+def test_nv_exact_ties_and_caller_amax():
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
+    x = np.zeros((2, 64), np.float32)
+    x[0, 0] = 2688.0                      # g = 1 exactly
+    x[0, 16:32] = [9.0] + [m * 1.5 for m in mids] + [-m * 1.5 for m in mids[:7]]
+    x[1] = np.random.default_rng(1).standard_normal(64) * 3
+    xd = to_dev(x)
+    n = fq.quantize_nvfp4(xd, counters=True)
+    c, s, g, _, cnt = oracle.quantize_nv(x)
+    assert_same(host(n.codes), c, "codes with exact ties")
+    assert_same(host(n.counters).astype(np.uint64), cnt, "counters")
+    amax = torch.tensor([1.0], dtype=torch.float32, device=xd.device)   # saturating caller amax
+    n = fq.quantize_nvfp4(xd, global_amax=amax, counters=True)
+    c, s, g, _, cnt = oracle.quantize_nv(x, global_amax=1.0)
+    assert host(n.global_scale)[0] == g
+    assert_same(host(n.scales), s, "scales (caller amax)")
+    assert_same(host(n.codes), c, "codes (caller amax)")
+    assert_same(host(n.counters).astype(np.uint64), cnt, "counters (caller amax)")
+
+
+@pytest.mark.parametrize("e", [-127, -20, 0, 5, 125, 126, 127])
+def test_mx_manual_exponent(e):
+    x = make_input(4, 128, "f32", 11)
+    for rounding in ("rne", "stochastic"):
+        r = fq.quantize_mxfp4(to_dev(x), policy="manual", manual_exponent=e, rounding=rounding, seed=5,
+                              counters=True)
+        c, s, cnt = oracle.quantize_mx(x, policy=1, manual_exponent=e, rounding=int(rounding != "rne"), seed=5)
+        assert_same(host(r.codes), c, "codes")
+        assert_same(host(r.scales), s, "scales")
+        assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+        d = fq.dequantize("mxfp4", r.codes, r.scales)
+        assert_same(bits(host(d)), bits(oracle.dequantize(oracle.MX, c, s)), "dequant")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequant_all_codes_and_scales(fmt, out_dtype):
+    rng = np.random.default_rng(3)
+    rows, cols = 16, 512
+    block = 32 if fmt == "mxfp4" else 16
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    codes[0, :128] = np.arange(128, dtype=np.uint8) * 2     # every nibble value
+    scales = rng.integers(0, 255 if fmt == "mxfp4" else 0x7F, (rows, cols // block), dtype=np.uint8)
+    scales[0, :] = np.arange(scales.shape[1]) % (256 if fmt == "mxfp4" else 128)
+    scales[1, 0] = 0xFF if fmt == "mxfp4" else 0x7F
+    gs = np.float32(0.0123457) if fmt == "nvfp4" else None
+    gdev = torch.tensor([gs], dtype=torch.float32, device=gpu()) if gs is not None else None
+    d = fq.dequantize(fmt, to_dev(codes), to_dev(scales), gdev, out_dtype=out_dtype)
+    od = oracle.F32 if out_dtype == torch.float32 else oracle.BF16
+    want = oracle.dequantize(oracle.MX if fmt == "mxfp4" else oracle.NV, codes, scales, gs, out_dtype=od)
+    got = host(d)
+    if out_dtype == torch.float32:
+        got, want = bits(got), bits(want)
+    nan_got = np.isnan(bf16_bits_to_f32(got)) if out_dtype == torch.bfloat16 else np.isnan(got.view(np.float32))
+    nan_want = np.isnan(bf16_bits_to_f32(want)) if out_dtype == torch.bfloat16 else np.isnan(want.view(np.float32))
+    assert_same(nan_got, nan_want, "NaN positions")
+    assert_same(np.where(nan_got, 0, got), np.where(nan_want, 0, want), "values")
+
+
+def test_deterministic_repeat():
+    x = to_dev(make_input(64, 512, "bf16", 99))
+    a = fq.quantize_nvfp4(x, policy="four_over_six", rounding="stochastic", rotation="rht16", seed=1)
+    b = fq.quantize_nvfp4(x, policy="four_over_six", rounding="stochastic", rotation="rht16", seed=1)
+    for u, v in zip(a, b):
+        if u is not None:
+            assert torch.equal(u, v)
+    c = fq.quantize_nvfp4(x, policy="four_over_six", rounding="stochastic", rotation="rht16", seed=2)
+    assert not torch.equal(a.codes, c.codes)
