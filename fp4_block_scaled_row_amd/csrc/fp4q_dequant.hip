@@ -40,18 +40,18 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int6
   float g = 1.0f;
   if constexpr (FMT == 1) g = *d.global_scale;
   const float one = e8m0_operand(127u);
-  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+  for (int64_t g0 = wave; g0 * kUnroll < ntiles; g0 += nwaves) {
     uint32_t cw[kUnroll], sb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
-      const bool act = (t0 + u * nwaves) < ntiles && s < nslots;
+      const int64_t s = ((g0 * kUnroll + u) << 6) + lane;
+      const bool act = s < nslots;
       cw[u] = act ? *reinterpret_cast<const uint32_t*>(d.codes + (s << 2)) : 0u;
       sb[u] = act ? (uint32_t)d.scales[FMT == 0 ? (s >> 2) : (s >> 1)] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t t = t0 + u * nwaves;
+      const int64_t t = g0 * kUnroll + u;
       if (t >= ntiles) break;
       const int64_t s = (t << 6) + lane;
       if (s >= nslots) continue;

@@ -23,7 +23,18 @@ __device__ __forceinline__ int64_t slot_in_offset(int64_t s, int64_t cols, int64
   return r * stride + (f - r * cols);
 }
 
-template <int IN, bool CONTIG>
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global load; NT marks it non-temporal (streamed once, not kept in
+// the caches), used when no later pass re-reads the data.
+template <bool NT>
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
+}
+
+template <int IN, bool CONTIG, bool NT = false>
 __device__ __forceinline__ void load_slot(const QuantLaunch& q, int64_t s, bool active, SlotRaw<IN>& r) {
   if (!active) {
 #pragma unroll
@@ -32,12 +43,12 @@ __device__ __forceinline__ void load_slot(const QuantLaunch& q, int64_t s, bool 
   }
   const int64_t off = slot_in_offset<CONTIG>(s, q.cols, q.stride);
   if constexpr (IN == kF32) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(q.x) + off);
-    const uint4 a = p[0], b = p[1];
+    const float* p = static_cast<const float*>(q.x) + off;
+    const u32x4_t a = load16<NT>(p), b = load16<NT>(p + 4);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
     r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
   } else {
-    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + off);
+    const u32x4_t a = load16<NT>(static_cast<const uint16_t*>(q.x) + off);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
   }
 }

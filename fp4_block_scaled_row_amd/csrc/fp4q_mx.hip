@@ -29,16 +29,18 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(QuantLaunch q) {
   const int64_t ntiles = (q.nslots + 63) >> 6;
   uint32_t n_sat = 0, n_und = 0, n_nf = 0;
 
-  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+  // wave-tile = 64 slots (512 elements); a wave owns kUnroll consecutive
+  // tiles per iteration so its loads and its code/scale stores are contiguous
+  for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
     SlotRaw<IN> raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
-      load_slot<IN, CONTIG>(q, s, (t0 + u * nwaves) < ntiles && s < q.nslots, raw[u]);
+      const int64_t s = ((g * kUnroll + u) << 6) + lane;
+      load_slot<IN, CONTIG, true>(q, s, s < q.nslots, raw[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t t = t0 + u * nwaves;
+      const int64_t t = g * kUnroll + u;
       if (t >= ntiles) break;                       // wave-uniform
       const int64_t s = (t << 6) + lane;
       const bool active = s < q.nslots;

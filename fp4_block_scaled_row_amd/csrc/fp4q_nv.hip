@@ -48,16 +48,16 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int64_t ntiles = (q.nslots + 63) >> 6;
   uint32_t acc = 0u;  // fp32 abs bit pattern of the running finite max
-  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+  for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
     SlotRaw<IN> raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
-      load_slot<IN, CONTIG>(q, s, (t0 + u * nwaves) < ntiles && s < q.nslots, raw[u]);
+      const int64_t s = ((g * kUnroll + u) << 6) + lane;
+      load_slot<IN, CONTIG, false>(q, s, s < q.nslots, raw[u]);   // kept in the caches for pass 2
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (t0 + u * nwaves >= ntiles) break;
+      if (g * kUnroll + u >= ntiles) break;
       if constexpr (IN == kBF16 && ROT == kRotNone) {
         ushort2_t m = __builtin_bit_cast(ushort2_t, raw[u].w[0] & 0x7FFF7FFFu);
 #pragma unroll
@@ -253,16 +253,18 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   const int64_t ntiles = (q.nslots + 63) >> 6;
   uint32_t n_sat = 0, n_und = 0, n_nf = 0;
   const bool odd = (lane & 1) != 0;
-  for (int64_t t0 = wave; t0 < ntiles; t0 += nwaves * kUnroll) {
+  // wave-tile = 64 slots (512 elements); a wave owns kUnroll consecutive
+  // tiles per iteration so its loads and its code/scale stores are contiguous
+  for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
     SlotRaw<IN> raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((t0 + u * nwaves) << 6) + lane;
-      load_slot<IN, CONTIG>(q, s, (t0 + u * nwaves) < ntiles && s < q.nslots, raw[u]);
+      const int64_t s = ((g * kUnroll + u) << 6) + lane;
+      load_slot<IN, CONTIG, true>(q, s, s < q.nslots, raw[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t t = t0 + u * nwaves;
+      const int64_t t = g * kUnroll + u;
       if (t >= ntiles) break;
       const int64_t s = (t << 6) + lane;
       const bool active = s < q.nslots;
