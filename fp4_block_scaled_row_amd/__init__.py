@@ -124,7 +124,7 @@ def quantize_nvfp4(x, *, policy="max6", rounding="rne", seed=0, rotation=None, g
         cnt = torch.empty(3, dtype=torch.int64, device=dev) if counters else None
         out = NvResult(codes, scales, gs, choice, rot, cnt)
     if workspace is None and global_amax is None:
-        workspace = torch.empty(workspace_bytes(16), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(workspace_bytes(16), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if global_amax is not None and (global_amax.dtype != torch.float32 or not global_amax.is_cuda):
         raise TypeError("fp4q: global_amax must be a float32 GPU tensor")

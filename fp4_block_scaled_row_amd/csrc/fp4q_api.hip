@@ -5,7 +5,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/fp4q.h"
+#include "fp4q.h"
 #include "fp4q_common.h"
 #include "fp4q_internal.h"
 
@@ -97,7 +97,7 @@ extern "C" {
 
 size_t fp4q_workspace_bytes(const fp4q_quant_args* args) {
   if (!args) return 0;
-  if (args->block_size == 16) return (size_t)kAmaxPartialsMax * sizeof(uint32_t);
+  if (args->block_size == 16) return kNvWorkspaceBytes;
   return 0;
 }
 

@@ -31,10 +31,18 @@ struct QuantLaunch {
 };
 
 constexpr int kAmaxPartialsMax = 1024;  // workgroups of the NV amax pass
+// NVFP4 workspace layout (bytes): [0, 64) epoch and release words of the
+// single-launch kernel, [64, 64 + 8 * 1024) its per-workgroup flags,
+// [8256, 8256 + 4 * 1024) the amax partials of the two-pass kernels.
+constexpr size_t kWsFlagsOffsetBytes = 64;
+constexpr size_t kWsPartialsOffsetBytes = kWsFlagsOffsetBytes + 8 * kAmaxPartialsMax;
+constexpr size_t kNvWorkspaceBytes = 16384;
 
 hipError_t launch_zero_counters(unsigned long long* counters, hipStream_t s);
 hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_nv_quant(const QuantLaunch& q, hipStream_t s);
+bool nv_resident_shape(const QuantLaunch& q, int* grid, int* nres);
+hipError_t launch_nv_resident(const QuantLaunch& q, int grid, int nres, hipStream_t s);
 
 // Row Walsh-Hadamard transform of rows of length d (fp32 out), optionally
 // fused with MXFP4 quantization of the rotated row.

@@ -27,6 +27,7 @@
 // E4M3 scales are encoded in fp64 with an exact residual check of ties.  For
 // tensors with g < 2^-100 every element takes the fp64 path.
 #include "fp4q_flat.h"
+#include "fp4q_nv_common.h"
 
 namespace fp4q {
 namespace {
@@ -97,108 +98,6 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
   if (blockIdx.x == 0 && threadIdx.x < 3 && q.counters) q.counters[threadIdx.x] = 0ull;
 }
 
-// ---------------------------------------------------------------- pass 2
-struct NvCtx {
-  float g;
-  double g64;
-  double mg6, inv6;   // 6 g and 1 / (6 g)
-  double mg4, inv4;   // 4 g and 1 / (4 g)
-  bool exact_all;
-};
-
-// Codes of the 8 elements of a lane for E4M3 scale byte c.
-template <bool SR, bool COUNT>
-__device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, const NvCtx& cx,
-                                              const float2* s_inv, const U4& rnd, uint32_t& satmask) {
-  const float2 iv = s_inv[c];
-  uint32_t ca = 0u, cb = 0u, sa = 0u, sb = 0u;
-  if constexpr (!SR) {
-    const float one = e8m0_operand(127u);
-    float qa[8], qb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qa[i] = v[i] * iv.x;
-      qb[i] = v[i] * iv.y;
-    }
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[0], qa[1], one, 0);
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[2], qa[3], one, 1);
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[4], qa[5], one, 2);
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[6], qa[7], one, 3);
-    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[0], qb[1], one, 0);
-    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[2], qb[3], one, 1);
-    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[4], qb[5], one, 2);
-    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[6], qb[7], one, 3);
-    if constexpr (COUNT) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sa |= (fabsf(qa[i]) > 6.0f ? 1u : 0u) << i;
-        sb |= (fabsf(qb[i]) > 6.0f ? 1u : 0u) << i;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a = fabsf(v[i] * iv.x), b = fabsf(v[i] * iv.y);
-      const bool nz = (v[i] != 0.0f) && (c != 0u);
-      const uint32_t u = draw16(rnd, i);
-      const uint32_t sg = (as_u(v[i]) >> 31) << 3;
-      ca |= (e2m1_sr_mag_f32(a, u, nz) | sg) << (4 * i);
-      cb |= (e2m1_sr_mag_f32(b, u, nz) | sg) << (4 * i);
-      if constexpr (COUNT) {
-        sa |= (a > 6.0f ? 1u : 0u) << i;
-        sb |= (b > 6.0f ? 1u : 0u) << i;
-      }
-    }
-  }
-  uint32_t codes = ca, sat = sa;
-  if (ca != cb || sa != sb || cx.exact_all) {
-    // exact path: correctly rounded fp64 quotient
-    const double den = (double)e4m3_value(c) * cx.g64;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t nib_diff = ((ca ^ cb) >> (4 * i)) & 0xFu;
-      const uint32_t sat_diff = ((sa ^ sb) >> i) & 1u;
-      if (cx.exact_all || nib_diff || sat_diff) {
-        uint32_t mag = 0u, st = 0u;
-        if (c != 0u) {
-          const double qd = fabs((double)v[i]) / den;
-          mag = SR ? e2m1_sr_mag_f64(qd, draw16(rnd, i)) : e2m1_rne_mag_f64(qd);
-          st = qd > 6.0 ? 1u : 0u;
-        }
-        const uint32_t sg = (as_u(v[i]) >> 31) << 3;
-        codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));
-        sat = (sat & ~(1u << i)) | (st << i);
-      }
-    }
-  }
-  satmask = sat;
-  return codes;
-}
-
-// Half of a block's sum of squared reconstruction errors, in the fixed fp32
-// order (no contraction): dq = (value * s) * g, d = x - dq, acc += d * d.
-__device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint32_t c, float g) {
-#pragma clang fp contract(off)
-  const float one = e8m0_operand(127u);
-  const float sd = e4m3_value(c);
-  float val[8];
-  float2_t p;
-  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0); val[0] = p.x; val[1] = p.y;
-  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1); val[2] = p.x; val[3] = p.y;
-  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2); val[4] = p.x; val[5] = p.y;
-  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3); val[6] = p.x; val[7] = p.y;
-  float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float vs = val[i] * sd;
-    const float dq = vs * g;
-    const float d = v[i] - dq;
-    const float sq = d * d;
-    acc = acc + sq;
-  }
-  return acc;
-}
-
 template <int IN, int ROT, bool SR, bool FOS, bool COUNT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int npartials) {
   __shared__ float2 s_inv[128];
@@ -220,31 +119,10 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
     for (int w = 1; w < kWaves; ++w) m = max(m, s_red[w]);
     amax_bits = m;
   }
-  const float amax = as_f(amax_bits);
   NvCtx cx;
-  // amax / 2688 (or / 1792) in fp64 then to fp32: the quotient of a 24-bit
-  // integer by 21 (or 7) times a power of two never lies within 2^-53 of an
-  // fp32 rounding boundary unless exact, so this is the correctly rounded
-  // fp32 division.
-  float g = (amax == 0.0f) ? 1.0f : (float)((double)amax / (FOS ? 1792.0 : 2688.0));
-  if (g == 0.0f) g = 0x1p-149f;
-  cx.g = g;
-  cx.g64 = (double)g;
-  cx.mg6 = 6.0 * cx.g64;
-  cx.inv6 = 1.0 / cx.mg6;
-  cx.mg4 = 4.0 * cx.g64;
-  cx.inv4 = 1.0 / cx.mg4;
-  cx.exact_all = !(g >= 0x1p-100f);
-  for (int c = threadIdx.x; c < 128; c += kThreads) {
-    float2 e = make_float2(0.0f, 0.0f);
-    if (c != 0 && c != 127) {
-      const double inv = 1.0 / ((double)e4m3_value((uint32_t)c) * cx.g64);
-      e.x = (float)(inv * (1.0 - 0x1p-22));
-      e.y = (float)(inv * (1.0 + 0x1p-22));
-    }
-    s_inv[c] = e;
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = g;
+  nv_context(as_f(amax_bits), FOS, cx);
+  nv_fill_inverse_table(s_inv, cx, threadIdx.x, kThreads);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
   __syncthreads();
 
   // ---- stream the tensor
@@ -255,16 +133,16 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   const bool odd = (lane & 1) != 0;
   // wave-tile = 64 slots (512 elements); a wave owns kUnroll consecutive
   // tiles per iteration so its loads and its code/scale stores are contiguous
-  for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
+  for (int64_t grp = wave; grp * kUnroll < ntiles; grp += nwaves) {
     SlotRaw<IN> raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((g * kUnroll + u) << 6) + lane;
+      const int64_t s = ((grp * kUnroll + u) << 6) + lane;
       load_slot<IN, CONTIG, true>(q, s, s < q.nslots, raw[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t t = g * kUnroll + u;
+      const int64_t t = grp * kUnroll + u;
       if (t >= ntiles) break;
       const int64_t s = (t << 6) + lane;
       const bool active = s < q.nslots;
@@ -284,15 +162,13 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
         rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
       }
-      uint32_t c6 = e4m3_encode_exact(bamax, (double)bamax * cx.inv6, cx.mg6);
-      if (nonfinite) c6 = 0u;
+      const uint32_t c6 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all);
       uint32_t sat6;
       uint32_t codes = nv_encode<SR, COUNT>(v, c6, cx, s_inv, rnd, sat6);
       uint32_t sbyte = c6, satm = sat6;
       bool pick4 = false;
       if constexpr (FOS) {
-        uint32_t c4 = e4m3_encode_exact(bamax, (double)bamax * cx.inv4, cx.mg4);
-        if (nonfinite) c4 = 0u;
+        const uint32_t c4 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv4_lo, cx.inv4_hi, cx.inv4, cx.mg4, cx.exact_all);
         uint32_t sat4;
         const uint32_t codes4 = nv_encode<SR, COUNT>(v, c4, cx, s_inv, rnd, sat4);
         float e6 = half_sse(v, codes, c6, cx.g);
@@ -409,11 +285,13 @@ hipError_t d_rot(const QuantLaunch& q, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_nv_quant(const QuantLaunch& q, hipStream_t st) {
-  if (q.nslots == 0) {
-    // empty tensor: still report g (amax 0 -> 1) and zero the counters
-    return q.in_dtype == kF32 ? d_rot<kF32>(q, st) : d_rot<kBF16>(q, st);
-  }
+hipError_t launch_nv_quant(const QuantLaunch& q0, hipStream_t st) {
+  // q0.partials is the workspace base (layout in fp4q_internal.h)
+  QuantLaunch q = q0;
+  int grid = 0, nres = 0;
+  if (q.partials && nv_resident_shape(q, &grid, &nres)) return launch_nv_resident(q, grid, nres, st);
+  if (q.partials) q.partials += kWsPartialsOffsetBytes / sizeof(uint32_t);
+  // (an empty tensor still runs both passes: g = 1 is reported, counters zeroed)
   return q.in_dtype == kF32 ? d_rot<kF32>(q, st) : d_rot<kBF16>(q, st);
 }
 

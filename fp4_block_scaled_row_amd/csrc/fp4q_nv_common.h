@@ -1,0 +1,341 @@
+// fp4q_nv_common.h -- NVFP4 encoding steps shared by the two-pass and the
+// single-read kernels ("Sub-4-Bit Microscaling", section 2; Four Over Six and
+// stochastic rounding, "Adaptive Block-Scaled Data Types" transcript cues 8
+// and 10).
+//
+// Exactness without per-element division.  For a block with E4M3 byte c the
+// exact quotient is q = x / (s_c g).  1/(s_c g) rounded down and up by 2^-22
+// (a 128-entry table, one per code) gives two fp32 products that bracket q;
+// the gfx950 scaled FP4 conversion (scale operand 1.0) rounds each to
+// nearest-even.  That rounding is monotone, so equal codes from both brackets
+// are the rounding of q itself.  An element whose brackets disagree is
+// recomputed from the correctly rounded fp64 quotient, which decides every
+// rounding exactly (x has <= 24 significant bits and s g <= 28, so a non-tie
+// quotient is at least 2^-47 away, relatively, from any decision point).  The
+// E4M3 block scale is bracketed the same way with the fp8 conversion, falling
+// back to an fp64 encoding with an exact residual check of ties.  Tensors with
+// g < 2^-100 take the fp64 path for every element.
+#pragma once
+
+#include "fp4q_flat.h"
+
+namespace fp4q {
+
+struct NvCtx {
+  float g;
+  double g64;
+  double mg6, inv6;          // 6 g and 1 / (6 g)
+  double mg4, inv4;          // 4 g and 1 / (4 g)
+  float inv6_lo, inv6_hi;    // 1 / (6 g) bracketed by 2^-22
+  float inv4_lo, inv4_hi;
+  bool exact_all;
+};
+
+// g = RN32(amax / D) with D = 6*448 (max->6) or 4*448 (Four Over Six).  amax /
+// D is evaluated in fp64 then rounded to fp32: the quotient of a 24-bit
+// integer by 21 (or 7) times a power of two never lies within 2^-53 of an
+// fp32 rounding boundary unless it is exact, so this is the correctly
+// rounded fp32 division.  amax 0 -> g = 1; a nonzero amax whose g underflows
+// -> g = 2^-149.
+// Context of a given tensor scale g (the derived factors below).
+__device__ __forceinline__ void nv_context_g(float g, NvCtx& cx) {
+  cx.g = g;
+  cx.g64 = (double)g;
+  cx.mg6 = 6.0 * cx.g64;
+  cx.inv6 = 1.0 / cx.mg6;
+  cx.mg4 = 4.0 * cx.g64;
+  cx.inv4 = 1.0 / cx.mg4;
+  cx.inv6_lo = (float)(cx.inv6 * (1.0 - 0x1p-22));
+  cx.inv6_hi = (float)(cx.inv6 * (1.0 + 0x1p-22));
+  cx.inv4_lo = (float)(cx.inv4 * (1.0 - 0x1p-22));
+  cx.inv4_hi = (float)(cx.inv4 * (1.0 + 0x1p-22));
+  cx.exact_all = !(g >= 0x1p-100f);
+}
+
+__device__ __forceinline__ void nv_context(float amax, bool fos, NvCtx& cx) {
+  float g = (amax == 0.0f) ? 1.0f : (float)((double)amax / (fos ? 1792.0 : 2688.0));
+  if (g == 0.0f) g = 0x1p-149f;
+  nv_context_g(g, cx);
+}
+
+// s_inv[c] = (1/(s_c g)) (1 -+ 2^-22) for every finite E4M3 code c > 0.
+__device__ __forceinline__ void nv_fill_inverse_table(float2* s_inv, const NvCtx& cx, int tid, int nthreads) {
+  for (int c = tid; c < 128; c += nthreads) {
+    float2 e = make_float2(0.0f, 0.0f);
+    if (c != 0 && c != 127) {
+      const double inv = 1.0 / ((double)e4m3_value((uint32_t)c) * cx.g64);
+      e.x = (float)(inv * (1.0 - 0x1p-22));
+      e.y = (float)(inv * (1.0 + 0x1p-22));
+    }
+    s_inv[c] = e;
+  }
+}
+
+// E4M3 block-scale byte RNE_E4M3(bamax / (mult g)), saturating at 448.  With
+// g < 2^-100 (exact_all) 1/(mult g) may not fit fp32, so the fp64 encoding
+// decides directly.
+__device__ __forceinline__ uint32_t nv_scale_code(float bamax, float inv_lo, float inv_hi, double inv64, double mg,
+                                                  bool exact_all) {
+  if (exact_all) return e4m3_encode_exact(bamax, (double)bamax * inv64, mg);
+  const float tl = fminf(bamax * inv_lo, 448.0f);
+  const float th = fminf(bamax * inv_hi, 448.0f);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
+  const uint32_t cl = b & 0xFFu, ch = (b >> 8) & 0xFFu;
+  if (cl == ch) return cl;
+  return e4m3_encode_exact(bamax, (double)bamax * inv64, mg);
+}
+
+// Codes of the 8 elements of a lane for E4M3 scale byte c.
+template <bool SR, bool COUNT>
+__device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, const NvCtx& cx,
+                                              const float2* s_inv, const U4& rnd, uint32_t& satmask) {
+  const float2 iv = s_inv[c];
+  uint32_t ca = 0u, cb = 0u, sa = 0u, sb = 0u;
+  if constexpr (!SR) {
+    const float one = e8m0_operand(127u);
+    float qa[8], qb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qa[i] = v[i] * iv.x;
+      qb[i] = v[i] * iv.y;
+    }
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[0], qa[1], one, 0);
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[2], qa[3], one, 1);
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[4], qa[5], one, 2);
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[6], qa[7], one, 3);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[0], qb[1], one, 0);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[2], qb[3], one, 1);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[4], qb[5], one, 2);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[6], qb[7], one, 3);
+    if constexpr (COUNT) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sa |= (fabsf(qa[i]) > 6.0f ? 1u : 0u) << i;
+        sb |= (fabsf(qb[i]) > 6.0f ? 1u : 0u) << i;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = fabsf(v[i] * iv.x), b = fabsf(v[i] * iv.y);
+      const bool nz = (v[i] != 0.0f) && (c != 0u);
+      const uint32_t u = draw16(rnd, i);
+      const uint32_t sg = (as_u(v[i]) >> 31) << 3;
+      ca |= (e2m1_sr_mag_f32(a, u, nz) | sg) << (4 * i);
+      cb |= (e2m1_sr_mag_f32(b, u, nz) | sg) << (4 * i);
+      if constexpr (COUNT) {
+        sa |= (a > 6.0f ? 1u : 0u) << i;
+        sb |= (b > 6.0f ? 1u : 0u) << i;
+      }
+    }
+  }
+  uint32_t codes = ca, sat = sa;
+  if (ca != cb || sa != sb || cx.exact_all) {
+    // exact path: correctly rounded fp64 quotient
+    const double den = (double)e4m3_value(c) * cx.g64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t nib_diff = ((ca ^ cb) >> (4 * i)) & 0xFu;
+      const uint32_t sat_diff = ((sa ^ sb) >> i) & 1u;
+      if (cx.exact_all || nib_diff || sat_diff) {
+        uint32_t mag = 0u, st = 0u;
+        if (c != 0u) {
+          const double qd = fabs((double)v[i]) / den;
+          mag = SR ? e2m1_sr_mag_f64(qd, draw16(rnd, i)) : e2m1_rne_mag_f64(qd);
+          st = qd > 6.0 ? 1u : 0u;
+        }
+        const uint32_t sg = (as_u(v[i]) >> 31) << 3;
+        codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));
+        sat = (sat & ~(1u << i)) | (st << i);
+      }
+    }
+  }
+  satmask = sat;
+  return codes;
+}
+
+// Half of a block's sum of squared reconstruction errors, in the fixed fp32
+// order (no contraction): dq = (value * s) * g, d = x - dq, acc += d * d.
+__device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint32_t c, float g) {
+#pragma clang fp contract(off)
+  const float one = e8m0_operand(127u);
+  const float sd = e4m3_value(c);
+  float val[8];
+  float2_t p;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0); val[0] = p.x; val[1] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1); val[2] = p.x; val[3] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2); val[4] = p.x; val[5] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3); val[6] = p.x; val[7] = p.y;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float vs = val[i] * sd;
+    const float dq = vs * g;
+    const float d = v[i] - dq;
+    const float sq = d * d;
+    acc = acc + sq;
+  }
+  return acc;
+}
+
+// The whole max->6 NVFP4 encoding of one slot of raw bf16 data (8 values at
+// flat slot s; the lane pair 2k, 2k+1 holds one 16-block and must execute
+// together): widen, optional RHT16, block amax, scale byte, codes, counters,
+// stores.
+template <int ROT, bool SR, bool COUNT>
+__device__ __forceinline__ void nv_encode_slot(const QuantLaunch& q, const NvCtx& cx, const float2* s_inv,
+                                               const uint4& w, int64_t s, bool active, int lane,
+                                               uint32_t& n_sat, uint32_t& n_und, uint32_t& n_nf) {
+  float v[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+  if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
+  uint32_t bm = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bm = max(bm, as_u(v[i]) & 0x7FFFFFFFu);
+  bm = max(bm, dpp_u32<kQuadXor1>(bm));
+  const bool nonfinite = bm >= 0x7F800000u;
+  const float bamax = as_f(bm);
+  U4 rnd = {0u, 0u, 0u, 0u};
+  if constexpr (SR) {
+    const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
+    rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
+  }
+  const uint32_t c = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all);
+  uint32_t satm;
+  uint32_t codes = nv_encode<SR, COUNT>(v, c, cx, s_inv, rnd, satm);
+  if (nonfinite) codes = 0u;
+  if constexpr (COUNT) {
+    if (active) {
+      if (nonfinite) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) n_nf += ((as_u(v[i]) & 0x7FFFFFFFu) >= 0x7F800000u) ? 1u : 0u;
+      } else {
+        n_sat += __popc(satm);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) n_und += (v[i] != 0.0f && ((codes >> (4 * i)) & 7u) == 0u) ? 1u : 0u;
+      }
+    }
+  }
+  if (active) {
+    *reinterpret_cast<uint32_t*>(q.codes + (s << 2)) = codes;
+    if (!(lane & 1)) q.scales[s >> 1] = (uint8_t)(nonfinite ? 0x7Fu : c);
+    if constexpr (ROT != kRotNone) {
+      if (q.rotated) store_rotated(q.rotated, s, v);
+    }
+  }
+}
+
+// Exact decisions for brackets that disagree.  When the two bracket products
+// of one quotient q = a / (k g) round to adjacent codes lo < hi, exactly one
+// decision point p (the midpoint of their values) lies between them, and q
+// is above, below or on it as a - (p k) g is positive, negative or zero: p k
+// is exact in fp32 (a few significant bits each) and one FMA evaluates the
+// difference exactly before its single rounding, so the sign is exact (for
+// g >= 2^-100 no product underflows).  A tie takes the code with the even
+// mantissa.  This replaces an fp64 division in the common near-tie case
+// (bf16 inputs make quotients within 2^-24 of a decision point frequent).
+
+// E4M3 scale byte of bamax / (mult g) given the bracket bytes cl < ch.
+__device__ __forceinline__ uint32_t resolve_e4m3(float bamax, uint32_t cl, uint32_t ch, float mult, float g) {
+  const float p = 0.5f * (e4m3_value(cl) + e4m3_value(ch));
+  const float r = fmaf(-(p * mult), g, bamax);
+  return r > 0.0f ? ch : (r < 0.0f ? cl : ((cl & 1u) ? ch : cl));
+}
+
+// E2M1 magnitude of |x| / (s g) given bracket magnitudes ml < mh (E2M1
+// magnitude codes, mh = ml + 1); sd = s as fp32.
+__device__ __forceinline__ uint32_t resolve_e2m1(float xabs, uint32_t ml, uint32_t mh, float sd, float g) {
+  const float one = e8m0_operand(127u);
+  const float2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ml | (mh << 4), one, 0);
+  const float p = 0.5f * (v.x + v.y);
+  const float r = fmaf(-(p * sd), g, xabs);
+  return r > 0.0f ? mh : (r < 0.0f ? ml : ((ml & 1u) ? mh : ml));
+}
+
+// Exact max->6 round-to-nearest encoding of flat slot s of a contiguous bf16
+// tensor from its 16-block (a: first half, b: second half), by the brackets
+// and the exact decisions above; a block holding a non-finite value gets
+// codes 0 and scale 0x7F.  cx and s_inv belong to the tensor scale times
+// xscale (a power of two) and the inputs are scaled by xscale too, which
+// leaves every quotient unchanged; cx.g must be at least 2^-100.
+__device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCtx& cx, const float2* s_inv,
+                                                float xscale, int64_t s, const u32x4_t& a, const u32x4_t& b) {
+  uint32_t bm = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bm = max(bm, max(a[i] & 0x7FFFu, (a[i] >> 16) & 0x7FFFu));
+    bm = max(bm, max(b[i] & 0x7FFFu, (b[i] >> 16) & 0x7FFFu));
+  }
+  uint32_t codes = 0u, scale = 0x7Fu;
+  if (bm < 0x7F80u) {
+    const float bamax = as_f(bm << 16) * xscale;
+    const float tl = fminf(bamax * cx.inv6_lo, 448.0f);
+    const float th = fminf(bamax * cx.inv6_hi, 448.0f);
+    const uint32_t sb2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
+    const uint32_t cl = sb2 & 0xFFu, ch = (sb2 >> 8) & 0xFFu;
+    const uint32_t c = cl == ch ? cl : resolve_e4m3(bamax, cl, ch, 6.0f, cx.g);
+    const float2 iv = s_inv[c];
+    const float sd = e4m3_value(c);
+    const u32x4_t own = (s & 1) ? b : a;
+    const float one = e8m0_operand(127u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = own[i >> 1];
+      const float v = ((i & 1) ? bf_hi(word) : bf_lo(word)) * xscale;
+      const uint32_t ka = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v * iv.x, 0.0f, one, 0) & 0xFu;
+      const uint32_t kb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v * iv.y, 0.0f, one, 0) & 0xFu;
+      uint32_t k = ka;
+      if (ka != kb) k = (ka & 8u) | resolve_e2m1(fabsf(v), ka & 7u, kb & 7u, sd, cx.g);
+      codes |= k << (4 * i);
+    }
+    scale = c;
+  }
+  *reinterpret_cast<uint32_t*>(q.codes + (s << 2)) = codes;
+  q.scales[s >> 1] = (uint8_t)scale;
+}
+
+// Lean max->6 round-to-nearest encoding of one raw bf16 slot (8 values, no
+// rotation, no counters), free of branches so that the compiler can overlap
+// consecutive slots.  The block amax comes from packed 16-bit maxima of the
+// bf16 bit patterns (the lane pair 2k, 2k+1 holds one 16-block and must
+// execute together).  Codes and scale byte come from the brackets and are
+// stored (both lanes of a pair store the same byte).  Returns true when the
+// slot must be recomputed exactly with nv_fix_slot_fma: a bracket disagreement on
+// the scale byte or on a code, or a non-finite value in the block.
+__device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_inv, const uint4& w,
+                                             uint32_t* codes_at, uint8_t* scale_at) {
+  ushort2_t m = __builtin_bit_cast(ushort2_t, w.x & 0x7FFF7FFFu);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.w & 0x7FFF7FFFu));
+  uint32_t bm = m.x > m.y ? m.x : m.y;
+  bm = max(bm, dpp_u32<kQuadXor1>(bm));
+  const float bamax = as_f(bm << 16);
+  // scale byte from both brackets (non-negative operands: sign bits clear; a
+  // non-finite block saturates here and is redone by the fix-up)
+  const float tl = fminf(bamax * cx.inv6_lo, 448.0f);
+  const float th = fminf(bamax * cx.inv6_hi, 448.0f);
+  // (the old operand of a packing conversion only fills bytes that are
+  // overwritten or ignored: a dead value avoids a register copy)
+  const uint32_t sb2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, (int)as_u(th), false);
+  const uint32_t c = sb2 & 0x7Fu;
+  const float2 iv = s_inv[c];
+  const float one = e8m0_operand(127u);
+  uint32_t ca = 0u, cb = 0u;
+#define FP4Q_PAIR(K, WK)                                                                          \
+  {                                                                                               \
+    const float lo = bf_lo(WK), hi = bf_hi(WK);                                                   \
+    const float al = lo * iv.x, ah = hi * iv.x, bl = lo * iv.y, bh = hi * iv.y;                   \
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(al) : ca, al, ah, one, K);        \
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(bl) : cb, bl, bh, one, K);        \
+  }
+  FP4Q_PAIR(0, w.x)
+  FP4Q_PAIR(1, w.y)
+  FP4Q_PAIR(2, w.z)
+  FP4Q_PAIR(3, w.w)
+#undef FP4Q_PAIR
+  *codes_at = ca;
+  *scale_at = (uint8_t)c;
+  return ((ca ^ cb) | ((sb2 ^ (sb2 >> 8)) & 0xFFu)) != 0u || bm >= 0x7F80u;
+}
+
+}  // namespace fp4q

@@ -1,0 +1,388 @@
+// fp4q_nv_resident.hip -- single-launch NVFP4 quantization that reads most of
+// the tensor from HBM once (gfx950: one 1024-thread workgroup per CU).
+//
+// Same computation as fp4q_nv.hip ("Sub-4-Bit Microscaling", section 2:
+// g = amax / (6 * 448), s = RNE_E4M3(bamax / (6 g)), code = RNE_E2M1(x /
+// (s g))), restricted to round-to-nearest without rotation on contiguous bf16:
+//
+//  phase 1  each workgroup owns a contiguous chunk of up to 32 sixteen-byte
+//           slots per thread.  Slots 0-12 go to VGPRs, 13-21 to LDS (direct
+//           global->LDS loads), the rest are only scanned for the maximum
+//           (cached loads, so the Infinity Cache holds them for phase 2);
+//  barrier  every workgroup publishes (epoch, chunk max) in a 64-bit flag of
+//           its own; workgroup 0 polls all flags in parallel, folds the
+//           maxima and publishes (epoch, tensor max) in one word the others
+//           poll -- no contended counter, relaxed atomics only (each word
+//           carries its own payload);
+//  phase 2  codes and scales from the on-chip slots, then from the re-read
+//           slots (prefetched ahead), in straight-line code; a thread that
+//           met a bracket disagreement or a non-finite block recomputes its
+//           slots exactly at the end.
+//
+// The launch is an ordinary one with at most one workgroup per CU.  Results
+// never depend on the workgroups being resident together: every wait is
+// bounded in time, and a workgroup whose wait runs out takes the tensor
+// maximum from a scan of the whole input instead (same value, only slower).
+// The epoch is a per-call number from the host, so flags left by an earlier
+// call never match; the workspace must be zero-filled before its first use.
+//
+// The 8192 x 8192 bf16 activation is 256 x 1024 x 32 slots: 69% stays on chip.
+#include <atomic>
+#include <utility>
+
+#include "fp4q_flat.h"
+#include "fp4q_nv_common.h"
+
+namespace fp4q {
+namespace {
+
+constexpr int kResThreads = 1024;
+constexpr int kRegSlots = 13;
+constexpr int kLdsSlots = 9;
+constexpr int kMaxSlots = 32;
+constexpr int kReSlots = kMaxSlots - kRegSlots - kLdsSlots;   // 10
+constexpr int kAhead = 4;                                      // re-read prefetch depth
+constexpr uint64_t kWaitTicks = 100000;    // 1 ms of the 100 MHz real-time counter
+constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint32_t raw_finite_absmax(const uint4& w) {
+  ushort2_t m = __builtin_bit_cast(ushort2_t, w.x & 0x7FFF7FFFu);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.w & 0x7FFF7FFFu));
+  uint32_t mx = m.x > m.y ? m.x : m.y;
+  if (mx >= 0x7F80u) {   // a non-finite value is present: take the finite max only
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    mx = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = ws[i] & 0x7FFFu, hi = (ws[i] >> 16) & 0x7FFFu;
+      if (lo < 0x7F80u) mx = max(mx, lo);
+      if (hi < 0x7F80u) mx = max(mx, hi);
+    }
+  }
+  return mx << 16;   // fp32 bit pattern of the max
+}
+
+// slot j of thread t is workgroup slot j * 1024 + t: byte offset 16 t + 16384 j
+__device__ __forceinline__ const uint16_t* slot_ptr(const uint16_t* wg_x, int j, int tid) {
+  return wg_x + (size_t)j * kResThreads * 8 + (uint32_t)tid * 8u;
+}
+
+template <int... J>
+__device__ __forceinline__ void load_reg_slots(uint4 (&r)[kRegSlots], const uint16_t* wg_x, int tid, int nres,
+                                               uint32_t n_valid, std::integer_sequence<int, J...>) {
+  auto one = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    r[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < nres && (uint32_t)(j * kResThreads + tid) < n_valid) {
+      const u32x4_t a = load16<true>(slot_ptr(wg_x, j, tid));
+      r[j] = make_uint4(a.x, a.y, a.z, a.w);
+    }
+  };
+  (one(std::integral_constant<int, J>{}), ...);
+}
+
+template <int... J>
+__device__ __forceinline__ uint32_t reg_slots_absmax(const uint4 (&r)[kRegSlots], std::integer_sequence<int, J...>) {
+  uint32_t acc = 0u;
+  ((acc = max(acc, raw_finite_absmax(r[J]))), ...);
+  return acc;
+}
+
+__device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, int j, int tid, int nres, uint32_t n_valid) {
+  if (j < nres && (uint32_t)(j * kResThreads + tid) < n_valid) {
+    const u32x4_t a = load16<false>(slot_ptr(wg_x, j, tid));
+    return make_uint4(a.x, a.y, a.z, a.w);
+  }
+  return make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Phase-2 state of one thread.  GUARD is false when every workgroup holds
+// exactly kMaxSlots full slot rows: then no slot needs a bounds test and the
+// encoding is straight-line code.  redo: bit j set when this thread must
+// recompute its slot j exactly (about one element in 2000 on Student-t
+// data: bf16 inputs put many quotients within 2^-22 of a rounding boundary).
+template <bool GUARD>
+struct Phase2 {
+  const NvCtx& cx;
+  const float2* s_inv;
+  uint8_t* codes_wg;     // this workgroup's first code byte
+  uint8_t* scales_wg;    // this workgroup's first scale byte
+  int tid, nres;
+  uint32_t n_valid;
+  uint32_t redo;
+
+  __device__ __forceinline__ void slot(int j, uint4 w) {
+    if (GUARD && j >= nres) return;
+    const uint32_t ls = (uint32_t)(j * kResThreads + tid);
+    // per-slot scalar bases plus the per-thread offset
+    uint32_t* cp = reinterpret_cast<uint32_t*>(codes_wg + (size_t)j * (kResThreads * 4)) + tid;
+    uint8_t* sp = scales_wg + (size_t)j * (kResThreads / 2) + (tid >> 1);
+    bool need = false;
+    if constexpr (GUARD) {
+      if (ls < n_valid) need = nv_fast_slot(cx, s_inv, w, cp, sp);
+    } else {
+      need = nv_fast_slot(cx, s_inv, w, cp, sp);
+    }
+    redo |= (need ? 1u : 0u) << j;
+  }
+};
+
+template <class P, int... J>
+__device__ __forceinline__ void encode_reg_slots(P& p, const uint4 (&r)[kRegSlots], std::integer_sequence<int, J...>) {
+  (p.slot(J, r[J]), ...);
+}
+
+template <class P, int... J>
+__device__ __forceinline__ void encode_lds_slots(P& p, const uint4* s_data, std::integer_sequence<int, J...>) {
+  (p.slot(kRegSlots + J, s_data[J * kResThreads + p.tid]), ...);
+}
+
+// the re-read slots with a kAhead-deep prefetch ring (compile-time indices)
+template <bool GUARD, class P, int... K>
+__device__ __forceinline__ void encode_reread_slots(P& p, uint4 (&pre)[kAhead], const uint16_t* wg_x,
+                                                    std::integer_sequence<int, K...>) {
+  constexpr int j0 = kRegSlots + kLdsSlots;
+  auto one = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const uint4 w = pre[k % kAhead];
+    if constexpr (k + kAhead < kReSlots) {
+      if constexpr (GUARD) {
+        pre[k % kAhead] = load_cached(wg_x, j0 + k + kAhead, p.tid, p.nres, p.n_valid);
+      } else {
+        const u32x4_t a = load16<false>(slot_ptr(wg_x, j0 + k + kAhead, p.tid));
+        pre[k % kAhead] = make_uint4(a.x, a.y, a.z, a.w);
+      }
+    }
+    p.slot(j0 + k, w);
+  };
+  (one(std::integral_constant<int, K>{}), ...);
+}
+
+// Tensor maximum (finite bf16 magnitudes, as an fp32 bit pattern) from a scan
+// of the whole input by one workgroup: the fallback of a wait that ran out.
+__device__ uint32_t scan_tensor_amax(const QuantLaunch& q, uint32_t* s_red) {
+  const uint16_t* x = static_cast<const uint16_t*>(q.x);
+  const int tid = threadIdx.x;
+  uint32_t acc = 0u;
+  for (int64_t sl = tid; sl < q.nslots; sl += kResThreads) {
+    const u32x4_t a = load16<false>(x + (sl << 3));
+    acc = max(acc, raw_finite_absmax(make_uint4(a.x, a.y, a.z, a.w)));
+  }
+  acc = wave_max_u32(acc);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[tid >> 6] = acc;
+  __syncthreads();
+  uint32_t m = 0u;
+#pragma unroll
+  for (int w = 0; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
+  __syncthreads();
+  return m;
+}
+
+// Poll *p until its high word equals epoch; false if the wait runs out.
+__device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, uint64_t& f) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < kSpinLimit; ++it) {
+    f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(f >> 32) == epoch) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+template <bool GUARD>
+__global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch q, int nres, unsigned char* ws,
+                                                                     uint32_t epoch) {
+  __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 147,456 bytes
+  __shared__ float2 s_inv[128];
+  __shared__ uint32_t s_red[kResThreads / 64];
+  __shared__ uint32_t s_timeout;
+  __shared__ uint32_t s_amax;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = gridDim.x;
+  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);                           // [1] tensor max word
+  uint64_t* flags = reinterpret_cast<uint64_t*>(ws + kWsFlagsOffsetBytes);   // one per workgroup
+  const int64_t chunk = (int64_t)kResThreads * nres;
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  const int64_t rem = q.nslots - base;
+  const uint32_t n_valid = (uint32_t)(rem < chunk ? (rem > 0 ? rem : 0) : chunk);
+  const uint16_t* wg_x = static_cast<const uint16_t*>(q.x) + (base << 3);
+  if (tid == 0) s_timeout = 0u;
+
+  // ---------------- phase 1
+  uint4 r[kRegSlots];
+  load_reg_slots(r, wg_x, tid, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
+  for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
+    const uint32_t ls0 = (uint32_t)(j * kResThreads + wv * 64);            // first slot of this wave
+    if (ls0 < n_valid) {
+      // lane l lands at s_data[(j - kRegSlots) * 1024 + wv * 64 + l]; a lane past
+      // the end re-reads the wave's first slot (in bounds) and is never used
+      const uint32_t ls = ls0 + (uint32_t)lane;
+      const uint32_t src = ls < n_valid ? ls : ls0;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(wg_x + (size_t)src * 8u),
+                                       (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
+    }
+  }
+  uint32_t acc = 0u;
+  for (int j = kRegSlots + kLdsSlots; j < nres; ++j) acc = max(acc, raw_finite_absmax(load_cached(wg_x, j, tid, nres, n_valid)));
+  acc = max(acc, reg_slots_absmax(r, std::make_integer_sequence<int, kRegSlots>{}));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
+    if ((uint32_t)(j * kResThreads + tid) < n_valid) acc = max(acc, raw_finite_absmax(s_data[(j - kRegSlots) * kResThreads + tid]));
+  }
+  acc = wave_max_u32(acc);
+  if (lane == 0) s_red[wv] = acc;
+  __syncthreads();
+
+  // ---------------- grid-wide exchange of the chunk maxima
+  if (tid == 0) {
+    uint32_t m = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
+    __hip_atomic_store(flags + blockIdx.x, ((uint64_t)epoch << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  uint32_t amax_bits = 0u;
+  if (blockIdx.x == 0) {
+    uint32_t m = 0u;
+    for (int i = tid; i < G; i += kResThreads) {
+      uint64_t f = 0;
+      if (!wait_epoch(flags + i, epoch, f)) s_timeout = 1u;
+      m = max(m, (uint32_t)f);
+    }
+    m = wave_max_u32(m);
+    __syncthreads();
+    if (lane == 0) s_red[wv] = m;
+    __syncthreads();
+    m = 0u;
+#pragma unroll
+    for (int w = 0; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
+    if (s_timeout) m = scan_tensor_amax(q, s_red);
+    if (tid == 0) __hip_atomic_store(hdr + 1, ((uint64_t)epoch << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    amax_bits = m;
+  } else {
+    __syncthreads();   // s_red is reused below
+    if (tid == 0) {
+      uint64_t f = 0;
+      if (wait_epoch(hdr + 1, epoch, f)) s_red[0] = (uint32_t)f;
+      else s_timeout = 1u;
+    }
+    __syncthreads();
+    amax_bits = s_timeout ? scan_tensor_amax(q, s_red) : s_red[0];
+  }
+
+  NvCtx cx;
+  nv_context(as_f(amax_bits), false, cx);
+  nv_fill_inverse_table(s_inv, cx, tid, kResThreads);
+  if (tid == 0) {
+    s_amax = amax_bits;
+    if (blockIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
+  }
+  __syncthreads();
+
+  // ---------------- phase 2
+  // (slot indices are recomputed from an opaque copy of the thread id: keeping
+  // them alive from phase 1 would cost registers)
+  int tid2 = tid;
+  asm volatile("" : "+v"(tid2));
+  uint4 pre[kAhead];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    if constexpr (GUARD) {
+      pre[k] = load_cached(wg_x, kRegSlots + kLdsSlots + k, tid2, nres, n_valid);
+    } else {
+      const u32x4_t a = load16<false>(slot_ptr(wg_x, kRegSlots + kLdsSlots + k, tid2));
+      pre[k] = make_uint4(a.x, a.y, a.z, a.w);
+    }
+  }
+  Phase2<GUARD> p2{cx, s_inv, q.codes + (base << 2), q.scales + (base >> 1), tid2, nres, n_valid, 0u};
+  encode_reg_slots(p2, r, std::make_integer_sequence<int, kRegSlots>{});
+  encode_lds_slots(p2, s_data, std::make_integer_sequence<int, kLdsSlots>{});
+  encode_reread_slots<GUARD>(p2, pre, wg_x, std::make_integer_sequence<int, kReSlots>{});
+  // exact recomputations, after this thread's fast stores: program order per
+  // address keeps the exact values last
+  // Exact recomputations, after this thread's fast stores (program order per
+  // address keeps the exact values last).  The context is rebuilt from LDS so
+  // that phase 2 keeps only the two bracket factors in registers.  With
+  // g < 2^-100 every slot is redone on inputs and g scaled by 2^100 (exact
+  // power-of-two scaling: the quotients are unchanged and nothing underflows).
+  asm volatile("" ::: "memory");
+  uint32_t redo = p2.redo;
+  NvCtx cf;
+  nv_context(as_f(s_amax), false, cf);
+  float xscale = 1.0f;
+  if (cf.exact_all) {
+    xscale = 0x1p100f;
+    nv_context_g(cf.g * xscale, cf);
+    __syncthreads();
+    nv_fill_inverse_table(s_inv, cf, tid2, kResThreads);
+    __syncthreads();
+    redo = 0u;
+    for (int j = 0; j < nres; ++j) redo |= ((uint32_t)(j * kResThreads + tid2) < n_valid ? 1u : 0u) << j;
+  }
+  // two slots per round, both blocks in flight together
+  const uint16_t* xs = static_cast<const uint16_t*>(q.x);
+  while (redo != 0u) {
+    const int j0 = __builtin_ctz(redo);
+    redo &= redo - 1u;
+    const bool two = redo != 0u;
+    const int j1 = two ? __builtin_ctz(redo) : j0;
+    if (two) redo &= redo - 1u;
+    const int64_t s0 = base + (int64_t)(j0 * kResThreads + tid2);
+    const int64_t s1 = base + (int64_t)(j1 * kResThreads + tid2);
+    const u32x4_t a0 = load16<false>(xs + ((s0 & ~(int64_t)1) << 3)), b0 = load16<false>(xs + ((s0 | 1) << 3));
+    const u32x4_t a1 = load16<false>(xs + ((s1 & ~(int64_t)1) << 3)), b1 = load16<false>(xs + ((s1 | 1) << 3));
+    nv_fix_slot_fma(q, cf, s_inv, xscale, s0, a0, b0);
+    if (two) nv_fix_slot_fma(q, cf, s_inv, xscale, s1, a1, b1);
+  }
+}
+
+// Per-call epoch: flags written by earlier calls never carry it (0 is the
+// value of a freshly zeroed workspace and is skipped).
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0u};
+  uint32_t e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  if (e == 0u) e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return e;
+}
+
+hipError_t launch_resident(const QuantLaunch& q, int grid, int nres, hipStream_t st) {
+  unsigned char* ws = reinterpret_cast<unsigned char*>(q.partials);
+  const uint32_t epoch = next_epoch();
+  // every workgroup full: kMaxSlots slot rows each and nothing left over
+  const bool full = nres == kMaxSlots && q.nslots == (int64_t)grid * kResThreads * kMaxSlots;
+  if (full) {
+    hipLaunchKernelGGL((nv_resident_kernel<false>), dim3(grid), dim3(kResThreads), 0, st, q, nres, ws, epoch);
+  } else {
+    hipLaunchKernelGGL((nv_resident_kernel<true>), dim3(grid), dim3(kResThreads), 0, st, q, nres, ws, epoch);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Whether the single-launch kernel takes this call, and its launch shape.
+bool nv_resident_shape(const QuantLaunch& q, int* grid, int* nres) {
+  if (q.in_dtype != kBF16 || q.four_over_six || q.global_amax || q.stride != q.cols || q.nslots == 0) return false;
+  if (q.rotation != kRotNone || q.stochastic || q.counters) return false;   // those variants stream twice
+  const int cus = device_cu_count();
+  int64_t g = (q.nslots + kResThreads - 1) / kResThreads;
+  if (g > cus) g = cus;
+  if (g > kAmaxPartialsMax) return false;
+  const int64_t n = (q.nslots + g * kResThreads - 1) / (g * kResThreads);
+  if (n > kMaxSlots) return false;
+  *grid = (int)g;
+  *nres = (int)n;
+  return true;
+}
+
+hipError_t launch_nv_resident(const QuantLaunch& q, int grid, int nres, hipStream_t st) {
+  return launch_resident(q, grid, nres, st);
+}
+
+}  // namespace fp4q
