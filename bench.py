@@ -3,13 +3,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
+    python bench.py --profile-kernels   # a few launches of each kernel, for rocprofv3
+
 A step is one NVFP4 quantization of the 8192x8192 bf16 activation tensor
-(2 * Student-t(4), seed 102): the in-call tensor-amax pass, then the encode
-pass writing E2M1 codes, E4M3 block scales and the fp32 tensor scale.  Inputs
-are resident in HBM before timing; the step cycles over 4 replicas of the
-input (4 x 128 MiB) so every step reads an input the Infinity Cache no longer
-holds.  value = algorithmic bytes (read the input once, write every output
-once) x K / wall time of the K steps.
+(2 * Student-t(4), seed 102): tensor amax computed in the call, E2M1 codes,
+E4M3 block scales and the fp32 tensor scale (one launch of the single-read
+kernel).  Inputs are resident in HBM before timing; the step cycles over 4
+replicas of the input (4 x 128 MiB) so every step reads an input the Infinity
+Cache no longer holds.  value = algorithmic bytes (read the input once, write
+every output once) x K / wall time of the K steps.
 
 The same line carries the MXFP4 quantization of the same tensor and the
 NVFP4 dequantization back to bf16 as sub-objects, the roofline of the
@@ -60,21 +62,100 @@ def traffic_for(kernel, launch_units=1):
     return int(k["hbm_bytes_per_launch"]) * launch_units
 
 
-def cpu_baseline(x_np):
-    """The oracle, untuned, on the first 512 rows (4 Mi elements) of the workload."""
-    import numpy as np  # noqa: F401
+def cpu_baseline(x_np, rows=4096, min_seconds=10.0, max_reps=4):
+    """The oracle, untuned and single-threaded, on the first `rows` rows of the
+    workload, repeated until about `min_seconds` of CPU work."""
     import oracle
-    rows = 512
     sample = x_np[:rows]
-    t = time.perf_counter()
-    oracle.quantize_nv(sample)
-    dt = time.perf_counter() - t
-    elems = rows * COLS
+    reps, dt = 0, 0.0
+    while reps < max_reps and (reps == 0 or dt < min_seconds):
+        t = time.perf_counter()
+        oracle.quantize_nv(sample)
+        dt += time.perf_counter() - t
+        reps += 1
+    elems = rows * COLS * reps
     gbps = elems * (NV_BYTES / N) / dt / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "NVFP4 quantize of rows 0..511 (4,194,304 elements) of the 8192x8192 workload, "
-                      "single-threaded C oracle, %.2f s" % dt,
+            "sample": "NVFP4 quantize (tensor amax, scales, codes) of rows 0..%d (%d elements) of the 8192x8192 "
+                      "workload, %d pass(es), single-threaded C oracle, %.1f s" % (rows - 1, rows * COLS, reps, dt),
             "elements_per_s": round(elems / dt, 1)}
+
+
+def profile_kernels(dev, reps=5):
+    """A few launches of every kernel on the five workloads' full sizes, plus a
+    plain 128 MiB device copy (the reference for HBM byte counters).  Prints
+    one text line per kernel with its average event time."""
+    import numpy as np
+    import torch
+
+    import fp4_block_scaled_row_amd as fq
+    import workloads
+
+    def dev_tensor(name):
+        x = workloads.make(name)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    def run(label, fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print("%-58s %9.2f us  %8.1f GB/s" % (label, us, nbytes / us / 1e3), flush=True)
+
+    src = torch.empty(BYTES_IN, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    run("copy 128 MiB (reference for byte counters)", lambda: dst.copy_(src), 2 * BYTES_IN)
+    del src, dst
+
+    x = dev_tensor("act_bf16_8192")
+    ws = torch.zeros(fq.workspace_bytes(16), dtype=torch.uint8, device=dev)
+    o = fq.quantize_nvfp4(x, workspace=ws)
+    run("C2 NVFP4 bf16 8192x8192, amax in call", lambda: fq.quantize_nvfp4(x, out=o, workspace=ws), NV_BYTES)
+    amax = torch.max(torch.abs(x.float())).reshape(1)
+    run("C2 NVFP4 bf16 8192x8192, amax given (encode pass)",
+        lambda: fq.quantize_nvfp4(x, out=o, global_amax=amax), NV_BYTES)
+    ox = fq.quantize_mxfp4(x)
+    run("H2 MXFP4 bf16 8192x8192", lambda: fq.quantize_mxfp4(x, out=ox), MX_BYTES)
+    y = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=dev)
+    run("C2 dequantize NVFP4 -> bf16 8192x8192",
+        lambda: fq.dequantize("nvfp4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=y), DQ_BYTES)
+    o5 = fq.quantize_nvfp4(x, rotation="rht16", rounding="stochastic", seed=workloads.SR_SEED, workspace=ws)
+    run("C5 RHT16 + stochastic NVFP4 bf16 8192x8192",
+        lambda: fq.quantize_nvfp4(x, rotation="rht16", rounding="stochastic", seed=workloads.SR_SEED, out=o5,
+                                  workspace=ws), NV_BYTES)
+    del x, o, ox, y, o5
+
+    x3 = dev_tensor("swiglu_bf16_16384x8192")
+    o3 = fq.quantize_mxfp4(x3, rotation="fwht_row")
+    n3 = x3.numel()
+    run("C3 FWHT-8192 + MXFP4 bf16 16384x8192",
+        lambda: fq.quantize_mxfp4(x3, rotation="fwht_row", out=o3), n3 * 2 + n3 // 2 + n3 // 32)
+    del x3, o3
+
+    x4 = dev_tensor("weight_bf16_8192x28672")
+    o4 = fq.quantize_nvfp4(x4, policy="four_over_six", workspace=ws)
+    n4 = x4.numel()
+    run("C4 Four-Over-Six NVFP4 bf16 8192x28672",
+        lambda: fq.quantize_nvfp4(x4, policy="four_over_six", out=o4, workspace=ws),
+        n4 * 2 + n4 // 2 + n4 // 16 + 4 + n4 // 128)
+    del x4, o4
+
+    x1 = dev_tensor("mx_f32_1024")
+    o1 = fq.quantize_mxfp4(x1, counters=True)
+    y1 = torch.empty_like(x1)
+    n1 = x1.numel()
+    run("C1 MXFP4 fp32 1024x1024 (with counters)", lambda: fq.quantize_mxfp4(x1, counters=True, out=o1),
+        n1 * 4 + n1 // 2 + n1 // 32)
+    run("C1 dequantize MXFP4 -> fp32 1024x1024",
+        lambda: fq.dequantize("mxfp4", o1.codes, o1.scales, out_dtype=torch.float32, out=y1), n1 // 2 + n1 // 32 + n1 * 4)
 
 
 def main():
@@ -83,6 +164,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="launch each kernel of the five workloads a few times (for rocprofv3) and print "
+                         "event timings as text; no JSON line")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py: this build runs on one GPU only (no collectives or sharding); "
@@ -96,6 +180,9 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    if a.profile_kernels:
+        profile_kernels(dev)
+        return
     x_np = workloads.make("act_bf16_8192")
     x0 = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
     xs = [x0] + [x0.clone() for _ in range(REPLICAS - 1)]
@@ -135,13 +222,17 @@ def main():
         torch.cuda.synchronize()
         return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps / 1e3
 
-    # ---- headline: NVFP4 quantize (amax pass + encode pass), K steps
+    # ---- headline: NVFP4 quantize, K steps (one launch of nv_resident_kernel each)
     sec = timed(nv_step, a.steps, a.warmup)
     value = NV_BYTES / sec / 1e9
 
-    # ---- roofline of the dominant kernel: the encode pass (nv_quant_kernel)
-    # launched alone with the tensor amax handed in, after an untimed amax
-    # pass on the same replica so its input is where the real step finds it.
+    # ---- roofline of the dominant kernel: the single-read NVFP4 kernel, the
+    # only launch of a step, timed with events around each call
+    call_sec = event_avg(nv_step, a.steps)
+    call_gbps = NV_BYTES / call_sec / 1e9
+
+    # ---- the two-pass NVFP4 encode (used when the caller hands in the
+    # tensor amax, and for shapes the single-read kernel does not take)
     for k in range(REPLICAS):
         amax_dev[k].copy_(torch.max(torch.abs(xs[k].float())).reshape(1))
     torch.cuda.synchronize()
@@ -153,8 +244,6 @@ def main():
     for i in range(a.warmup):
         encode_only(i)
     enc_sec = event_avg(encode_only, a.steps, pre=nv_step)
-    call_sec = event_avg(nv_step, a.steps)
-    enc_gbps = NV_BYTES / enc_sec / 1e9
 
     # ---- MXFP4 of the same tensor
     def mx_step(i):
@@ -188,13 +277,15 @@ def main():
                    "rows": ROWS, "cols": COLS, "algorithmic_bytes_per_step": NV_BYTES,
                    "elements_per_s": round(N / sec, 1), "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
                    "input_replicas": REPLICAS},
-        "roofline": {"bound": "hbm", "kernel": "nv_quant_kernel (encode pass)",
-                     "achieved": round(enc_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
-                     "avg_launch_us": round(enc_sec * 1e6, 3),
+        "roofline": {"bound": "hbm", "kernel": "nv_resident_kernel",
+                     "achieved": round(call_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(call_gbps / HBM_PEAK_GBPS, 4),
+                     "avg_launch_us": round(call_sec * 1e6, 3),
                      "bytes_per_launch": NV_BYTES,
-                     "traffic": traffic_for("nv_quant_kernel")},
-        "nvfp4_call_event_us": round(call_sec * 1e6, 3),
+                     "traffic": traffic_for("nv_resident_kernel")},
+        "nvfp4_encode_given_amax": {"kernel": "nv_quant_kernel", "event_us": round(enc_sec * 1e6, 3),
+                                    "value": round(NV_BYTES / enc_sec / 1e9, 2), "unit": "GB/s",
+                                    "traffic": traffic_for("nv_quant_kernel")},
         "mxfp4": {"value": round(MX_BYTES / mx_sec / 1e9, 2), "unit": "GB/s",
                   "frac_of_hbm_peak": round(MX_BYTES / mx_sec / 1e9 / HBM_PEAK_GBPS, 4),
                   "ms_per_step": round(mx_sec * 1e3, 5), "event_us": round(mx_ev * 1e6, 3),

@@ -31,9 +31,10 @@ struct QuantLaunch {
 };
 
 constexpr int kAmaxPartialsMax = 1024;  // workgroups of the NV amax pass
-// NVFP4 workspace layout (bytes): [0, 64) epoch and release words of the
-// single-launch kernel, [64, 64 + 8 * 1024) its per-workgroup flags,
-// [8256, 8256 + 4 * 1024) the amax partials of the two-pass kernels.
+// NVFP4 workspace layout (bytes): [0, 64) header of the single-launch kernel
+// (word 1: tensor max, word 2: wait limit override), [64, 64 + 8 * 1024) its
+// per-workgroup flags, [8256, 8256 + 4 * 1024) the amax partials of the
+// two-pass kernels.
 constexpr size_t kWsFlagsOffsetBytes = 64;
 constexpr size_t kWsPartialsOffsetBytes = kWsFlagsOffsetBytes + 8 * kAmaxPartialsMax;
 constexpr size_t kNvWorkspaceBytes = 16384;

@@ -42,7 +42,7 @@ constexpr int kLdsSlots = 9;
 constexpr int kMaxSlots = 32;
 constexpr int kReSlots = kMaxSlots - kRegSlots - kLdsSlots;   // 10
 constexpr int kAhead = 4;                                      // re-read prefetch depth
-constexpr uint64_t kWaitTicks = 100000;    // 1 ms of the 100 MHz real-time counter
+constexpr uint64_t kWaitTicks = 100000;    // 1 ms of the 100 MHz real-time counter (default)
 constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -183,13 +183,14 @@ __device__ uint32_t scan_tensor_amax(const QuantLaunch& q, uint32_t* s_red) {
   return m;
 }
 
-// Poll *p until its high word equals epoch; false if the wait runs out.
-__device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, uint64_t& f) {
+// Poll *p until its high word equals epoch; false if the wait (limit in
+// ticks of the 100 MHz counter) runs out.
+__device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, uint64_t limit, uint64_t& f) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < kSpinLimit; ++it) {
     f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(f >> 32) == epoch) return true;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > limit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
   __shared__ uint32_t s_amax;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = gridDim.x;
-  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);                           // [1] tensor max word
+  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);   // [1] tensor max word, [2] wait limit override
   uint64_t* flags = reinterpret_cast<uint64_t*>(ws + kWsFlagsOffsetBytes);   // one per workgroup
   const int64_t chunk = (int64_t)kResThreads * nres;
   const int64_t base = (int64_t)blockIdx.x * chunk;
@@ -241,6 +242,10 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
   __syncthreads();
 
   // ---------------- grid-wide exchange of the chunk maxima
+  // (a nonzero header word 2 replaces the default wait limit: tests set it
+  // to a few ticks to drive the fallback scan)
+  const uint64_t lim_set = hdr[2];
+  const uint64_t limit = lim_set ? lim_set : kWaitTicks;
   if (tid == 0) {
     uint32_t m = s_red[0];
 #pragma unroll
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
     uint32_t m = 0u;
     for (int i = tid; i < G; i += kResThreads) {
       uint64_t f = 0;
-      if (!wait_epoch(flags + i, epoch, f)) s_timeout = 1u;
+      if (!wait_epoch(flags + i, epoch, limit, f)) s_timeout = 1u;
       m = max(m, (uint32_t)f);
     }
     m = wave_max_u32(m);
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
     __syncthreads();   // s_red is reused below
     if (tid == 0) {
       uint64_t f = 0;
-      if (wait_epoch(hdr + 1, epoch, f)) s_red[0] = (uint32_t)f;
+      if (wait_epoch(hdr + 1, epoch, limit, f)) s_red[0] = (uint32_t)f;
       else s_timeout = 1u;
     }
     __syncthreads();

@@ -106,8 +106,10 @@ def test_nv_bf16_8192_headline_and_dequant():
     assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
     d16 = fq.dequantize("nvfp4", r.codes, r.scales, r.global_scale, out_dtype=torch.bfloat16)
     assert_same(host(d16), oracle.dequantize(oracle.NV, c, s, g, out_dtype=oracle.BF16), "dequant bf16")
-    r2 = fq.quantize_nvfp4(xd)
-    assert_same(host(r2.codes), c, "codes (second call, no counters)")
+    r2 = fq.quantize_nvfp4(xd)            # no counters: the single-read kernel
+    assert host(r2.global_scale)[0] == g
+    assert_same(host(r2.scales), s, "scales (single-read kernel)")
+    assert_same(host(r2.codes), c, "codes (single-read kernel)")
 
 
 def test_fwht_mx_swiglu_16384x8192():
@@ -378,3 +380,60 @@ def test_deterministic_repeat():
             assert torch.equal(u, v)
     c = fq.quantize_nvfp4(x, policy="four_over_six", rounding="stochastic", rotation="rht16", seed=2)
     assert not torch.equal(a.codes, c.codes)
+
+
+# ------------------------------------------------------------------ single-read NVFP4 kernel
+# Contiguous bf16, max->6, RNE, no rotation, no counters, no caller amax: one
+# launch holding the tensor on chip.  Compared with the oracle like every
+# other path; the two-pass path is covered by the tests above (counters on).
+def _nv_single(x, ws=None):
+    xd = to_dev(x)
+    r = fq.quantize_nvfp4(xd, workspace=ws)
+    c, s, g, _, _ = oracle.quantize_nv(x)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    return r
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 64), (17, 96), (64, 256), (33, 544), (1000, 1024),
+                                       (2048, 4096), (4097, 2048), (8192, 8192 - 16)])
+def test_nv_single_read_shapes(rows, cols):
+    _nv_single(workloads.random_tensor(rows, cols, "bf16", rows + 3 * cols, scale=2.0, dist="t"))
+
+
+def test_nv_single_read_full_workgroups():
+    """64 Mi elements in a shape other than the headline: every workgroup full."""
+    x = workloads.random_tensor(4096, 16384, "bf16", 77, scale=2.0)
+    _nv_single(x)
+
+
+def test_nv_single_read_specials_and_ties():
+    _nv_single(_special_tensor("bf16"))
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
+    x = np.zeros((2, 64), np.float32)
+    x[0, 0] = 2688.0                      # g = 1 exactly: exact ties at every decision point
+    x[0, 16:32] = [9.0] + [m * 1.5 for m in mids] + [-m * 1.5 for m in mids[:7]]
+    x[1] = np.random.default_rng(1).standard_normal(64) * 3
+    _nv_single(f32_to_bf16_bits(x))
+
+
+@pytest.mark.parametrize("scale_exp", [-133, -120, -101, -60, 100, 120])
+def test_nv_single_read_tiny_and_huge(scale_exp):
+    rng = np.random.default_rng(scale_exp + 900)
+    x = np.ldexp(rng.standard_t(4, (8, 64)), scale_exp).astype(np.float32)
+    _nv_single(f32_to_bf16_bits(x))
+
+
+def test_nv_single_read_workspace_reuse_and_fallback():
+    """One workspace across calls of different sizes (stale flags must never
+    match), then a wait limit of one tick so every workgroup's wait runs out
+    and each takes the tensor maximum from its own scan."""
+    ws = torch.zeros(fq.workspace_bytes(16), dtype=torch.uint8, device=gpu())
+    for shape, seed in (((512, 4096), 1), ((64, 256), 2), ((2048, 8192), 3), ((512, 4096), 4)):
+        _nv_single(workloads.random_tensor(shape[0], shape[1], "bf16", seed, scale=2.0), ws)
+    ws.view(torch.int64)[2] = 1
+    for shape, seed in (((96, 1024), 5), ((1500, 2048), 6)):
+        _nv_single(workloads.random_tensor(shape[0], shape[1], "bf16", seed, scale=2.0), ws)
+    ws.view(torch.int64)[2] = 0
+    _nv_single(workloads.random_tensor(300, 4096, "bf16", 7, scale=2.0), ws)
