@@ -71,6 +71,74 @@ __device__ __forceinline__ void nv_fill_inverse_table(float2* s_inv, const NvCtx
   }
 }
 
+// Single adjusted multipliers for bf16 inputs.  A bf16 magnitude a has 8
+// significant bits, so within 2^-12 (relative) of a threshold T = p s g (p a
+// decision point of the E2M1 rounding, or 6 for the saturation count) lies
+// at most one bf16 value, at relative offset d = (a - T) / T, and every other
+// bf16 value is at least 2^-12 away.  m = (1 + eps) / (s g) rounded to fp32,
+// with |eps| <= 2^-14, keeps RN32(a m) on the same side of p as the exact
+// a / (s g) for all far values; for the near value it does so when
+// (1 + d)(1 + eps) is at least 1 + 2^-22 above (or below) 1 -- half an fp32
+// ulp of any p is at most 2^-24 relative, so the product rounds away from p,
+// and 2^-23 of slack covers the rounding of m itself.  An exact tie (d = 0)
+// must fall on the side of the even code.  The constraints of the 8 points
+// bound eps from both sides; the midpoint of the interval is taken, and a
+// code whose interval is empty is flagged so that its blocks take the exact
+// path.  Decision points and the side of their even neighbour:
+//   0.25 down, 0.75 up, 1.25 down, 1.75 up, 2.5 down, 3.5 up, 5 down, 6 down
+// (6 itself is not saturated).
+//
+// s_adj[c] = (m_c, flag) and s_br[c] = the 2^-22 brackets of 1/(s_c g) (for
+// the exact path), for every E4M3 code; c = 0 gives (0, 0) (every code of
+// such a block is a signed zero), c = 127 (NaN scale) is flagged.  Work item
+// t = 8 c + k of 1024 handles point k of code c; the 8 items of a code are
+// consecutive lanes of one wave (nthreads must be a multiple of 64).
+__device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_br, const NvCtx& cx, int tid,
+                                                       int nthreads) {
+#pragma unroll 1
+  for (int t = tid; t < 1024; t += nthreads) {
+    const uint32_t c = (uint32_t)t >> 3;
+    const int k = t & 7;
+    const double sg = (double)e4m3_value(c) * cx.g64;   // exact (4 x 24 bits)
+    double lo = -0x1p-14, hi = 0x1p-14;
+    if (c != 0u && c != 127u) {
+      const double p = k < 4 ? 0.25 + 0.5 * k : (k == 4 ? 2.5 : (k == 5 ? 3.5 : (k == 6 ? 5.0 : 6.0)));
+      const bool tie_up = k == 1 || k == 3 || k == 5;
+      const double T = p * sg;                            // exact (3 x 28 bits)
+      const double ulp = ldexp(1.0, ilogb(T) - 7);        // bf16 spacing at T
+      const double a0 = floor(T / ulp) * ulp;             // (division by a power of two: exact)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const double a = a0 + (double)i * ulp;
+        const double diff = a - T;                        // exact
+        if (fabs(diff) < 0x1p-12 * T) {                   // the near value (rare)
+          const double d = diff / T;
+          if (d > 0.0 || (d == 0.0 && tie_up)) lo = fmax(lo, (1.0 + 0x1p-22) / (1.0 + d) - 1.0);
+          else hi = fmin(hi, (1.0 - 0x1p-22) / (1.0 + d) - 1.0);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      lo = fmax(lo, __shfl_xor(lo, off));
+      hi = fmin(hi, __shfl_xor(hi, off));
+    }
+    if (k == 0) {
+      float2 adj = make_float2(0.0f, 1.0f), br = make_float2(0.0f, 0.0f);
+      if (c == 0u) {
+        adj = make_float2(0.0f, 0.0f);
+      } else if (c != 127u) {
+        const double inv = 1.0 / sg;
+        br = make_float2((float)(inv * (1.0 - 0x1p-22)), (float)(inv * (1.0 + 0x1p-22)));
+        adj = (lo + 0x1p-23 <= hi - 0x1p-23) ? make_float2((float)(inv * (1.0 + 0.5 * (lo + hi))), 0.0f)
+                                             : make_float2((float)inv, 1.0f);
+      }
+      s_adj[c] = adj;
+      s_br[c] = br;
+    }
+  }
+}
+
 // E4M3 block-scale byte RNE_E4M3(bamax / (mult g)), saturating at 448.  With
 // g < 2^-100 (exact_all) 1/(mult g) may not fit fp32, so the fp64 encoding
 // decides directly.
@@ -254,10 +322,11 @@ __device__ __forceinline__ uint32_t resolve_e2m1(float xabs, uint32_t ml, uint32
 // Exact max->6 round-to-nearest encoding of flat slot s of a contiguous bf16
 // tensor from its 16-block (a: first half, b: second half), by the brackets
 // and the exact decisions above; a block holding a non-finite value gets
-// codes 0 and scale 0x7F.  cx and s_inv belong to the tensor scale times
+// codes 0 and scale 0x7F.  cx and s_br (brackets of 1 / (s g) per scale
+// code, see nv_fill_adjusted_table) belong to the tensor scale times
 // xscale (a power of two) and the inputs are scaled by xscale too, which
 // leaves every quotient unchanged; cx.g must be at least 2^-100.
-__device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCtx& cx, const float2* s_inv,
+__device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCtx& cx, const float2* s_br,
                                                 float xscale, int64_t s, const u32x4_t& a, const u32x4_t& b) {
   uint32_t bm = 0u;
 #pragma unroll
@@ -273,7 +342,7 @@ __device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCt
     const uint32_t sb2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
     const uint32_t cl = sb2 & 0xFFu, ch = (sb2 >> 8) & 0xFFu;
     const uint32_t c = cl == ch ? cl : resolve_e4m3(bamax, cl, ch, 6.0f, cx.g);
-    const float2 iv = s_inv[c];
+    const float2 iv = s_br[c];
     const float sd = e4m3_value(c);
     const u32x4_t own = (s & 1) ? b : a;
     const float one = e8m0_operand(127u);
@@ -297,11 +366,12 @@ __device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCt
 // rotation, no counters), free of branches so that the compiler can overlap
 // consecutive slots.  The block amax comes from packed 16-bit maxima of the
 // bf16 bit patterns (the lane pair 2k, 2k+1 holds one 16-block and must
-// execute together).  Codes and scale byte come from the brackets and are
-// stored (both lanes of a pair store the same byte).  Returns true when the
-// slot must be recomputed exactly with nv_fix_slot_fma: a bracket disagreement on
-// the scale byte or on a code, or a non-finite value in the block.
-__device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_inv, const uint4& w,
+// execute together).  The scale byte comes from its brackets, the codes from
+// one product with the adjusted multiplier of that byte; both are stored
+// (both lanes of a pair store the same byte).  Returns true when the slot must
+// be recomputed exactly with nv_fix_slot_fma: the scale brackets disagree, the
+// scale code is flagged, or the block holds a non-finite value.
+__device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_adj, const uint4& w,
                                              uint32_t* codes_at, uint8_t* scale_at) {
   ushort2_t m = __builtin_bit_cast(ushort2_t, w.x & 0x7FFF7FFFu);
   m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.y & 0x7FFF7FFFu));
@@ -318,15 +388,13 @@ __device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_in
   // overwritten or ignored: a dead value avoids a register copy)
   const uint32_t sb2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, (int)as_u(th), false);
   const uint32_t c = sb2 & 0x7Fu;
-  const float2 iv = s_inv[c];
+  const float2 mf = s_adj[c];   // adjusted multiplier of this scale code, flag
   const float one = e8m0_operand(127u);
-  uint32_t ca = 0u, cb = 0u;
+  uint32_t ca = 0u;
 #define FP4Q_PAIR(K, WK)                                                                          \
   {                                                                                               \
-    const float lo = bf_lo(WK), hi = bf_hi(WK);                                                   \
-    const float al = lo * iv.x, ah = hi * iv.x, bl = lo * iv.y, bh = hi * iv.y;                   \
+    const float al = bf_lo(WK) * mf.x, ah = bf_hi(WK) * mf.x;                                     \
     ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(al) : ca, al, ah, one, K);        \
-    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(bl) : cb, bl, bh, one, K);        \
   }
   FP4Q_PAIR(0, w.x)
   FP4Q_PAIR(1, w.y)
@@ -335,7 +403,7 @@ __device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_in
 #undef FP4Q_PAIR
   *codes_at = ca;
   *scale_at = (uint8_t)c;
-  return ((ca ^ cb) | ((sb2 ^ (sb2 >> 8)) & 0xFFu)) != 0u || bm >= 0x7F80u;
+  return ((sb2 ^ (sb2 >> 8)) & 0xFFu) != 0u || mf.y != 0.0f || bm >= 0x7F80u;
 }
 
 }  // namespace fp4q

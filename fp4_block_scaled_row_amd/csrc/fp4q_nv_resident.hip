@@ -1,32 +1,33 @@
 // fp4q_nv_resident.hip -- single-launch NVFP4 quantization that reads most of
-// the tensor from HBM once (gfx950: one 1024-thread workgroup per CU).
+// the tensor from HBM once (gfx950: four 256-thread workgroups per CU).
 //
 // Same computation as fp4q_nv.hip ("Sub-4-Bit Microscaling", section 2:
 // g = amax / (6 * 448), s = RNE_E4M3(bamax / (6 g)), code = RNE_E2M1(x /
 // (s g))), restricted to round-to-nearest without rotation on contiguous bf16:
 //
 //  phase 1  each workgroup owns a contiguous chunk of up to 32 sixteen-byte
-//           slots per thread.  Slots 0-12 go to VGPRs, 13-21 to LDS (direct
-//           global->LDS loads), the rest are only scanned for the maximum
-//           (cached loads, so the Infinity Cache holds them for phase 2);
+//           slots per thread, each wave a contiguous run of them.  The first
+//           reg_slots() go to VGPRs (non-temporal loads), the next kLdsSlots to
+//           LDS (direct global->LDS loads), the rest are only scanned for the
+//           maximum (cached loads, so that phase 2 finds them closer);
 //  barrier  every workgroup publishes (epoch, chunk max) in a 64-bit flag of
-//           its own; workgroup 0 polls all flags in parallel, folds the
+//           its own; the last workgroup polls all flags in parallel, folds the
 //           maxima and publishes (epoch, tensor max) in one word the others
 //           poll -- no contended counter, relaxed atomics only (each word
 //           carries its own payload);
 //  phase 2  codes and scales from the on-chip slots, then from the re-read
-//           slots (prefetched ahead), in straight-line code; a thread that
-//           met a bracket disagreement or a non-finite block recomputes its
-//           slots exactly at the end.
+//           slots (prefetched ahead), in straight-line code; slots that need
+//           the exact path are recomputed at the end.
 //
-// The launch is an ordinary one with at most one workgroup per CU.  Results
-// never depend on the workgroups being resident together: every wait is
-// bounded in time, and a workgroup whose wait runs out takes the tensor
+// The launch is an ordinary one with at most kResPerCu workgroups per CU.
+// Results never depend on the workgroups being resident together: every wait
+// is bounded in time, and a workgroup whose wait runs out takes the tensor
 // maximum from a scan of the whole input instead (same value, only slower).
 // The epoch is a per-call number from the host, so flags left by an earlier
 // call never match; the workspace must be zero-filled before its first use.
 //
-// The 8192 x 8192 bf16 activation is 256 x 1024 x 32 slots: 69% stays on chip.
+// The 8192 x 8192 bf16 activation is 1024 x 256 x 32 slots on 256 CUs: 27 of
+// every 32 slots stay on chip.
 #include <atomic>
 #include <utility>
 
@@ -36,11 +37,16 @@
 namespace fp4q {
 namespace {
 
-constexpr int kResThreads = 1024;
-constexpr int kRegSlots = 13;
+constexpr int kResThreads = 256;
+constexpr int kResPerCu = 4;               // workgroups resident per CU
+// slots held in VGPRs: as many as fit in 128 registers without spilling (the
+// bounds-tested variant needs a few more registers of its own)
+template <bool GUARD>
+constexpr int reg_slots() { return GUARD ? 15 : 17; }
 constexpr int kLdsSlots = 9;
 constexpr int kMaxSlots = 32;
-constexpr int kReSlots = kMaxSlots - kRegSlots - kLdsSlots;   // 10
+template <bool GUARD>
+constexpr int reread_slots() { return kMaxSlots - reg_slots<GUARD>() - kLdsSlots; }
 constexpr int kAhead = 4;                                      // re-read prefetch depth
 constexpr uint64_t kWaitTicks = 100000;    // 1 ms of the 100 MHz real-time counter (default)
 constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
@@ -66,35 +72,39 @@ __device__ __forceinline__ uint32_t raw_finite_absmax(const uint4& w) {
   return mx << 16;   // fp32 bit pattern of the max
 }
 
-// slot j of thread t is workgroup slot j * 1024 + t: byte offset 16 t + 16384 j
-__device__ __forceinline__ const uint16_t* slot_ptr(const uint16_t* wg_x, int j, int tid) {
-  return wg_x + (size_t)j * kResThreads * 8 + (uint32_t)tid * 8u;
-}
+// Slot j of a lane is workgroup slot wbase + 64 j + lane, with wbase = 64 nres
+// times the wave's index: every wave streams one contiguous run of 64 nres
+// sixteen-byte slots (1 KiB per slot row), which HBM serves far better than
+// rows strided across the workgroup.
+__device__ __forceinline__ uint32_t slot_of(int wbase, int j, int lane) { return (uint32_t)(wbase + j * 64 + lane); }
 
-template <int... J>
-__device__ __forceinline__ void load_reg_slots(uint4 (&r)[kRegSlots], const uint16_t* wg_x, int tid, int nres,
-                                               uint32_t n_valid, std::integer_sequence<int, J...>) {
+__device__ __forceinline__ const uint16_t* slot_ptr(const uint16_t* wg_x, uint32_t ls) { return wg_x + (size_t)ls * 8u; }
+
+template <int RS, int... J>
+__device__ __forceinline__ void load_reg_slots(uint4 (&r)[RS], const uint16_t* wg_x, int wbase, int lane,
+                                               int nres, uint32_t n_valid, std::integer_sequence<int, J...>) {
   auto one = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
     r[j] = make_uint4(0u, 0u, 0u, 0u);
-    if (j < nres && (uint32_t)(j * kResThreads + tid) < n_valid) {
-      const u32x4_t a = load16<true>(slot_ptr(wg_x, j, tid));
+    const uint32_t ls = slot_of(wbase, j, lane);
+    if (j < nres && ls < n_valid) {
+      const u32x4_t a = load16<true>(slot_ptr(wg_x, ls));
       r[j] = make_uint4(a.x, a.y, a.z, a.w);
     }
   };
   (one(std::integral_constant<int, J>{}), ...);
 }
 
-template <int... J>
-__device__ __forceinline__ uint32_t reg_slots_absmax(const uint4 (&r)[kRegSlots], std::integer_sequence<int, J...>) {
+template <int RS, int... J>
+__device__ __forceinline__ uint32_t reg_slots_absmax(const uint4 (&r)[RS], std::integer_sequence<int, J...>) {
   uint32_t acc = 0u;
   ((acc = max(acc, raw_finite_absmax(r[J]))), ...);
   return acc;
 }
 
-__device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, int j, int tid, int nres, uint32_t n_valid) {
-  if (j < nres && (uint32_t)(j * kResThreads + tid) < n_valid) {
-    const u32x4_t a = load16<false>(slot_ptr(wg_x, j, tid));
+__device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, uint32_t ls, bool valid) {
+  if (valid) {
+    const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
     return make_uint4(a.x, a.y, a.z, a.w);
   }
   return make_uint4(0u, 0u, 0u, 0u);
@@ -108,52 +118,57 @@ __device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, int j, int ti
 template <bool GUARD>
 struct Phase2 {
   const NvCtx& cx;
-  const float2* s_inv;
+  const float2* s_adj;
   uint8_t* codes_wg;     // this workgroup's first code byte
   uint8_t* scales_wg;    // this workgroup's first scale byte
-  int tid, nres;
+  int wbase, lane, tid, nres;
   uint32_t n_valid;
   uint32_t redo;
 
   __device__ __forceinline__ void slot(int j, uint4 w) {
     if (GUARD && j >= nres) return;
-    const uint32_t ls = (uint32_t)(j * kResThreads + tid);
-    // per-slot scalar bases plus the per-thread offset
-    uint32_t* cp = reinterpret_cast<uint32_t*>(codes_wg + (size_t)j * (kResThreads * 4)) + tid;
-    uint8_t* sp = scales_wg + (size_t)j * (kResThreads / 2) + (tid >> 1);
+    const uint32_t ls = slot_of(wbase, j, lane);
+    uint32_t* cp = reinterpret_cast<uint32_t*>(codes_wg + (size_t)ls * 4u);
+    uint8_t* sp = scales_wg + (ls >> 1);
     bool need = false;
     if constexpr (GUARD) {
-      if (ls < n_valid) need = nv_fast_slot(cx, s_inv, w, cp, sp);
+      if (ls < n_valid) need = nv_fast_slot(cx, s_adj, w, cp, sp);
     } else {
-      need = nv_fast_slot(cx, s_inv, w, cp, sp);
+      need = nv_fast_slot(cx, s_adj, w, cp, sp);
     }
-    redo |= (need ? 1u : 0u) << j;
+    // (materialised in a VGPR at once: 32 pending lane masks would exhaust
+    // the scalar registers)
+    uint32_t bit = need ? (1u << j) : 0u;
+    asm volatile("" : "+v"(bit));
+    redo |= bit;
   }
 };
 
-template <class P, int... J>
-__device__ __forceinline__ void encode_reg_slots(P& p, const uint4 (&r)[kRegSlots], std::integer_sequence<int, J...>) {
+template <class P, int RS, int... J>
+__device__ __forceinline__ void encode_reg_slots(P& p, const uint4 (&r)[RS], std::integer_sequence<int, J...>) {
   (p.slot(J, r[J]), ...);
 }
 
-template <class P, int... J>
+template <int RS, class P, int... J>
 __device__ __forceinline__ void encode_lds_slots(P& p, const uint4* s_data, std::integer_sequence<int, J...>) {
-  (p.slot(kRegSlots + J, s_data[J * kResThreads + p.tid]), ...);
+  (p.slot(RS + J, s_data[J * kResThreads + p.tid]), ...);
 }
 
 // the re-read slots with a kAhead-deep prefetch ring (compile-time indices)
 template <bool GUARD, class P, int... K>
 __device__ __forceinline__ void encode_reread_slots(P& p, uint4 (&pre)[kAhead], const uint16_t* wg_x,
                                                     std::integer_sequence<int, K...>) {
-  constexpr int j0 = kRegSlots + kLdsSlots;
+  constexpr int j0 = reg_slots<GUARD>() + kLdsSlots;
   auto one = [&](auto kc) {
     constexpr int k = decltype(kc)::value;
     const uint4 w = pre[k % kAhead];
-    if constexpr (k + kAhead < kReSlots) {
+    if constexpr (k + kAhead < reread_slots<GUARD>()) {
+      const int jn = j0 + k + kAhead;
+      const uint32_t ls = slot_of(p.wbase, jn, p.lane);
       if constexpr (GUARD) {
-        pre[k % kAhead] = load_cached(wg_x, j0 + k + kAhead, p.tid, p.nres, p.n_valid);
+        pre[k % kAhead] = load_cached(wg_x, ls, jn < p.nres && ls < p.n_valid);
       } else {
-        const u32x4_t a = load16<false>(slot_ptr(wg_x, j0 + k + kAhead, p.tid));
+        const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
         pre[k % kAhead] = make_uint4(a.x, a.y, a.z, a.w);
       }
     }
@@ -184,27 +199,34 @@ __device__ uint32_t scan_tensor_amax(const QuantLaunch& q, uint32_t* s_red) {
 }
 
 // Poll *p until its high word equals epoch; false if the wait (limit in
-// ticks of the 100 MHz counter) runs out.
+// ticks of the 100 MHz counter) runs out.  The pause between polls doubles up
+// to about 0.4 us: every poll reaches the device-wide coherence point, and a
+// thousand waiting workgroups polling flat out would slow down the ones still
+// streaming their input.
 __device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, uint64_t limit, uint64_t& f) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  int pause = 1;
   for (int it = 0; it < kSpinLimit; ++it) {
     f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(f >> 32) == epoch) return true;
     if (__builtin_amdgcn_s_memrealtime() - t0 > limit) return false;
-    __builtin_amdgcn_s_sleep(1);
+    for (int k = 0; k < pause; ++k) __builtin_amdgcn_s_sleep(1);
+    pause = pause < 16 ? 2 * pause : 16;
   }
   return false;
 }
 
 template <bool GUARD>
-__global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch q, int nres, unsigned char* ws,
+__global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(QuantLaunch q, int nres, unsigned char* ws,
                                                                      uint32_t epoch) {
-  __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 147,456 bytes
-  __shared__ float2 s_inv[128];
+  __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 36,864 bytes (four workgroups per CU)
+  __shared__ float2 s_adj[128];   // adjusted multiplier and flag per scale code
+  __shared__ float2 s_br[128];    // brackets of 1 / (s g) per scale code
   __shared__ uint32_t s_red[kResThreads / 64];
   __shared__ uint32_t s_timeout;
   __shared__ uint32_t s_amax;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
   const int G = gridDim.x;
   uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);   // [1] tensor max word, [2] wait limit override
   uint64_t* flags = reinterpret_cast<uint64_t*>(ws + kWsFlagsOffsetBytes);   // one per workgroup
@@ -213,15 +235,17 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
   const int64_t rem = q.nslots - base;
   const uint32_t n_valid = (uint32_t)(rem < chunk ? (rem > 0 ? rem : 0) : chunk);
   const uint16_t* wg_x = static_cast<const uint16_t*>(q.x) + (base << 3);
+  const int wbase = wv * 64 * nres;                                   // this wave's first slot
   if (tid == 0) s_timeout = 0u;
 
   // ---------------- phase 1
+  constexpr int kRegSlots = reg_slots<GUARD>();
   uint4 r[kRegSlots];
-  load_reg_slots(r, wg_x, tid, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
+  load_reg_slots(r, wg_x, wbase, lane, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
   for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
-    const uint32_t ls0 = (uint32_t)(j * kResThreads + wv * 64);            // first slot of this wave
+    const uint32_t ls0 = slot_of(wbase, j, 0);                             // first slot of this wave's row
     if (ls0 < n_valid) {
-      // lane l lands at s_data[(j - kRegSlots) * 1024 + wv * 64 + l]; a lane past
+      // lane l lands at s_data[(j - kRegSlots) * kResThreads + wv * 64 + l]; a lane past
       // the end re-reads the wave's first slot (in bounds) and is never used
       const uint32_t ls = ls0 + (uint32_t)lane;
       const uint32_t src = ls < n_valid ? ls : ls0;
@@ -229,13 +253,26 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
                                        (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
     }
   }
+  // the re-read slots: all loads in flight before the first use (a use
+  // between loads would wait for every load issued before it)
   uint32_t acc = 0u;
-  for (int j = kRegSlots + kLdsSlots; j < nres; ++j) acc = max(acc, raw_finite_absmax(load_cached(wg_x, j, tid, nres, n_valid)));
+  {
+    constexpr int kScan = reread_slots<GUARD>();
+    uint4 sc[kScan];
+#pragma unroll
+    for (int k = 0; k < kScan; ++k) {
+      const int j = kRegSlots + kLdsSlots + k;
+      const uint32_t ls = slot_of(wbase, j, lane);
+      sc[k] = load_cached(wg_x, ls, (!GUARD || j < nres) && ls < n_valid);
+    }
+#pragma unroll
+    for (int k = 0; k < kScan; ++k) acc = max(acc, raw_finite_absmax(sc[k]));
+  }
   acc = max(acc, reg_slots_absmax(r, std::make_integer_sequence<int, kRegSlots>{}));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
-    if ((uint32_t)(j * kResThreads + tid) < n_valid) acc = max(acc, raw_finite_absmax(s_data[(j - kRegSlots) * kResThreads + tid]));
+    if (slot_of(wbase, j, lane) < n_valid) acc = max(acc, raw_finite_absmax(s_data[(j - kRegSlots) * kResThreads + tid]));
   }
   acc = wave_max_u32(acc);
   if (lane == 0) s_red[wv] = acc;
@@ -252,8 +289,10 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
     for (int w = 1; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
     __hip_atomic_store(flags + blockIdx.x, ((uint64_t)epoch << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // the master is the last workgroup: it streams the highest addresses and
+  // tends to finish phase 1 last, so it rarely waits long
   uint32_t amax_bits = 0u;
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == (unsigned)G - 1u) {
     uint32_t m = 0u;
     for (int i = tid; i < G; i += kResThreads) {
       uint64_t f = 0;
@@ -283,34 +322,35 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
 
   NvCtx cx;
   nv_context(as_f(amax_bits), false, cx);
-  nv_fill_inverse_table(s_inv, cx, tid, kResThreads);
+  nv_fill_adjusted_table(s_adj, s_br, cx, tid, kResThreads);
   if (tid == 0) {
     s_amax = amax_bits;
-    if (blockIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
+    if (blockIdx.x == (unsigned)G - 1u && q.global_scale) *q.global_scale = cx.g;
   }
   __syncthreads();
 
   // ---------------- phase 2
-  // (slot indices are recomputed from an opaque copy of the thread id: keeping
+  // (slot indices are recomputed from an opaque copy of the lane id: keeping
   // them alive from phase 1 would cost registers)
-  int tid2 = tid;
-  asm volatile("" : "+v"(tid2));
+  int lane2 = lane;
+  asm volatile("" : "+v"(lane2));
   uint4 pre[kAhead];
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) {
+    const int j = kRegSlots + kLdsSlots + k;
+    const uint32_t ls = slot_of(wbase, j, lane2);
     if constexpr (GUARD) {
-      pre[k] = load_cached(wg_x, kRegSlots + kLdsSlots + k, tid2, nres, n_valid);
+      pre[k] = load_cached(wg_x, ls, j < nres && ls < n_valid);
     } else {
-      const u32x4_t a = load16<false>(slot_ptr(wg_x, kRegSlots + kLdsSlots + k, tid2));
+      const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
       pre[k] = make_uint4(a.x, a.y, a.z, a.w);
     }
   }
-  Phase2<GUARD> p2{cx, s_inv, q.codes + (base << 2), q.scales + (base >> 1), tid2, nres, n_valid, 0u};
+  Phase2<GUARD> p2{cx, s_adj, q.codes + (base << 2), q.scales + (base >> 1), wbase, lane2, wv * 64 + lane2, nres,
+                   n_valid, 0u};
   encode_reg_slots(p2, r, std::make_integer_sequence<int, kRegSlots>{});
-  encode_lds_slots(p2, s_data, std::make_integer_sequence<int, kLdsSlots>{});
-  encode_reread_slots<GUARD>(p2, pre, wg_x, std::make_integer_sequence<int, kReSlots>{});
-  // exact recomputations, after this thread's fast stores: program order per
-  // address keeps the exact values last
+  encode_lds_slots<kRegSlots>(p2, s_data, std::make_integer_sequence<int, kLdsSlots>{});
+  encode_reread_slots<GUARD>(p2, pre, wg_x, std::make_integer_sequence<int, reread_slots<GUARD>()>{});
   // Exact recomputations, after this thread's fast stores (program order per
   // address keeps the exact values last).  The context is rebuilt from LDS so
   // that phase 2 keeps only the two bracket factors in registers.  With
@@ -325,10 +365,10 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
     xscale = 0x1p100f;
     nv_context_g(cf.g * xscale, cf);
     __syncthreads();
-    nv_fill_inverse_table(s_inv, cf, tid2, kResThreads);
+    nv_fill_adjusted_table(s_adj, s_br, cf, tid, kResThreads);
     __syncthreads();
     redo = 0u;
-    for (int j = 0; j < nres; ++j) redo |= ((uint32_t)(j * kResThreads + tid2) < n_valid ? 1u : 0u) << j;
+    for (int j = 0; j < nres; ++j) redo |= (slot_of(wbase, j, lane2) < n_valid ? 1u : 0u) << j;
   }
   // two slots per round, both blocks in flight together
   const uint16_t* xs = static_cast<const uint16_t*>(q.x);
@@ -338,12 +378,12 @@ __global__ __launch_bounds__(kResThreads, 1) void nv_resident_kernel(QuantLaunch
     const bool two = redo != 0u;
     const int j1 = two ? __builtin_ctz(redo) : j0;
     if (two) redo &= redo - 1u;
-    const int64_t s0 = base + (int64_t)(j0 * kResThreads + tid2);
-    const int64_t s1 = base + (int64_t)(j1 * kResThreads + tid2);
+    const int64_t s0 = base + (int64_t)slot_of(wbase, j0, lane2);
+    const int64_t s1 = base + (int64_t)slot_of(wbase, j1, lane2);
     const u32x4_t a0 = load16<false>(xs + ((s0 & ~(int64_t)1) << 3)), b0 = load16<false>(xs + ((s0 | 1) << 3));
     const u32x4_t a1 = load16<false>(xs + ((s1 & ~(int64_t)1) << 3)), b1 = load16<false>(xs + ((s1 | 1) << 3));
-    nv_fix_slot_fma(q, cf, s_inv, xscale, s0, a0, b0);
-    if (two) nv_fix_slot_fma(q, cf, s_inv, xscale, s1, a1, b1);
+    nv_fix_slot_fma(q, cf, s_br, xscale, s0, a0, b0);
+    if (two) nv_fix_slot_fma(q, cf, s_br, xscale, s1, a1, b1);
   }
 }
 
@@ -369,15 +409,34 @@ hipError_t launch_resident(const QuantLaunch& q, int grid, int nres, hipStream_t
   return hipGetLastError();
 }
 
+// Workgroups of the single-launch kernel that fit on the device at once
+// (kResPerCu per CU when its registers and LDS allow it), cached per device.
+int64_t resident_workgroups() {
+  static std::atomic<int64_t> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v != 0) return v;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&nv_resident_kernel<false>),
+                                                   kResThreads, 0) != hipSuccess)
+    per_cu = 0;
+  if (per_cu > kResPerCu) per_cu = kResPerCu;
+  v = per_cu > 0 ? (int64_t)per_cu * device_cu_count() : -1;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 }  // namespace
 
 // Whether the single-launch kernel takes this call, and its launch shape.
 bool nv_resident_shape(const QuantLaunch& q, int* grid, int* nres) {
   if (q.in_dtype != kBF16 || q.four_over_six || q.global_amax || q.stride != q.cols || q.nslots == 0) return false;
   if (q.rotation != kRotNone || q.stochastic || q.counters) return false;   // those variants stream twice
-  const int cus = device_cu_count();
+  const int64_t cap = resident_workgroups();
+  if (cap <= 0) return false;
   int64_t g = (q.nslots + kResThreads - 1) / kResThreads;
-  if (g > cus) g = cus;
+  if (g > cap) g = cap;
   if (g > kAmaxPartialsMax) return false;
   const int64_t n = (q.nslots + g * kResThreads - 1) / (g * kResThreads);
   if (n > kMaxSlots) return false;
