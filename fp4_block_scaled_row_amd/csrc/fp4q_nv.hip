@@ -100,7 +100,12 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
 
 template <int IN, int ROT, bool SR, bool FOS, bool COUNT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int npartials) {
+  // bf16 values rounded to nearest: one product per element with the adjusted
+  // multiplier of the block's scale code; otherwise (fp32 or rotated values,
+  // stochastic rounding) the bracketed products
+  constexpr bool kAdj = IN == kBF16 && ROT == kRotNone && !SR;
   __shared__ float2 s_inv[128];
+  __shared__ float2 s_adj[kAdj ? 128 : 1];
   __shared__ uint32_t s_red[kWaves];
   const int lane = threadIdx.x & 63;
 
@@ -121,7 +126,8 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   }
   NvCtx cx;
   nv_context(as_f(amax_bits), FOS, cx);
-  nv_fill_inverse_table(s_inv, cx, threadIdx.x, kThreads);
+  if constexpr (kAdj) nv_fill_adjusted_table(s_adj, s_inv, cx, threadIdx.x, kThreads);
+  else nv_fill_inverse_table(s_inv, cx, threadIdx.x, kThreads);
   if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
   __syncthreads();
 
@@ -164,13 +170,17 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       }
       const uint32_t c6 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all);
       uint32_t sat6;
-      uint32_t codes = nv_encode<SR, COUNT>(v, c6, cx, s_inv, rnd, sat6);
+      uint32_t codes;
+      if constexpr (kAdj) codes = nv_encode_adj<COUNT>(v, c6, cx, s_adj, s_inv, sat6);
+      else codes = nv_encode<SR, COUNT>(v, c6, cx, s_inv, rnd, sat6);
       uint32_t sbyte = c6, satm = sat6;
       bool pick4 = false;
       if constexpr (FOS) {
         const uint32_t c4 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv4_lo, cx.inv4_hi, cx.inv4, cx.mg4, cx.exact_all);
         uint32_t sat4;
-        const uint32_t codes4 = nv_encode<SR, COUNT>(v, c4, cx, s_inv, rnd, sat4);
+        uint32_t codes4;
+        if constexpr (kAdj) codes4 = nv_encode_adj<COUNT>(v, c4, cx, s_adj, s_inv, sat4);
+        else codes4 = nv_encode<SR, COUNT>(v, c4, cx, s_inv, rnd, sat4);
         float e6 = half_sse(v, codes, c6, cx.g);
         float e4 = half_sse(v, codes4, c4, cx.g);
         const float p6 = dpp_xor1_f(e6), p4 = dpp_xor1_f(e4);

@@ -222,6 +222,36 @@ __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, cons
   return codes;
 }
 
+// Round-to-nearest codes (and saturation flags) of the 8 bf16-valued elements
+// of a lane for E4M3 scale byte c, by one product with the adjusted multiplier
+// of c (nv_fill_adjusted_table): the common case.  A flagged code, or a
+// tensor with g < 2^-100, takes the bracketed path of nv_encode.
+template <bool COUNT>
+__device__ __forceinline__ uint32_t nv_encode_adj(const float v[8], uint32_t c, const NvCtx& cx, const float2* s_adj,
+                                                  const float2* s_br, uint32_t& satmask) {
+  const float2 mf = s_adj[c];
+  if (mf.y != 0.0f || cx.exact_all) {
+    const U4 none = {0u, 0u, 0u, 0u};
+    return nv_encode<false, COUNT>(v, c, cx, s_br, none, satmask);
+  }
+  const float one = e8m0_operand(127u);
+  float qv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] = v[i] * mf.x;
+  uint32_t codes = 0u;
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qv[0], qv[1], one, 0);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qv[2], qv[3], one, 1);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qv[4], qv[5], one, 2);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qv[6], qv[7], one, 3);
+  uint32_t sat = 0u;
+  if constexpr (COUNT) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sat |= (fabsf(qv[i]) > 6.0f ? 1u : 0u) << i;
+  }
+  satmask = sat;
+  return codes;
+}
+
 // Half of a block's sum of squared reconstruction errors, in the fixed fp32
 // order (no contraction): dq = (value * s) * g, d = x - dq, acc += d * d.
 __device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint32_t c, float g) {
