@@ -437,3 +437,61 @@ def test_nv_single_read_workspace_reuse_and_fallback():
         _nv_single(workloads.random_tensor(shape[0], shape[1], "bf16", seed, scale=2.0), ws)
     ws.view(torch.int64)[2] = 0
     _nv_single(workloads.random_tensor(300, 4096, "bf16", 7, scale=2.0), ws)
+
+
+# ------------------------------------------------------------------ exhaustive NVFP4 coverage
+def _e4m3_value(c):
+    return c * 2.0 ** -9 if c < 8 else (1 + (c & 7) / 8.0) * 2.0 ** ((c >> 3) - 7)
+
+
+def _exhaustive_nv_tensor(amax_bits):
+    """Block 0 holds the tensor max; then, for every E4M3 scale code c, blocks
+    whose max makes c the block's scale (near bamax = amax * s_c / 448) and
+    whose other 15 elements run through every bf16 magnitude up to that max,
+    with alternating signs: every (scale code, bf16 magnitude) pair once."""
+    amax = float(bf16_bits_to_f32(np.array([amax_bits], np.uint16))[0])
+    allmag = np.arange(1, 0x7F80, dtype=np.uint16)
+    blocks = [np.array([amax_bits] + [0] * 15, np.uint16)]
+    for c in range(1, 127):
+        b = f32_to_bf16_bits(np.array([amax * _e4m3_value(c) / 448.0], np.float32))[0]
+        if b == 0:
+            continue
+        sel = allmag[allmag <= b]
+        sel = np.concatenate([sel, np.zeros((-len(sel)) % 15, np.uint16)]).reshape(-1, 15)
+        sel[:, 1::2] |= 0x8000
+        blocks.append(np.concatenate([np.full((len(sel), 1), b, np.uint16), sel], axis=1).reshape(-1))
+    flat = np.concatenate(blocks)
+    cols = 4096
+    flat = np.concatenate([flat, np.zeros((-len(flat)) % cols, np.uint16)])
+    return flat.reshape(-1, cols)
+
+
+@pytest.mark.parametrize("amax", [418.0, 168.0, 3.7e-3, 2.0 ** -95, 3.0e38])
+def test_nv_exhaustive_scale_codes_and_magnitudes(amax):
+    """418: the workload's amax (near-ties from the rounding of g); 168: g
+    exact, so exact ties at every decision point; 2^-95: g < 2^-100; 3e38:
+    near the top of the range.  Single-read, two-pass and caller-amax paths."""
+    a_bits = int(f32_to_bf16_bits(np.array([amax], np.float32))[0])
+    x = _exhaustive_nv_tensor(a_bits)
+    c, s, g, _, cnt = oracle.quantize_nv(x)
+    xd = to_dev(x)
+    r = fq.quantize_nvfp4(xd)                                   # single read
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales (single read)")
+    assert_same(host(r.codes), c, "codes (single read)")
+    r = fq.quantize_nvfp4(xd, counters=True)                    # two passes
+    assert_same(host(r.scales), s, "scales (two-pass)")
+    assert_same(host(r.codes), c, "codes (two-pass)")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters (two-pass)")
+    amax_dev = torch.tensor([float(bf16_bits_to_f32(np.array([a_bits], np.uint16))[0])], dtype=torch.float32,
+                            device=xd.device)
+    r = fq.quantize_nvfp4(xd, global_amax=amax_dev)             # caller amax, encode pass only
+    assert_same(host(r.scales), s, "scales (caller amax)")
+    assert_same(host(r.codes), c, "codes (caller amax)")
+    r = fq.quantize_nvfp4(xd, policy="four_over_six", counters=True)
+    c4, s4, g4, ch4, cnt4 = oracle.quantize_nv(x, policy=3)
+    assert host(r.global_scale)[0] == g4
+    assert_same(host(r.scales), s4, "scales (four over six)")
+    assert_same(host(r.codes), c4, "codes (four over six)")
+    assert_same(host(r.choice_bits), ch4, "choice bits (four over six)")
+    assert_same(host(r.counters).astype(np.uint64), cnt4, "counters (four over six)")
