@@ -292,7 +292,8 @@ def main():
                   "bytes_per_step": MX_BYTES, "kernel": "mx_quant_kernel",
                   "traffic": traffic_for("mx_quant_kernel")},
         "dequant_nvfp4_to_bf16": {"value": round(DQ_BYTES / dq_sec / 1e9, 2), "unit": "GB/s",
-                                  "ms_per_step": round(dq_sec * 1e3, 5), "bytes_per_step": DQ_BYTES},
+                                  "ms_per_step": round(dq_sec * 1e3, 5), "bytes_per_step": DQ_BYTES,
+                                  "kernel": "dequant_kernel", "traffic": traffic_for("dequant_kernel")},
         "kernel_source_sha": kernel_source_sha(),
     }
     if not a.no_cpu_baseline:

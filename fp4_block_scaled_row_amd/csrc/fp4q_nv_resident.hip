@@ -26,7 +26,7 @@
 // The epoch is a per-call number from the host, so flags left by an earlier
 // call never match; the workspace must be zero-filled before its first use.
 //
-// The 8192 x 8192 bf16 activation is 1024 x 256 x 32 slots on 256 CUs: 27 of
+// The 8192 x 8192 bf16 activation is 1024 x 256 x 32 slots on 256 CUs: 26 of
 // every 32 slots stay on chip.
 #include <atomic>
 #include <utility>
