@@ -8,28 +8,40 @@
 // in fp32; the product with g is rounded once: for fp32 output by the fp32
 // multiply, for bf16 output by rounding the fp32 product to nearest-even and,
 // when that product sits exactly on a bf16 rounding boundary, deciding with
-// the exact fp64 product (value * s * g has <= 31 significant bits).
+// the sign of its exact rounding error: fma(v s, g, -p) is that error exactly
+// (the error of an fp32 product is an fp32 number), so the side of the
+// boundary the exact product lies on is known without wider arithmetic; products
+// below 2^-100, where the error could underflow, use the fp64 product
+// (value * s * g has <= 31 significant bits).  bf16 outputs are stored
+// non-temporally: they are written once and not read back by this kernel.
 #include "fp4q_flat.h"
 
 namespace fp4q {
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 __device__ __forceinline__ uint32_t bf16_of_product(float vs, float g) {
-  const float a = fabsf(vs) * g;
+  const float av = fabsf(vs);
+  const float a = av * g;
   const uint32_t b = as_u(a);
-  uint32_t r;
-  if ((b & 0xFFFFu) == 0x8000u) {
-    const double ex = (double)fabsf(vs) * (double)g;
-    const double ad = (double)a;
-    const uint32_t hi = b >> 16;
-    r = (ex > ad) ? hi + 1u : (ex < ad) ? hi : hi + (hi & 1u);
-  } else {
-    r = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  const uint32_t hi = b >> 16;
+  uint32_t r = (b + 0x7FFFu + (hi & 1u)) >> 16;
+  if ((b & 0xFFFFu) == 0x8000u) {   // on a bf16 midpoint: which side is the exact product?
+    int side;
+    if (a >= 0x1p-100f) {
+      const float e = fmaf(av, g, -a);
+      side = e > 0.0f ? 1 : (e < 0.0f ? -1 : 0);
+    } else {
+      const double ex = (double)av * (double)g;
+      side = ex > (double)a ? 1 : (ex < (double)a ? -1 : 0);
+    }
+    r = side > 0 ? hi + 1u : (side < 0 ? hi : hi + (hi & 1u));
   }
   return r | ((as_u(vs) >> 31) << 15);
 }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <int FMT, int OUT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int64_t nslots) {
@@ -77,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int6
           o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 2));
           o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 3));
           if (nan) o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + (s << 3)) = o;
+          __builtin_nontemporal_store(u32x4_t{o.x, o.y, o.z, o.w},
+                                      reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.out) + (s << 3)));
         }
       } else {
         const bool nan = sb[u] == 0x7Fu || sb[u] == 0xFFu;
@@ -94,12 +107,33 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int6
           for (int i = 0; i < 8; ++i) o[i] = nan ? as_f(0x7FC00000u) : (val[i] * sd) * g;
           store_rotated(static_cast<float*>(d.out), s, o);
         } else {
-          uint32_t h[8];
+          // fp32 products rounded to bf16 by the hardware conversion (nearest-even);
+          // a product sitting exactly on a bf16 midpoint is redone exactly
+          float pr[8];
+          uint32_t tie = 0u;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) h[i] = nan ? 0x7FC0u : bf16_of_product(val[i] * sd, g);
-          const uint4 o = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                     h[6] | (h[7] << 16));
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + (s << 3)) = o;
+          for (int i = 0; i < 8; ++i) {
+            pr[i] = (val[i] * sd) * g;
+            tie |= ((as_u(pr[i]) & 0xFFFFu) == 0x8000u) ? (1u << i) : 0u;
+          }
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2_t pk = {(__bf16)pr[2 * i], (__bf16)pr[2 * i + 1]};
+            h[i] = __builtin_bit_cast(uint32_t, pk);
+          }
+          if (tie != 0u) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              if ((tie >> i) & 1u) {
+                const uint32_t r = bf16_of_product(val[i] * sd, g);
+                h[i >> 1] = (i & 1) ? ((h[i >> 1] & 0xFFFFu) | (r << 16)) : ((h[i >> 1] & 0xFFFF0000u) | r);
+              }
+            }
+          }
+          if (nan) h[0] = h[1] = h[2] = h[3] = 0x7FC07FC0u;
+          const u32x4_t o = {h[0], h[1], h[2], h[3]};
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.out) + (s << 3)));
         }
       }
     }
