@@ -40,6 +40,7 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i of each 8-lane half-row <- lane 7 - i
 
 __device__ __forceinline__ float dpp_xor1_f(float v) { return as_f(dpp_u32<kQuadXor1>(as_u(v))); }
 __device__ __forceinline__ float dpp_xor2_f(float v) { return as_f(dpp_u32<kQuadXor2>(as_u(v))); }

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   constexpr bool kAdj = IN == kBF16 && ROT == kRotNone && !SR;
   __shared__ float2 s_inv[128];
   __shared__ float2 s_adj[kAdj ? 128 : 1];
+  __shared__ float2 s_eps[8];
   __shared__ uint32_t s_red[kWaves];
   const int lane = threadIdx.x & 63;
 
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   }
   NvCtx cx;
   nv_context(as_f(amax_bits), FOS, cx);
-  if constexpr (kAdj) nv_fill_adjusted_table(s_adj, s_inv, cx, threadIdx.x, kThreads);
+  if constexpr (kAdj) nv_fill_adjusted_table(s_adj, s_inv, s_eps, cx, threadIdx.x);
   else nv_fill_inverse_table(s_inv, cx, threadIdx.x, kThreads);
   if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
   __syncthreads();

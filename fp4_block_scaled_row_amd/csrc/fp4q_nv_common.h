@@ -75,67 +75,89 @@ __device__ __forceinline__ void nv_fill_inverse_table(float2* s_inv, const NvCtx
 // significant bits, so within 2^-12 (relative) of a threshold T = p s g (p a
 // decision point of the E2M1 rounding, or 6 for the saturation count) lies
 // at most one bf16 value, at relative offset d = (a - T) / T, and every other
-// bf16 value is at least 2^-12 away.  m = (1 + eps) / (s g) rounded to fp32,
-// with |eps| <= 2^-14, keeps RN32(a m) on the same side of p as the exact
-// a / (s g) for all far values; for the near value it does so when
-// (1 + d)(1 + eps) is at least 1 + 2^-22 above (or below) 1 -- half an fp32
-// ulp of any p is at most 2^-24 relative, so the product rounds away from p,
-// and 2^-23 of slack covers the rounding of m itself.  An exact tie (d = 0)
+// bf16 value is at least 2^-12 away.  A multiplier m = (1 + e) / (s g) with
+// |e| <= 2^-14 keeps RN32(a m) on the same side of p as the exact a / (s g)
+// for all far values; for the near value it does so when (1 + d)(1 + e) is at
+// least 1 + 2^-22 above (or below) 1 -- half an fp32 ulp of any p is at most
+// 2^-24 relative, so the product rounds away from p.  An exact tie (d = 0)
 // must fall on the side of the even code.  The constraints of the 8 points
-// bound eps from both sides; the midpoint of the interval is taken, and a
-// code whose interval is empty is flagged so that its blocks take the exact
-// path.  Decision points and the side of their even neighbour:
+// bound the intended e from both sides; the midpoint of the interval is
+// taken, and a code whose interval is narrower than 2 * 2^-21 is flagged so
+// that its blocks take the exact path.  The 2^-21 of slack covers the
+// deviation of the stored multiplier from (1 + e) / (s g): the fp32 product
+// s g and its correctly rounded reciprocal (2^-23 together), the rounding of
+// 1 + e and of the final product (2^-24 each).  Decision points and the side
+// of their even neighbour:
 //   0.25 down, 0.75 up, 1.25 down, 1.75 up, 2.5 down, 3.5 up, 5 down, 6 down
 // (6 itself is not saturated).
 //
-// s_adj[c] = (m_c, flag) and s_br[c] = the 2^-22 brackets of 1/(s_c g) (for
-// the exact path), for every E4M3 code; c = 0 gives (0, 0) (every code of
-// such a block is a signed zero), c = 127 (NaN scale) is flagged.  Work item
-// t = 8 c + k of 1024 handles point k of code c; the 8 items of a code are
-// consecutive lanes of one wave (nthreads must be a multiple of 64).
-__device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_br, const NvCtx& cx, int tid,
-                                                       int nthreads) {
-#pragma unroll 1
-  for (int t = tid; t < 1024; t += nthreads) {
-    const uint32_t c = (uint32_t)t >> 3;
-    const int k = t & 7;
-    const double sg = (double)e4m3_value(c) * cx.g64;   // exact (4 x 24 bits)
-    double lo = -0x1p-14, hi = 0x1p-14;
-    if (c != 0u && c != 127u) {
-      const double p = k < 4 ? 0.25 + 0.5 * k : (k == 4 ? 2.5 : (k == 5 ? 3.5 : (k == 6 ? 5.0 : 6.0)));
-      const bool tie_up = k == 1 || k == 3 || k == 5;
-      const double T = p * sg;                            // exact (3 x 28 bits)
-      const double ulp = ldexp(1.0, ilogb(T) - 7);        // bf16 spacing at T
-      const double a0 = floor(T / ulp) * ulp;             // (division by a power of two: exact)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const double a = a0 + (double)i * ulp;
-        const double diff = a - T;                        // exact
-        if (fabs(diff) < 0x1p-12 * T) {                   // the near value (rare)
-          const double d = diff / T;
-          if (d > 0.0 || (d == 0.0 && tie_up)) lo = fmax(lo, (1.0 + 0x1p-22) / (1.0 + d) - 1.0);
-          else hi = fmin(hi, (1.0 - 0x1p-22) / (1.0 + d) - 1.0);
-        }
-      }
+// The constraints depend on s only through its significand: scaling s by a
+// power of two scales T and maps the bf16 grid onto itself (T stays inside
+// the normal range: 2^-111 <= T <= 2688 g for g >= 2^-100), so e is computed
+// once per significand class (8 classes: 1, 1.125, ..., 1.875 -- subnormal
+// E4M3 scales fall into the same classes) and point: 64 work items.
+//
+// All in fp32: T = th + tl exactly (th = RN32(p s g) with p s exact, tl the
+// FMA error term); the nearest bf16 value a to th is the nearest to T unless
+// T is near a bf16 midpoint (then no value is within 2^-12); a - th is exact
+// (Sterbenz).  d uses the hardware reciprocal of th and the bounds
+// (+-2^-22 - d) / (1 + d) are taken as (+-2^-22 - d)(1 - d): relative errors
+// near 2^-22 on quantities below 2^-12, i.e. below 2^-33 in absolute terms,
+// far inside the slack.  The 8 points of a class are folded with DPP.
+//
+// s_adj[c] = (m_c, flag) and s_br[c] = 1/(s_c g) times (1 -+ 2^-22) -- still
+// a strict bracket of the exact reciprocal with the fp32 reciprocal's 2^-23
+// error -- for the exact path, for every E4M3 code; c = 0 gives (0, 0)
+// (every code of such a block is a signed zero), c = 127 (NaN scale) is
+// flagged.  s_eps: 8 entries of scratch.  Every thread of the workgroup calls
+// this (it synchronises); the workgroup has at least 128 threads.  Requires
+// g >= 2^-100 for meaningful entries.
+__device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_br, float2* s_eps, const NvCtx& cx,
+                                                       int tid) {
+  const float g = cx.g;
+  if (tid < 64) {
+    const int cls = tid >> 3, k = tid & 7;
+    const float sd = 1.0f + 0.125f * (float)cls;
+    const float p = k < 4 ? 0.25f + 0.5f * (float)k : (k == 4 ? 2.5f : (k == 5 ? 3.5f : (k == 6 ? 5.0f : 6.0f)));
+    const bool tie_up = k == 1 || k == 3 || k == 5;
+    float lo = -0x1p-14f, hi = 0x1p-14f;
+    const float ps = p * sd;                           // exact
+    const float th = ps * g;
+    const float tl = fmaf(ps, g, -th);                 // T = th + tl exactly
+    const uint32_t tb = as_u(th);
+    const float a = as_f(((tb + 0x7FFFu + ((tb >> 16) & 1u)) >> 16) << 16);   // nearest bf16
+    const float diff = (a - th) - tl;
+    if (fabsf(diff) < 0x1p-12f * th) {
+      const float d = diff * __builtin_amdgcn_rcpf(th);
+      if (d > 0.0f || (d == 0.0f && tie_up)) lo = fmaxf(lo, (0x1p-22f - d) * (1.0f - d));
+      else hi = fminf(hi, (-0x1p-22f - d) * (1.0f - d));
     }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      lo = fmax(lo, __shfl_xor(lo, off));
-      hi = fmin(hi, __shfl_xor(hi, off));
+    // fold the 8 consecutive lanes of this class: quad exchanges, then the
+    // mirror within each half-row pairs quad 0 with quad 1
+    lo = fmaxf(lo, dpp_xor1_f(lo));
+    hi = fminf(hi, dpp_xor1_f(hi));
+    lo = fmaxf(lo, dpp_xor2_f(lo));
+    hi = fminf(hi, dpp_xor2_f(hi));
+    lo = fmaxf(lo, as_f(dpp_u32<kRowHalfMirror>(as_u(lo))));
+    hi = fminf(hi, as_f(dpp_u32<kRowHalfMirror>(as_u(hi))));
+    if (k == 0)
+      s_eps[cls] = (lo + 0x1p-21f <= hi - 0x1p-21f) ? make_float2(0.5f * (lo + hi), 0.0f) : make_float2(0.0f, 1.0f);
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const uint32_t c = (uint32_t)tid;
+    float2 adj = make_float2(0.0f, 1.0f), br = make_float2(0.0f, 0.0f);
+    if (c == 0u) {
+      adj = make_float2(0.0f, 0.0f);
+    } else if (c != 127u) {
+      const float sd = e4m3_value(c);
+      const float2 e = s_eps[(as_u(sd) >> 20) & 7u];   // significand class of s_c
+      const float inv = 1.0f / (sd * g);
+      br = make_float2(inv * (1.0f - 0x1p-22f), inv * (1.0f + 0x1p-22f));
+      adj = make_float2(inv * (1.0f + e.x), e.y);
     }
-    if (k == 0) {
-      float2 adj = make_float2(0.0f, 1.0f), br = make_float2(0.0f, 0.0f);
-      if (c == 0u) {
-        adj = make_float2(0.0f, 0.0f);
-      } else if (c != 127u) {
-        const double inv = 1.0 / sg;
-        br = make_float2((float)(inv * (1.0 - 0x1p-22)), (float)(inv * (1.0 + 0x1p-22)));
-        adj = (lo + 0x1p-23 <= hi - 0x1p-23) ? make_float2((float)(inv * (1.0 + 0.5 * (lo + hi))), 0.0f)
-                                             : make_float2((float)inv, 1.0f);
-      }
-      s_adj[c] = adj;
-      s_br[c] = br;
-    }
+    s_adj[c] = adj;
+    s_br[c] = br;
   }
 }
 

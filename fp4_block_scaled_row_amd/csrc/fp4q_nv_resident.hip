@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 36,864 bytes (four workgroups per CU)
   __shared__ float2 s_adj[128];   // adjusted multiplier and flag per scale code
   __shared__ float2 s_br[128];    // brackets of 1 / (s g) per scale code
+  __shared__ float2 s_eps[8];     // multiplier adjustment per significand class
   __shared__ uint32_t s_red[kResThreads / 64];
   __shared__ uint32_t s_timeout;
   __shared__ uint32_t s_amax;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
 
   NvCtx cx;
   nv_context(as_f(amax_bits), false, cx);
-  nv_fill_adjusted_table(s_adj, s_br, cx, tid, kResThreads);
+  nv_fill_adjusted_table(s_adj, s_br, s_eps, cx, tid);
   if (tid == 0) {
     s_amax = amax_bits;
     if (blockIdx.x == (unsigned)G - 1u && q.global_scale) *q.global_scale = cx.g;
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     xscale = 0x1p100f;
     nv_context_g(cf.g * xscale, cf);
     __syncthreads();
-    nv_fill_adjusted_table(s_adj, s_br, cf, tid, kResThreads);
+    nv_fill_adjusted_table(s_adj, s_br, s_eps, cf, tid);
     __syncthreads();
     redo = 0u;
     for (int j = 0; j < nres; ++j) redo |= (slot_of(wbase, j, lane2) < n_valid ? 1u : 0u) << j;
