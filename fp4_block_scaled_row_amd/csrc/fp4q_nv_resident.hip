@@ -80,16 +80,17 @@ __device__ __forceinline__ uint32_t slot_of(int wbase, int j, int lane) { return
 
 __device__ __forceinline__ const uint16_t* slot_ptr(const uint16_t* wg_x, uint32_t ls) { return wg_x + (size_t)ls * 8u; }
 
-template <int RS, int... J>
+template <bool GUARD, int RS, int... J>
 __device__ __forceinline__ void load_reg_slots(uint4 (&r)[RS], const uint16_t* wg_x, int wbase, int lane,
                                                int nres, uint32_t n_valid, std::integer_sequence<int, J...>) {
   auto one = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    r[j] = make_uint4(0u, 0u, 0u, 0u);
     const uint32_t ls = slot_of(wbase, j, lane);
-    if (j < nres && ls < n_valid) {
+    if (!GUARD || (j < nres && ls < n_valid)) {
       const u32x4_t a = load16<true>(slot_ptr(wg_x, ls));
       r[j] = make_uint4(a.x, a.y, a.z, a.w);
+    } else {
+      r[j] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
   (one(std::integral_constant<int, J>{}), ...);
@@ -198,20 +199,26 @@ __device__ uint32_t scan_tensor_amax(const QuantLaunch& q, uint32_t* s_red) {
   return m;
 }
 
-// Poll *p until its high word equals epoch; false if the wait (limit in
-// ticks of the 100 MHz counter) runs out.  The pause between polls doubles up
-// to about 0.4 us: every poll reaches the device-wide coherence point, and a
-// thousand waiting workgroups polling flat out would slow down the ones still
-// streaming their input.
-__device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, uint64_t limit, uint64_t& f) {
+// Poll *p until its high word equals epoch; false if the wait runs out.  The
+// limit is 1 ms of the 100 MHz counter unless *limit_word is nonzero (tests
+// set it to a few ticks to drive the fallback scan); it is read only once a
+// wait has begun, so its latency hides inside the wait.  The pause between
+// polls doubles up to about 0.4 us: every poll reaches the device-wide
+// coherence point, and a thousand waiting workgroups polling flat out would
+// slow down the ones still streaming their input.
+__device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, const uint64_t* limit_word, uint64_t& f) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(f >> 32) == epoch) return true;
+  const uint64_t set = __hip_atomic_load(limit_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t limit = set ? set : kWaitTicks;
   int pause = 1;
   for (int it = 0; it < kSpinLimit; ++it) {
+    for (int k = 0; k < pause; ++k) __builtin_amdgcn_s_sleep(1);
+    pause = pause < 16 ? 2 * pause : 16;
     f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(f >> 32) == epoch) return true;
     if (__builtin_amdgcn_s_memrealtime() - t0 > limit) return false;
-    for (int k = 0; k < pause; ++k) __builtin_amdgcn_s_sleep(1);
-    pause = pause < 16 ? 2 * pause : 16;
   }
   return false;
 }
@@ -242,17 +249,25 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   // ---------------- phase 1
   constexpr int kRegSlots = reg_slots<GUARD>();
   uint4 r[kRegSlots];
-  load_reg_slots(r, wg_x, wbase, lane, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
-  for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
-    const uint32_t ls0 = slot_of(wbase, j, 0);                             // first slot of this wave's row
-    if (ls0 < n_valid) {
-      // lane l lands at s_data[(j - kRegSlots) * kResThreads + wv * 64 + l]; a lane past
-      // the end re-reads the wave's first slot (in bounds) and is never used
-      const uint32_t ls = ls0 + (uint32_t)lane;
-      const uint32_t src = ls < n_valid ? ls : ls0;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(wg_x + (size_t)src * 8u),
-                                       (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
+  // (the full-workgroup variant issues every load unconditionally, back to back)
+  load_reg_slots<GUARD>(r, wg_x, wbase, lane, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
+  if constexpr (GUARD) {
+    for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
+      const uint32_t ls0 = slot_of(wbase, j, 0);                           // first slot of this wave's row
+      if (ls0 < n_valid) {
+        // lane l lands at s_data[(j - kRegSlots) * kResThreads + wv * 64 + l]; a lane past
+        // the end re-reads the wave's first slot (in bounds) and is never used
+        const uint32_t ls = ls0 + (uint32_t)lane;
+        const uint32_t src = ls < n_valid ? ls : ls0;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wg_x + (size_t)src * 8u),
+                                         (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
+      }
     }
+  } else {
+#pragma unroll
+    for (int j = kRegSlots; j < kRegSlots + kLdsSlots; ++j)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(slot_ptr(wg_x, slot_of(wbase, j, lane))),
+                                       (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
   }
   // the re-read slots: all loads in flight before the first use (a use
   // between loads would wait for every load issued before it)
@@ -280,10 +295,6 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   __syncthreads();
 
   // ---------------- grid-wide exchange of the chunk maxima
-  // (a nonzero header word 2 replaces the default wait limit: tests set it
-  // to a few ticks to drive the fallback scan)
-  const uint64_t lim_set = hdr[2];
-  const uint64_t limit = lim_set ? lim_set : kWaitTicks;
   if (tid == 0) {
     uint32_t m = s_red[0];
 #pragma unroll
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     uint32_t m = 0u;
     for (int i = tid; i < G; i += kResThreads) {
       uint64_t f = 0;
-      if (!wait_epoch(flags + i, epoch, limit, f)) s_timeout = 1u;
+      if (!wait_epoch(flags + i, epoch, hdr + 2, f)) s_timeout = 1u;
       m = max(m, (uint32_t)f);
     }
     m = wave_max_u32(m);
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     __syncthreads();   // s_red is reused below
     if (tid == 0) {
       uint64_t f = 0;
-      if (wait_epoch(hdr + 1, epoch, limit, f)) s_red[0] = (uint32_t)f;
+      if (wait_epoch(hdr + 1, epoch, hdr + 2, f)) s_red[0] = (uint32_t)f;
       else s_timeout = 1u;
     }
     __syncthreads();
