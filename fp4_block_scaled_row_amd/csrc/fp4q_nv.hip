@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         }
       }
       if (active) {
-        *reinterpret_cast<uint32_t*>(q.codes + (f >> 1)) = codes;
+        __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(q.codes + (f >> 1)));
         if (!odd) q.scales[f >> 4] = (uint8_t)sbyte;
         if constexpr (ROT != kRotNone) {
           if (q.rotated) store_rotated(q.rotated, s, v);

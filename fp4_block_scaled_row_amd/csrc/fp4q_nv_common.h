@@ -410,7 +410,7 @@ __device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCt
     }
     scale = c;
   }
-  *reinterpret_cast<uint32_t*>(q.codes + (s << 2)) = codes;
+  __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(q.codes + (s << 2)));   // as the fast path
   q.scales[s >> 1] = (uint8_t)scale;
 }
 
@@ -453,7 +453,10 @@ __device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_ad
   FP4Q_PAIR(2, w.z)
   FP4Q_PAIR(3, w.w)
 #undef FP4Q_PAIR
-  *codes_at = ca;
+  // codes non-temporal: they stream out during the encode instead of piling
+  // up as dirty L2 lines that drain after it (scale bytes stay cached: their
+  // partial lines are better merged in L2)
+  __builtin_nontemporal_store(ca, codes_at);
   *scale_at = (uint8_t)c;
   return ((sb2 ^ (sb2 >> 8)) & 0xFFu) != 0u || mf.y != 0.0f || bm >= 0x7F80u;
 }
