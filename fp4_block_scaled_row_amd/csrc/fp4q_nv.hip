@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
         rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
       }
-      const uint32_t c6 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all);
+      const uint32_t c6 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all, 6.0f, cx.g);
       uint32_t sat6;
       uint32_t codes;
       if constexpr (kAdj) codes = nv_encode_adj<COUNT>(v, c6, cx, s_adj, s_inv, sat6);
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       uint32_t sbyte = c6, satm = sat6;
       bool pick4 = false;
       if constexpr (FOS) {
-        const uint32_t c4 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv4_lo, cx.inv4_hi, cx.inv4, cx.mg4, cx.exact_all);
+        const uint32_t c4 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv4_lo, cx.inv4_hi, cx.inv4, cx.mg4, cx.exact_all, 4.0f, cx.g);
         uint32_t sat4;
         uint32_t codes4;
         if constexpr (kAdj) codes4 = nv_encode_adj<COUNT>(v, c4, cx, s_adj, s_inv, sat4);

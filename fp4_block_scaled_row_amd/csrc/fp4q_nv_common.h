@@ -161,18 +161,66 @@ __device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_
   }
 }
 
+// Exact decisions for brackets that disagree.  When the two bracket products
+// of one quotient q = a / (k g) round to adjacent codes lo < hi, exactly one
+// decision point p (the midpoint of their values) lies between them, and q
+// is above, below or on it as a - (p k) g is positive, negative or zero: p k
+// is exact in fp32 (a few significant bits each) and one FMA evaluates the
+// difference exactly before its single rounding, so the sign is exact (for
+// g >= 2^-100 no product underflows).  A tie takes the code with the even
+// mantissa.  This replaces an fp64 division in the common near-tie case
+// (bf16 inputs make quotients within 2^-24 of a decision point frequent).
+
+// E4M3 scale byte of bamax / (mult g) given the bracket bytes cl < ch.
+__device__ __forceinline__ uint32_t resolve_e4m3(float bamax, uint32_t cl, uint32_t ch, float mult, float g) {
+  const float p = 0.5f * (e4m3_value(cl) + e4m3_value(ch));
+  const float r = fmaf(-(p * mult), g, bamax);
+  return r > 0.0f ? ch : (r < 0.0f ? cl : ((cl & 1u) ? ch : cl));
+}
+
+// E2M1 magnitude of |x| / (s g) given bracket magnitudes ml < mh (E2M1
+// magnitude codes, mh = ml + 1); sd = s as fp32.
+__device__ __forceinline__ uint32_t resolve_e2m1(float xabs, uint32_t ml, uint32_t mh, float sd, float g) {
+  const float one = e8m0_operand(127u);
+  const float2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ml | (mh << 4), one, 0);
+  const float p = 0.5f * (v.x + v.y);
+  const float r = fmaf(-(p * sd), g, xabs);
+  return r > 0.0f ? mh : (r < 0.0f ? ml : ((ml & 1u) ? mh : ml));
+}
+
+// Lattice value of E2M1 magnitude code k (0, 0.5, 1, 1.5, 2, 3, 4, 6).
+__device__ __forceinline__ float e2m1_lattice(uint32_t k) {
+  return k < 4u ? 0.5f * (float)k : (k == 4u ? 2.0f : (k == 5u ? 3.0f : (k == 6u ? 4.0f : 6.0f)));
+}
+
+// Stochastic-rounding magnitude (R-17: up iff |q| > lo + u 2^-16 (hi - lo)
+// between the lattice neighbours lo <= |q| < hi, |q| >= 6 -> 6) of
+// |q| = a / (s g), decided exactly: the interval is fixed by FMA residuals
+// against L[k] s g starting from the hint k, and the threshold t = lo +
+// u 2^-16 (hi - lo) has at most 18 significant bits, so t s is exact and one
+// FMA residual a - (t s) g decides.  With g >= 2^-100 every (t s) g is a
+// multiple of 2^-149 (t of 2^-17, s of 2^-9, g of 2^-123), and so is a, so
+// a nonzero residual never rounds to zero.
+__device__ __forceinline__ uint32_t e2m1_sr_mag_exact(float a, uint32_t u, uint32_t k, float sd, float g) {
+  while (k < 7u && fmaf(-(e2m1_lattice(k + 1u) * sd), g, a) >= 0.0f) ++k;
+  while (k > 0u && fmaf(-(e2m1_lattice(k) * sd), g, a) < 0.0f) --k;
+  if (k == 7u) return 7u;
+  const float lo = e2m1_lattice(k), hi = e2m1_lattice(k + 1u);
+  const float t = fmaf((float)u * 0x1p-16f, hi - lo, lo);
+  return fmaf(-(t * sd), g, a) > 0.0f ? k + 1u : k;
+}
+
 // E4M3 block-scale byte RNE_E4M3(bamax / (mult g)), saturating at 448.  With
 // g < 2^-100 (exact_all) 1/(mult g) may not fit fp32, so the fp64 encoding
 // decides directly.
 __device__ __forceinline__ uint32_t nv_scale_code(float bamax, float inv_lo, float inv_hi, double inv64, double mg,
-                                                  bool exact_all) {
+                                                  bool exact_all, float mult, float g) {
   if (exact_all) return e4m3_encode_exact(bamax, (double)bamax * inv64, mg);
   const float tl = fminf(bamax * inv_lo, 448.0f);
   const float th = fminf(bamax * inv_hi, 448.0f);
   const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, 0, false);
   const uint32_t cl = b & 0xFFu, ch = (b >> 8) & 0xFFu;
-  if (cl == ch) return cl;
-  return e4m3_encode_exact(bamax, (double)bamax * inv64, mg);
+  return cl == ch ? cl : resolve_e4m3(bamax, cl, ch, mult, g);
 }
 
 // Codes of the 8 elements of a lane for E4M3 scale byte c.
@@ -220,19 +268,36 @@ __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, cons
     }
   }
   uint32_t codes = ca, sat = sa;
-  if (ca != cb || sa != sb || cx.exact_all) {
-    // exact path: correctly rounded fp64 quotient
+  if (cx.exact_all) {
+    // g < 2^-100: correctly rounded fp64 quotients for every element
     const double den = (double)e4m3_value(c) * cx.g64;
-#pragma unroll
+#pragma unroll 1
     for (int i = 0; i < 8; ++i) {
-      const uint32_t nib_diff = ((ca ^ cb) >> (4 * i)) & 0xFu;
+      uint32_t mag = 0u, st = 0u;
+      if (c != 0u) {
+        const double qd = fabs((double)v[i]) / den;
+        mag = SR ? e2m1_sr_mag_f64(qd, draw16(rnd, i)) : e2m1_rne_mag_f64(qd);
+        st = qd > 6.0 ? 1u : 0u;
+      }
+      const uint32_t sg = (as_u(v[i]) >> 31) << 3;
+      codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));
+      sat = (sat & ~(1u << i)) | (st << i);
+    }
+  } else if (ca != cb || sa != sb) {
+    // elements whose brackets disagree: exact FMA-residual decisions
+    const float gs = cx.g;
+    const float sd = e4m3_value(c);
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ka = (ca >> (4 * i)) & 7u, kb = (cb >> (4 * i)) & 7u;
       const uint32_t sat_diff = ((sa ^ sb) >> i) & 1u;
-      if (cx.exact_all || nib_diff || sat_diff) {
+      if (ka != kb || sat_diff) {
         uint32_t mag = 0u, st = 0u;
         if (c != 0u) {
-          const double qd = fabs((double)v[i]) / den;
-          mag = SR ? e2m1_sr_mag_f64(qd, draw16(rnd, i)) : e2m1_rne_mag_f64(qd);
-          st = qd > 6.0 ? 1u : 0u;
+          const float a = fabsf(v[i]);
+          if constexpr (SR) mag = e2m1_sr_mag_exact(a, draw16(rnd, i), ka, sd, gs);
+          else mag = ka != kb ? resolve_e2m1(a, ka, kb, sd, gs) : ka;
+          st = fmaf(-(6.0f * sd), gs, a) > 0.0f ? 1u : 0u;
         }
         const uint32_t sg = (as_u(v[i]) >> 31) << 3;
         codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));
@@ -319,7 +384,7 @@ __device__ __forceinline__ void nv_encode_slot(const QuantLaunch& q, const NvCtx
     const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
     rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
   }
-  const uint32_t c = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all);
+  const uint32_t c = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all, 6.0f, cx.g);
   uint32_t satm;
   uint32_t codes = nv_encode<SR, COUNT>(v, c, cx, s_inv, rnd, satm);
   if (nonfinite) codes = 0u;
@@ -342,33 +407,6 @@ __device__ __forceinline__ void nv_encode_slot(const QuantLaunch& q, const NvCtx
       if (q.rotated) store_rotated(q.rotated, s, v);
     }
   }
-}
-
-// Exact decisions for brackets that disagree.  When the two bracket products
-// of one quotient q = a / (k g) round to adjacent codes lo < hi, exactly one
-// decision point p (the midpoint of their values) lies between them, and q
-// is above, below or on it as a - (p k) g is positive, negative or zero: p k
-// is exact in fp32 (a few significant bits each) and one FMA evaluates the
-// difference exactly before its single rounding, so the sign is exact (for
-// g >= 2^-100 no product underflows).  A tie takes the code with the even
-// mantissa.  This replaces an fp64 division in the common near-tie case
-// (bf16 inputs make quotients within 2^-24 of a decision point frequent).
-
-// E4M3 scale byte of bamax / (mult g) given the bracket bytes cl < ch.
-__device__ __forceinline__ uint32_t resolve_e4m3(float bamax, uint32_t cl, uint32_t ch, float mult, float g) {
-  const float p = 0.5f * (e4m3_value(cl) + e4m3_value(ch));
-  const float r = fmaf(-(p * mult), g, bamax);
-  return r > 0.0f ? ch : (r < 0.0f ? cl : ((cl & 1u) ? ch : cl));
-}
-
-// E2M1 magnitude of |x| / (s g) given bracket magnitudes ml < mh (E2M1
-// magnitude codes, mh = ml + 1); sd = s as fp32.
-__device__ __forceinline__ uint32_t resolve_e2m1(float xabs, uint32_t ml, uint32_t mh, float sd, float g) {
-  const float one = e8m0_operand(127u);
-  const float2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ml | (mh << 4), one, 0);
-  const float p = 0.5f * (v.x + v.y);
-  const float r = fmaf(-(p * sd), g, xabs);
-  return r > 0.0f ? mh : (r < 0.0f ? ml : ((ml & 1u) ? mh : ml));
 }
 
 // Exact max->6 round-to-nearest encoding of flat slot s of a contiguous bf16
