@@ -188,6 +188,11 @@ __device__ __forceinline__ uint32_t resolve_e2m1(float xabs, uint32_t ml, uint32
   return r > 0.0f ? mh : (r < 0.0f ? ml : ((ml & 1u) ? mh : ml));
 }
 
+// Round-to-nearest E2M1 magnitude of |x| / (s g) when it is k or k + 1.
+__device__ __forceinline__ uint32_t e2m1_rne_mag_exact(float xabs, uint32_t k, float sd, float g) {
+  return k >= 7u ? 7u : resolve_e2m1(xabs, k, k + 1u, sd, g);
+}
+
 // Lattice value of E2M1 magnitude code k (0, 0.5, 1, 1.5, 2, 3, 4, 6).
 __device__ __forceinline__ float e2m1_lattice(uint32_t k) {
   return k < 4u ? 0.5f * (float)k : (k == 4u ? 2.0f : (k == 5u ? 3.0f : (k == 6u ? 4.0f : 6.0f)));
@@ -223,12 +228,37 @@ __device__ __forceinline__ uint32_t nv_scale_code(float bamax, float inv_lo, flo
   return cl == ch ? cl : resolve_e4m3(bamax, cl, ch, mult, g);
 }
 
-// Codes of the 8 elements of a lane for E4M3 scale byte c.
+// Stochastic-rounding magnitude read off one product a ~ |q| (relative error
+// at most 1.5 * 2^-22): the lattice interval comes from a's exponent and top
+// mantissa bit and the position inside it as a 22-bit fraction of the step
+// (a's mantissa bits; a * 2^23 below 0.5), compared with the draw u scaled to
+// the same units (R-17: up iff the fraction exceeds u 2^-16).  The fraction
+// is off by at most 7 units, so a comparison within 16 units, and draw 0
+// (where a product on the other side of a lattice point from q matters), is
+// marked unsure and decided exactly.
+__device__ __forceinline__ uint32_t sr_mag_fast(float a, uint32_t u, bool& unsure) {
+  const uint32_t b = as_u(a);
+  const uint32_t e = b >> 23;
+  const uint32_t f_hi = b & 0x3FFFFFu;                 // [1, 6): step 0.5 * 2^floor(log2 a)
+  const uint32_t f_mid = (b >> 1) & 0x3FFFFFu;         // [0.5, 1): step 0.5
+  const uint32_t f_lo = (uint32_t)(a * 0x1p23f);       // [0, 0.5): step 0.5
+  const uint32_t k = e >= 127u ? (b >> 22) - 252u : (e == 126u ? 1u : 0u);
+  const uint32_t fr = e >= 127u ? f_hi : (e == 126u ? f_mid : f_lo);
+  const uint32_t thr = u << 6;
+  unsure = (fr - thr + 16u) < 32u || u == 0u;
+  return a >= 6.0f ? 7u : k + (fr > thr ? 1u : 0u);
+}
+
+// Codes of the 8 elements of a lane for E4M3 scale byte c.  Round to nearest:
+// the two bracket products of s_inv[c] rounded by the FP4 conversion; they
+// agree except within 2^-22 of a decision point.  Stochastic rounding: one
+// product (sr_mag_fast).  Elements left undecided take exact FMA-residual
+// decisions; a tensor with g < 2^-100 takes correctly rounded fp64 quotients.
 template <bool SR, bool COUNT>
 __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, const NvCtx& cx,
                                               const float2* s_inv, const U4& rnd, uint32_t& satmask) {
   const float2 iv = s_inv[c];
-  uint32_t ca = 0u, cb = 0u, sa = 0u, sb = 0u;
+  uint32_t codes = 0u, sat = 0u, redo = 0u;
   if constexpr (!SR) {
     const float one = e8m0_operand(127u);
     float qa[8], qb[8];
@@ -237,41 +267,45 @@ __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, cons
       qa[i] = v[i] * iv.x;
       qb[i] = v[i] * iv.y;
     }
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[0], qa[1], one, 0);
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[2], qa[3], one, 1);
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[4], qa[5], one, 2);
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, qa[6], qa[7], one, 3);
+    uint32_t cb = 0u;
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qa[0], qa[1], one, 0);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qa[2], qa[3], one, 1);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qa[4], qa[5], one, 2);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, qa[6], qa[7], one, 3);
     cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[0], qb[1], one, 0);
     cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[2], qb[3], one, 1);
     cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[4], qb[5], one, 2);
     cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, qb[6], qb[7], one, 3);
-    if constexpr (COUNT) {
+    const uint32_t d = codes ^ cb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sa |= (fabsf(qa[i]) > 6.0f ? 1u : 0u) << i;
-        sb |= (fabsf(qb[i]) > 6.0f ? 1u : 0u) << i;
+    for (int i = 0; i < 8; ++i) {
+      uint32_t r = ((d >> (4 * i)) & 7u) != 0u ? 1u : 0u;
+      if constexpr (COUNT) {
+        const uint32_t sa = fabsf(qa[i]) > 6.0f ? 1u : 0u, sb = fabsf(qb[i]) > 6.0f ? 1u : 0u;
+        sat |= sa << i;
+        r |= sa ^ sb;
       }
+      redo |= r << i;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float a = fabsf(v[i] * iv.x), b = fabsf(v[i] * iv.y);
-      const bool nz = (v[i] != 0.0f) && (c != 0u);
-      const uint32_t u = draw16(rnd, i);
-      const uint32_t sg = (as_u(v[i]) >> 31) << 3;
-      ca |= (e2m1_sr_mag_f32(a, u, nz) | sg) << (4 * i);
-      cb |= (e2m1_sr_mag_f32(b, u, nz) | sg) << (4 * i);
+      const float a = fabsf(v[i]) * iv.x;
+      bool un;
+      const uint32_t mag = sr_mag_fast(a, draw16(rnd, i), un);
+      codes |= (mag | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+      uint32_t r = un ? 1u : 0u;
       if constexpr (COUNT) {
-        sa |= (a > 6.0f ? 1u : 0u) << i;
-        sb |= (b > 6.0f ? 1u : 0u) << i;
+        sat |= (a > 6.0f ? 1u : 0u) << i;
+        r |= fabsf(a - 6.0f) <= 0x1p-17f ? 1u : 0u;   // relative 2^-20 of 6
       }
+      redo |= r << i;
     }
   }
-  uint32_t codes = ca, sat = sa;
   if (cx.exact_all) {
     // g < 2^-100: correctly rounded fp64 quotients for every element
     const double den = (double)e4m3_value(c) * cx.g64;
-#pragma unroll 1
+#pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t mag = 0u, st = 0u;
       if (c != 0u) {
@@ -283,21 +317,19 @@ __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, cons
       codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));
       sat = (sat & ~(1u << i)) | (st << i);
     }
-  } else if (ca != cb || sa != sb) {
-    // elements whose brackets disagree: exact FMA-residual decisions
-    const float gs = cx.g;
+  } else if (redo != 0u) {
+    // undecided elements: exact FMA-residual decisions against s g
     const float sd = e4m3_value(c);
-#pragma unroll 1
+#pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t ka = (ca >> (4 * i)) & 7u, kb = (cb >> (4 * i)) & 7u;
-      const uint32_t sat_diff = ((sa ^ sb) >> i) & 1u;
-      if (ka != kb || sat_diff) {
+      if ((redo >> i) & 1u) {
+        const uint32_t k = (codes >> (4 * i)) & 7u;
         uint32_t mag = 0u, st = 0u;
         if (c != 0u) {
           const float a = fabsf(v[i]);
-          if constexpr (SR) mag = e2m1_sr_mag_exact(a, draw16(rnd, i), ka, sd, gs);
-          else mag = ka != kb ? resolve_e2m1(a, ka, kb, sd, gs) : ka;
-          st = fmaf(-(6.0f * sd), gs, a) > 0.0f ? 1u : 0u;
+          if constexpr (SR) mag = e2m1_sr_mag_exact(a, draw16(rnd, i), k, sd, cx.g);
+          else mag = e2m1_rne_mag_exact(a, k, sd, cx.g);
+          st = fmaf(-(6.0f * sd), cx.g, a) > 0.0f ? 1u : 0u;
         }
         const uint32_t sg = (as_u(v[i]) >> 31) << 3;
         codes = (codes & ~(0xFu << (4 * i))) | ((mag | sg) << (4 * i));

@@ -495,3 +495,61 @@ def test_nv_exhaustive_scale_codes_and_magnitudes(amax):
     assert_same(host(r.codes), c4, "codes (four over six)")
     assert_same(host(r.choice_bits), ch4, "choice bits (four over six)")
     assert_same(host(r.counters).astype(np.uint64), cnt4, "counters (four over six)")
+    seed = 0xC0FFEE
+    cs, ss, gs_, _, cnts = oracle.quantize_nv(x, rounding=1, seed=seed)
+    r = fq.quantize_nvfp4(xd, rounding="stochastic", seed=seed, counters=True)
+    assert host(r.global_scale)[0] == gs_
+    assert_same(host(r.scales), ss, "scales (stochastic)")
+    assert_same(host(r.codes), cs, "codes (stochastic)")
+    assert_same(host(r.counters).astype(np.uint64), cnts, "counters (stochastic)")
+
+
+_E2M1_LATTICE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+@pytest.mark.parametrize("rounding", ["rne", "stochastic"])
+@pytest.mark.parametrize("counters", [False, True])
+def test_nv_fp32_decision_points(rounding, counters):
+    """fp32 elements on, and one ulp either side of, the values where the code
+    changes: with round to nearest the midpoints of neighbouring E2M1 values
+    (and 6 for the saturation count), with stochastic rounding the thresholds
+    lo + u 2^-16 (hi - lo) of each element's own draw u and the lattice points
+    themselves, all times the block's s g.  Product-based decisions are within
+    rounding error of every one of them and must fall back to exact ones."""
+    rng = np.random.default_rng(11)
+    rows, cols, seed = 64, 512, 0x5EED
+    rmode = 1 if rounding == "stochastic" else 0
+    x = np.zeros((rows, cols), np.float32)
+    x[:, ::16] = rng.uniform(1.0, 400.0, size=(rows, cols // 16)).astype(np.float32)
+    x[0, 0] = 1000.0
+    _, s0, g0, _, _ = oracle.quantize_nv(x, rounding=rmode, seed=seed)
+    lat = _E2M1_LATTICE
+    for r in range(rows):
+        for b in range(cols // 16):
+            sg = oracle.e4m3_value(int(s0[r, b])) * float(g0)
+            for j in range(1, 16):
+                col = b * 16 + j
+                k = int(rng.integers(0, 6))
+                mode = int(rng.integers(0, 3))
+                if rmode == 0:
+                    t = 6.0 if (k == 5 and mode == 0) else 0.5 * (lat[k] + lat[k + 1])
+                elif mode == 0:
+                    u = oracle.sr_draw(seed, r * cols + col)
+                    t = lat[k] + u * 2.0 ** -16 * (lat[k + 1] - lat[k])
+                else:
+                    t = lat[k + mode - 1]
+                v = np.float32(t * sg)              # t * s * g is exact in fp64
+                d = int(rng.integers(-1, 2))
+                if d:
+                    v = np.nextafter(v, np.float32(np.inf if d > 0 else 0.0))
+                if v >= x[r, b * 16]:               # keep the block max (and so s)
+                    v = np.float32(0.25 * sg)
+                x[r, col] = -v if rng.integers(0, 2) else v
+    c, s, g, _, cnt = oracle.quantize_nv(x, rounding=rmode, seed=seed)
+    assert g == g0 and (s == s0).all()
+    r = fq.quantize_nvfp4(to_dev(x), rounding=rounding, seed=seed, counters=counters)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    if counters:
+        assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
