@@ -34,9 +34,12 @@ __device__ __forceinline__ float e8m0_operand(uint32_t b) { return as_f(b << 23)
 
 // ----------------------------------------------------------------------------
 // cross-lane helpers (wave64)
+// Every control used here reads a valid lane for every lane, so bound_ctrl
+// changes nothing; with it set (and old = 0) the compiler folds the move into
+// the consuming VALU instruction as its DPP operand.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]

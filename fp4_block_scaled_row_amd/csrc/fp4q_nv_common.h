@@ -229,24 +229,25 @@ __device__ __forceinline__ uint32_t nv_scale_code(float bamax, float inv_lo, flo
 }
 
 // Stochastic-rounding magnitude read off one product a ~ |q| (relative error
-// at most 1.5 * 2^-22): the lattice interval comes from a's exponent and top
-// mantissa bit and the position inside it as a 22-bit fraction of the step
-// (a's mantissa bits; a * 2^23 below 0.5), compared with the draw u scaled to
-// the same units (R-17: up iff the fraction exceeds u 2^-16).  The fraction
-// is off by at most 7 units, so a comparison within 16 units, and draw 0
-// (where a product on the other side of a lattice point from q matters), is
-// marked unsure and decided exactly.
-__device__ __forceinline__ uint32_t sr_mag_fast(float a, uint32_t u, bool& unsure) {
-  const uint32_t b = as_u(a);
-  const uint32_t e = b >> 23;
-  const uint32_t f_hi = b & 0x3FFFFFu;                 // [1, 6): step 0.5 * 2^floor(log2 a)
-  const uint32_t f_mid = (b >> 1) & 0x3FFFFFu;         // [0.5, 1): step 0.5
-  const uint32_t f_lo = (uint32_t)(a * 0x1p23f);       // [0, 0.5): step 0.5
-  const uint32_t k = e >= 127u ? (b >> 22) - 252u : (e == 126u ? 1u : 0u);
-  const uint32_t fr = e >= 127u ? f_hi : (e == 126u ? f_mid : f_lo);
-  const uint32_t thr = u << 6;
-  unsure = (fr - thr + 16u) < 32u || u == 0u;
-  return a >= 6.0f ? 7u : k + (fr > thr ? 1u : 0u);
+// at most 1.5 * 2^-22).  Below 1 the sum a + 1 carries a's position in the
+// step-0.5 intervals [0, .5) and [.5, 1) in its mantissa; from 1 on a's own
+// mantissa does, the step being half the power of two below a.  Either way
+// the exponent with the top mantissa bit gives the interval and the low 22
+// bits the fraction f of the step in 2^-22 units, off by at most 7 units.
+// R-17 rounds up iff f exceeds u 2^-16, u << 6 units.  `near` keeps the
+// lane's minimum of f - (u << 6) + 16, below 32 within 16 units of the
+// threshold, and of 2^22 + 16 - f, below 32 within 16 units of the next
+// lattice point, where a and q may lie in different intervals (which leaves
+// the result unchanged unless u = 0).  A lane with near < 32 is decided
+// exactly.
+__device__ __forceinline__ uint32_t sr_mag_fast(float a, uint32_t u, uint32_t& near) {
+  const bool small = a < 1.0f;
+  const uint32_t b = as_u(small ? a + 1.0f : a);
+  const uint32_t fr = b & 0x3FFFFFu;
+  const int32_t d = (int32_t)fr - (int32_t)(u << 6);
+  near = min(near, min((uint32_t)d + 16u, 0x400010u - fr));
+  const uint32_t k = (b >> 22) - (small ? 254u : 252u) + (d > 0 ? 1u : 0u);
+  return min(k, 7u);   // a >= 6 (or an overflowed product) gives k >= 7
 }
 
 // Codes of the 8 elements of a lane for E4M3 scale byte c.  Round to nearest:
@@ -288,19 +289,18 @@ __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, cons
       redo |= r << i;
     }
   } else {
+    uint32_t near = ~0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float a = fabsf(v[i]) * iv.x;
-      bool un;
-      const uint32_t mag = sr_mag_fast(a, draw16(rnd, i), un);
+      const uint32_t mag = sr_mag_fast(a, draw16(rnd, i), near);
       codes |= (mag | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
-      uint32_t r = un ? 1u : 0u;
       if constexpr (COUNT) {
         sat |= (a > 6.0f ? 1u : 0u) << i;
-        r |= fabsf(a - 6.0f) <= 0x1p-17f ? 1u : 0u;   // relative 2^-20 of 6
+        redo |= (fabsf(a - 6.0f) <= 0x1p-17f ? 1u : 0u) << i;   // relative 2^-20 of 6
       }
-      redo |= r << i;
     }
+    if (near < 32u) redo = 0xFFu;
   }
   if (cx.exact_all) {
     // g < 2^-100: correctly rounded fp64 quotients for every element
