@@ -7,6 +7,6 @@ code.  See the header of ``fp4_oracle.c`` for the pages each function follows.
 """
 from .oracle import (  # noqa: F401
     build, load, e2m1_value, e8m0_value, e4m3_value, e4m3_encode, e2m1_round,
-    mx_exponent, philox4x32_10, sr_draw, rht_sign_negative, quantize_mx,
-    quantize_nv, tensor_amax, fwht, dequantize, MX, NV, F32, BF16,
+    int4_round, mx_exponent, philox4x32_10, sr_draw, rht_sign_negative, quantize_mx,
+    quantize_nv, tensor_amax, fwht, dequantize, MX, NV, IF4, F32, BF16,
 )

@@ -19,17 +19,18 @@
  *  [EXEC] metrale_circuit "hardware::exec" module description (the exact
  *        E2M1 -> E4M3 bit conversion).
  *  [ABS] "Adaptive Block-Scaled Data Types" podcast transcript, cue 8
- *        (random Hadamard transform, stochastic rounding) and cue 10
- *        (Four Over Six).
+ *        (random Hadamard transform, stochastic rounding), cue 10
+ *        (Four Over Six), cues 14 and 17 (IF4: FP4 or scaled INT4 per
+ *        16-block, flagged in the sign bit of the block scale).
  * Where the pages leave a step open, the reading taken is named R-n; the
  * list of readings lives with the design notes of this repository.
  *
  * Parity status: every exported function is pinned by the host test suite
  * (worked examples, library routines, exact-rational brute force, closed
  * forms).  Parity unpinned: the exact Philox bit stream beyond the rocRAND
- * cross-check, and Four-Over-Six choices on blocks whose two sums of squared
- * errors are within fp32 rounding of each other (the frozen summation order
- * R-14 decides those).
+ * cross-check, and Four-Over-Six and IF4 choices on blocks whose two sums of
+ * squared errors are within fp32 rounding of each other (the frozen
+ * summation order R-14 decides those).
  */
 #include <math.h>
 #include <stdint.h>
@@ -146,6 +147,25 @@ int oracle_e2m1_round(double q, int rounding, unsigned u, int *sat)
     double a = fabs(q);
     int mag = rounding ? e2m1_stochastic_mag(a, u, sat) : e2m1_nearest_mag(a, sat);
     return s | mag;
+}
+
+/* Scaled-INT4 element of IF4 ([ABS] cues 14 and 17; reading R-22): the
+ * integer k nearest to q with ties to the even integer, |k| <= 7; |q| > 7
+ * clamps to 7 and counts as saturated.  The nibble is sign-magnitude like
+ * an E2M1 code, sign << 3 | |k|, keeping the sign of q (also of zero). */
+int oracle_int4_round(double q, int *sat)
+{
+    int s = signbit(q) ? 8 : 0, k;
+    double a = fabs(q), fl;
+    *sat = 0;
+    if (a > 7.0) {
+        *sat = 1;
+        return s | 7;
+    }
+    fl = floor(a);
+    k = (int)fl;
+    if (a - fl > 0.5 || (a - fl == 0.5 && (k & 1))) k++; /* a - fl is exact */
+    return s | k;
 }
 
 /* OCP max-based E8M0 exponent, [MXA] "Read the shared E8M0 scale":
@@ -358,6 +378,58 @@ static float block_sse_f32(const double *v, const int *codes16, int sb, float g)
     return slo + shi;
 }
 
+/* IF4's scaled-INT4 candidate ([ABS] cue 17; reading R-22) of a 16-block
+ * under the block's NVFP4 scale byte sb: the element is the integer nearest
+ * to q = x * 7 / (6 * s_dec * g), i.e. the INT4 grid is stretched by 7/6 so
+ * that 7 lands where FP4's 6 does.  fp64 decides the rounding exactly: 7x
+ * has at most 27 significant bits and 6 * s_dec * g at most 30, so a
+ * quotient that is not a tie stays at least 2^-40 (relatively) away from
+ * every half-integer.  A zero scale maps the block to signed zeros. */
+static void int4_encode_block(const double *v, int sb, float g, int *codes16, uint64_t *nsat, uint64_t *nunder)
+{
+    double sdec = oracle_e4m3_value(sb);
+    double denom = 6.0 * sdec * (double)g; /* exact */
+    int i;
+    *nsat = 0;
+    *nunder = 0;
+    for (i = 0; i < 16; i++) {
+        int sat = 0, code;
+        if (sdec == 0.0) code = signbit(v[i]) ? 8 : 0;
+        else code = oracle_int4_round(7.0 * v[i] / denom, &sat);
+        codes16[i] = code;
+        *nsat += (uint64_t)sat;
+        if (v[i] != 0.0 && (code & 7) == 0) (*nunder)++;
+    }
+}
+
+/* Reconstruction of an INT4 nibble, k * 6 * s_dec * g / 7 (reading R-23).
+ * The product is exact in fp64 (at most 33 significant bits); the fp64
+ * quotient is never within 2^-33 (relatively) of an fp32 or bf16 rounding
+ * boundary unless the exact value lies on it, so rounding it once more to
+ * fp32 or bf16 gives the single rounding of the exact value. */
+static double int4_recon(int code, double sdec, float g)
+{
+    double m = (double)(code & 7) * 6.0 * sdec * (double)g / 7.0;
+    return (code & 8) ? -m : m;
+}
+
+/* The INT4 candidate's block SSE in the order of reading R-14, with
+ * dq = fl32(k * 6 * s_dec * g / 7) in place of the FP4 reconstruction. */
+static float block_sse_int4_f32(const double *v, const int *codes16, int sb, float g)
+{
+    double sdec = oracle_e4m3_value(sb);
+    float slo = 0.0f, shi = 0.0f;
+    int i;
+    for (i = 0; i < 16; i++) {
+        float dq = (float)int4_recon(codes16[i], sdec, g);
+        float d = (float)v[i] - dq;
+        float sq = d * d;
+        if (i < 8) slo = slo + sq;
+        else shi = shi + sq;
+    }
+    return slo + shi;
+}
+
 /* [SUB4] section 2: per-tensor fp32 scale g = amax / (6 * 448) and per 16-
  * block E4M3 scale s = RNE_E4M3(bamax / (6 g)); elements round to E2M1 after
  * dividing by s * g.  policy 2 = max->6, policy 3 = Four Over Six ([ABS]
@@ -365,6 +437,10 @@ static float block_sse_f32(const double *v, const int *codes16, int sb, float g)
  * s6 = RNE_E4M3(bamax / (6 g)) and s4 = RNE_E4M3(bamax / (4 g)) and keeps the
  * candidate with the lower block SSE (ties keep max->6); the choice bit of
  * flat block b = r * (cols/16) + j is bit (b mod 8) of byte b/8, 1 = max->4.
+ * policy 4 = IF4 ([ABS] cues 14 and 17): g and s as for max->6; each
+ * block is also encoded as scaled INT4 (int4_encode_block) and keeps the
+ * candidate with the lower block SSE, ties keeping FP4 (reading R-24); an
+ * INT4 block sets bit 7 of its scale byte.  Round to nearest only.
  * global_amax (optional) replaces the in-call tensor amax.  amax excludes
  * non-finite values; amax 0 gives g = 1 (reading R-10); a nonzero amax whose
  * g would underflow to 0 takes g = 2^-149 (reading R-21).  A block holding a
@@ -376,9 +452,10 @@ int oracle_quantize_nv(int64_t rows, int64_t cols, int64_t stride, int dtype, co
 {
     int64_t r, b, i, nb = cols / 16;
     float amax = 0.0f, g, denom_mult;
-    const int fos = (policy == 3);
+    const int fos = (policy == 3), if4 = (policy == 4);
     if (rows < 0 || cols < 0 || cols % 16 != 0 || stride < cols) return OR_BAD;
-    if (policy != 2 && policy != 3) return OR_BAD;
+    if (policy != 2 && policy != 3 && policy != 4) return OR_BAD;
+    if (if4 && rounding) return OR_BAD;
     if (fos && !choice_bits) return OR_BAD;
     counters_zero(counters);
     memset(codes, 0, (size_t)(rows * cols / 2));
@@ -395,7 +472,7 @@ int oracle_quantize_nv(int64_t rows, int64_t cols, int64_t stride, int dtype, co
     for (r = 0; r < rows; r++) {
         for (b = 0; b < nb; b++) {
             double v[16], bamax = 0.0;
-            int nonfinite = 0, c6[16], c4[16], *chosen, sb, sb6, sb4, pick4 = 0;
+            int nonfinite = 0, c6[16], c4[16], ci[16], *chosen, sb, sb6, sb4, pick4 = 0;
             uint64_t sat6, und6, sat4 = 0, und4 = 0, sat, und;
             int64_t flat0 = r * cols + b * 16, fb = r * nb + b;
             for (i = 0; i < 16; i++) {
@@ -425,6 +502,16 @@ int oracle_quantize_nv(int64_t rows, int64_t cols, int64_t stride, int dtype, co
                     chosen = c4; sb = sb4; sat = sat4; und = und4;
                 }
                 if (pick4) choice_bits[fb >> 3] |= (uint8_t)(1u << (fb & 7));
+            }
+            if (if4) {
+                uint64_t sati, undi;
+                float ssef, ssei;
+                int4_encode_block(v, sb6, g, ci, &sati, &undi);
+                ssef = block_sse_f32(v, c6, sb6, g);
+                ssei = block_sse_int4_f32(v, ci, sb6, g);
+                if (ssei < ssef) {
+                    chosen = ci; sb = sb6 | 0x80; sat = sati; und = undi;
+                }
             }
             scales[fb] = (uint8_t)sb;
             if (counters) {
@@ -505,15 +592,19 @@ static uint16_t to_bf16_bits(double v)
 /* [MXA] "Encode one MXFP4 block step by step": reconstruction multiplies
  * the lattice value back by the scale.  MX: value * 2^(b - 127) (exact).
  * NV: value * s_dec * g, exact in fp64, rounded once to the output type
- * (reading R-13).  A NaN scale code yields NaN for its block.
- * format 0 = MX (block 32), 1 = NV (block 16); out_dtype 0 fp32, 1 bf16. */
+ * (reading R-13).  IF4 (format 2): a scale byte with bit 7 set marks an
+ * INT4 block, whose value is k * 6 * s_dec * g / 7 rounded once (reading
+ * R-23), s_dec from the low 7 bits; otherwise as NV.  A NaN scale code
+ * yields NaN for its block.  format 0 = MX (block 32), 1 = NV and 2 = IF4
+ * (block 16); out_dtype 0 fp32, 1 bf16. */
 int oracle_dequantize(int format, int64_t rows, int64_t cols, int block,
                       const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                       int out_dtype, void *out)
 {
     int64_t r, c;
     if (rows < 0 || cols < 0 || block <= 0 || cols % block != 0) return OR_BAD;
-    if ((format == 0 && block != 32) || (format == 1 && (block != 16 || !global_scale))) return OR_BAD;
+    if (format < 0 || format > 2) return OR_BAD;
+    if ((format == 0 && block != 32) || (format != 0 && (block != 16 || !global_scale))) return OR_BAD;
     for (r = 0; r < rows; r++)
         for (c = 0; c < cols; c++) {
             int64_t flat = r * cols + c;
@@ -522,8 +613,11 @@ int oracle_dequantize(int format, int64_t rows, int64_t cols, int block,
             double v;
             if (format == 0) {
                 v = (sb == 255) ? NAN : oracle_e2m1_value(code) * oracle_e8m0_value(sb);
+            } else if (format == 2 && (sb & 0x80)) {
+                double sdec = oracle_e4m3_value(sb & 0x7F);
+                v = isnan(sdec) ? NAN : int4_recon(code, sdec, *global_scale);
             } else {
-                double sdec = oracle_e4m3_value(sb);
+                double sdec = oracle_e4m3_value(format == 2 ? (sb & 0x7F) : sb);
                 v = isnan(sdec) ? NAN : oracle_e2m1_value(code) * sdec * (double)(*global_scale);
             }
             if (out_dtype == 0) ((float *)out)[flat] = (float)v;

@@ -16,7 +16,7 @@ SRC = os.path.join(HERE, "fp4_oracle.c")
 LIB = os.path.join(HERE, "libfp4oracle.so")
 
 F32, BF16 = 0, 1
-MX, NV = 0, 1
+MX, NV, IF4 = 0, 1, 2
 _lock = threading.Lock()
 _lib = None
 
@@ -47,6 +47,7 @@ def load():
             lib.oracle_e4m3_encode.argtypes = [dp]; lib.oracle_e4m3_encode.restype = i32
             lib.oracle_e2m1_round.argtypes = [dp, i32, C.c_uint, C.POINTER(C.c_int)]
             lib.oracle_e2m1_round.restype = i32
+            lib.oracle_int4_round.argtypes = [dp, C.POINTER(C.c_int)]; lib.oracle_int4_round.restype = i32
             lib.oracle_mx_exponent.argtypes = [dp]; lib.oracle_mx_exponent.restype = i32
             lib.oracle_philox4x32_10.argtypes = [vp, vp, vp]; lib.oracle_philox4x32_10.restype = None
             lib.oracle_sr_draw.argtypes = [u64, u64]; lib.oracle_sr_draw.restype = C.c_uint
@@ -98,6 +99,12 @@ def e4m3_encode(t):
 def e2m1_round(q, rounding=0, u=0):
     sat = C.c_int(0)
     code = load().oracle_e2m1_round(float(q), int(rounding), int(u), C.byref(sat))
+    return code, sat.value
+
+
+def int4_round(q):
+    sat = C.c_int(0)
+    code = load().oracle_int4_round(float(q), C.byref(sat))
     return code, sat.value
 
 

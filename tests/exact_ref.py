@@ -167,6 +167,64 @@ def nv_quantize(x, divisor=2688, mult=6, rounding=0, draws=None):
     return codes, scales, g, [sat, und]
 
 
+def nearest_int4_code(x, step):
+    """Scaled INT4 of IF4: the sign-magnitude nibble (x's sign) whose
+    reconstruction k*step, 0 <= k <= 7, is nearest to |x|; ties go to the even
+    k.  Returns (code, saturated) with saturated = |x| > 7*step."""
+    xs = abs(Fr(float(x)))
+    best = None
+    for k in range(8):
+        d = abs(xs - k * step)
+        if best is None or d < best[0] or (d == best[0] and k % 2 == 0 and best[1] % 2 == 1):
+            best = (d, k)
+    return (8 if _signbit(x) else 0) | best[1], xs > 7 * step
+
+
+def if4_blocks(x):
+    """IF4 of a small 2-D float64 array in exact arithmetic: g and the scale
+    byte s of NVFP4 max->6, then per 16-block both candidates -- FP4 codes on
+    the step s*g and INT4 codes on the step 6*s*g/7 -- with their exact sums
+    of squared errors.  Yields (r, b, sb, fp4_codes, int4_codes, sse_fp4,
+    sse_int4, int4_sat) and returns nothing else; g via nv_global_scale."""
+    rows, cols = x.shape
+    g = nv_global_scale(float(np.max(np.abs(x))), 2688)
+    gF = Fr(float(g))
+    for r in range(rows):
+        for b in range(cols // 16):
+            blk = x[r, b * 16:(b + 1) * 16]
+            sb = e4m3_nearest(Fr(max(abs(float(v)) for v in blk)) / (6 * gF))
+            sg = Fr(e4m3_byte_value(sb)) * gF
+            if sg == 0:
+                zero = [8 if _signbit(v) else 0 for v in blk]
+                yield r, b, sb, zero, zero, Fr(0), Fr(0), 0
+                continue
+            cf = [nearest_code(v, sg)[0] for v in blk]
+            ci = [nearest_int4_code(v, sg * 6 / 7) for v in blk]
+            ef = sum((Fr(float(v)) - E2M1[c] * sg) ** 2 for v, c in zip(blk, cf))
+            ei = sum((Fr(float(v)) - (-1 if c & 8 else 1) * (c & 7) * sg * 6 / 7) ** 2 for v, (c, _) in zip(blk, ci))
+            yield r, b, sb, cf, [c for c, _ in ci], ef, ei, sum(int(s) for _, s in ci)
+
+
+def round_to_f32_exact(v):
+    """Nearest fp32 to the exact rational v (ties to even), as a Fraction."""
+    if v == 0:
+        return Fr(0)
+    s = -1 if v < 0 else 1
+    a = abs(v)
+    e = 0
+    while Fr(2) ** e > a:
+        e -= 1
+    while Fr(2) ** (e + 1) <= a:
+        e += 1
+    q = Fr(2) ** (max(e, -126) - 23)  # quantum: 24 significant bits, subnormals below 2^-126
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fr(1, 2) or (rem == Fr(1, 2) and fl % 2 == 1):
+        fl += 1
+    return s * fl * q
+
+
 def unpack_codes(packed):
     """[rows, cols/2] bytes -> [rows, cols] codes, element 2k in the low nibble."""
     packed = np.asarray(packed, dtype=np.uint8)

@@ -332,6 +332,132 @@ def test_four_over_six_choice_and_invariants():
     assert agree > 100
 
 
+# ---------------------------------------------------------------- IF4
+def test_int4_round_ties_saturation_and_sign():
+    # nearest integer, ties to even, |q| > 7 clamps to 7 and counts; the nibble
+    # is sign-magnitude (bit 3 = sign, also for zero)
+    cases = [(0.0, 0, 0), (0.5, 0, 0), (0.5000001, 1, 0), (1.5, 2, 0), (2.5, 2, 0), (3.5, 4, 0),
+             (4.5, 4, 0), (5.5, 6, 0), (6.5, 6, 0), (6.9, 7, 0), (7.0, 7, 0), (7.0000001, 7, 1),
+             (100.0, 7, 1), (-0.0, 8, 0), (-0.3, 8, 0), (-2.6, 11, 0), (-7.5, 15, 1)]
+    for q, code, sat in cases:
+        assert oracle.int4_round(q) == (code, sat), q
+
+
+def _if4_grid_tensor():
+    """amax 18.375 makes g = 7/1024 exactly; a block max of 6g = 42/1024 gives
+    s = 1, so the INT4 step 6 s g / 7 is 6/1024 and the FP4 step s g is 7/1024."""
+    x = np.zeros((2, 64), np.float32)
+    x[0, 0] = 18.375
+    x[0, 16:32] = np.array([7, -3, 1, 5, -6, 2, 0, 4, -1, 7, 3, -5, 6, -2, 1, 0]) * 6 / 1024
+    x[0, 32:48] = np.array([6, -4, 1, 0.5, 2, -3, 1.5, 0, 6, -1, 4, 2, -0.5, 3, 1, 0]) * 7 / 1024
+    return x
+
+
+def test_if4_exact_grids_pick_their_format():
+    x = _if4_grid_tensor()
+    c, s, g, choice, cnt = oracle.quantize_nv(x, policy=4)
+    assert g == np.float32(7 / 1024) and choice is None
+    codes = codes_of(c)
+    # INT4-grid block: scaled INT4 with sign-magnitude nibbles, flag bit 7 on s = 1.0 (0x38)
+    assert s[0, 1] == 0xB8
+    assert list(codes[0, 16:32]) == [7, 11, 1, 5, 14, 2, 0, 4, 9, 7, 3, 13, 6, 10, 1, 0]
+    # FP4-grid block keeps FP4 (flag clear), codes as NVFP4 max->6
+    nc, ns, ng, _, _ = oracle.quantize_nv(x)
+    assert s[0, 2] == ns[0, 2] == 0x38 and ng == g
+    assert list(codes[0, 32:48]) == list(codes_of(nc)[0, 32:48])
+    # all-zero block: scale 0, FP4, signed zeros
+    assert s[0, 3] == 0 and s[1, 0] == 0
+    # both grids reconstruct exactly
+    for fmt_out in (oracle.F32, oracle.BF16):
+        y = oracle.dequantize(oracle.IF4, c, s, global_scale=g, out_dtype=fmt_out)
+        y = bf16_bits_to_f32(y) if fmt_out == oracle.BF16 else y
+        assert np.array_equal(y[0, 16:48], x[0, 16:48])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_if4_matches_exact_bruteforce(dtype):
+    rng = np.random.default_rng(31)
+    x = np.concatenate([_if4_grid_tensor(), _nv_cases()[:, :64],
+                        (rng.laplace(0, 1.0, (4, 64)) * np.array([[1.0], [1e-3], [30.0], [1.0]])).astype(np.float32)])
+    # a Hadamard-rotated row (where INT4 tends to win) and a heavy-tailed one
+    from scipy.linalg import hadamard
+    x = np.concatenate([x, (rng.standard_t(3, (2, 64)) @ hadamard(64) / 8).astype(np.float32)])
+    xin = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    xv = bf16_bits_to_f32(xin).astype(np.float64) if dtype == "bf16" else x.astype(np.float64)
+    c, s, g, _, cnt = oracle.quantize_nv(xin, policy=4)
+    assert g == X.nv_global_scale(float(np.abs(xv).max()), 2688)
+    codes = codes_of(c)
+    decided = picked_int4 = 0
+    sat = und = 0
+    for r, b, sb, cf, ci, ef, ei, isat in X.if4_blocks(xv):
+        got = list(codes[r, b * 16:(b + 1) * 16])
+        assert s[r, b] & 0x7F == sb
+        int4 = bool(s[r, b] & 0x80)
+        assert got == (ci if int4 else cf)
+        blk = xv[r, b * 16:(b + 1) * 16]
+        sat += isat if int4 else sum(int(X.nearest_code(v, Fr(X.e4m3_byte_value(sb)) * Fr(float(g)))[1])
+                                     for v in blk) if sb else 0
+        und += sum(1 for v, cc in zip(blk, got) if v != 0 and cc & 7 == 0)
+        if ef == ei or abs(ef - ei) <= Fr(1, 10 ** 5) * max(ef, ei):
+            continue                                 # near-tie: the frozen fp32 order decides
+        assert int4 == (ei < ef)
+        decided += 1
+        picked_int4 += int4
+    assert [int(cnt[0]), int(cnt[1])] == [sat, und]
+    assert decided >= 30 and 0 < picked_int4 < decided
+
+
+def test_if4_blocks_never_worse_than_nvfp4():
+    rng = np.random.default_rng(32)
+    x = bf16_bits_to_f32(f32_to_bf16_bits((rng.standard_t(4, (16, 256)) * 0.5).astype(np.float32)))
+    c4, s4, g4, _, _ = oracle.quantize_nv(x, policy=4)
+    cn, sn, gn, _, _ = oracle.quantize_nv(x)
+    assert g4 == gn
+    k4, kn = codes_of(c4), codes_of(cn)
+    gF = Fr(float(gn))
+    for r in range(16):
+        for b in range(16):
+            sl = slice(b * 16, (b + 1) * 16)
+            if not s4[r, b] & 0x80:                 # FP4 kept: byte-identical to NVFP4 max->6
+                assert s4[r, b] == sn[r, b] and list(k4[r, sl]) == list(kn[r, sl])
+                continue
+            sg = Fr(X.e4m3_byte_value(int(s4[r, b]) & 0x7F)) * gF
+            ei = sum((Fr(float(v)) - (-1 if cc & 8 else 1) * (cc & 7) * sg * 6 / 7) ** 2 for v, cc in zip(x[r, sl], k4[r, sl]))
+            ef = sum((Fr(float(v)) - X.E2M1[cc] * sg) ** 2 for v, cc in zip(x[r, sl], kn[r, sl]))
+            assert ei <= ef * (1 + Fr(1, 10 ** 5))
+
+
+def test_dequantize_if4_single_rounding():
+    rng = np.random.default_rng(33)
+    codes = rng.integers(0, 256, (6, 32), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (6, 4), dtype=np.uint8) | (rng.integers(0, 2, (6, 4), dtype=np.uint8) << 7)
+    scales[0, 0] = 0xFF
+    scales[0, 1] = 0x7F
+    for g in (np.float32(0.0123456), np.float32(1.0) / np.float32(2688), np.float32(3.3e-20), np.float32(2.0 ** -149)):
+        o32 = oracle.dequantize(oracle.IF4, codes, scales, global_scale=g, out_dtype=oracle.F32)
+        o16 = bf16_bits_to_f32(oracle.dequantize(oracle.IF4, codes, scales, global_scale=g, out_dtype=oracle.BF16))
+        cc = codes_of(codes)
+        for r in range(6):
+            for i in range(64):
+                sb = int(scales[r, i // 16])
+                if sb & 0x7F == 0x7F:
+                    assert np.isnan(o32[r, i]) and np.isnan(o16[r, i])
+                    continue
+                sd = Fr(X.e4m3_byte_value(sb & 0x7F)) * Fr(float(g))
+                c = int(cc[r, i])
+                if sb & 0x80:
+                    exact = (-1 if c & 8 else 1) * (c & 7) * 6 * sd / 7
+                else:
+                    exact = X.E2M1[c] * sd
+                assert Fr(float(o32[r, i])) == X.round_to_f32_exact(exact)
+                assert Fr(float(o16[r, i])) == X.round_to_bf16_exact(exact)
+
+
+def test_if4_rejects_stochastic_rounding():
+    with pytest.raises(ValueError):
+        oracle.quantize_nv(np.zeros((1, 16), np.float32), policy=4, rounding=1)
+
+
 # ---------------------------------------------------------------- FWHT / RHT
 def test_fwht_matches_dense_hadamard():
     from scipy.linalg import hadamard
