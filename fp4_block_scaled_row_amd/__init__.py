@@ -9,7 +9,8 @@ Formats (pages cited by title and section):
     Audit the 4.25-Bit Blocks", "Read the shared E8M0 scale").
   * NVFP4: 16-element blocks, E4M3 block scale and fp32 tensor scale
     ("Sub-4-Bit Microscaling", section 2); Four Over Six ("Adaptive
-    Block-Scaled Data Types" transcript, cue 10).
+    Block-Scaled Data Types" transcript, cue 10); IF4, FP4 or 7/6-scaled
+    INT4 per block flagged in the scale's sign bit (transcript, cues 14, 17).
   * Rotations: full-row FWHT ("Sub-4-Bit Microscaling", section 3) and the
     16-point random Hadamard transform (transcript, cue 8).
 """
@@ -105,13 +106,15 @@ def quantize_nvfp4(x, *, policy="max6", rounding="rne", seed=0, rotation=None, g
                    return_rotated=False, counters=False, out=None, workspace=None):
     """NVFP4-quantize a 2-D fp32/bf16 GPU tensor along its rows.
 
-    policy "max6" (g = amax/2688) or "four_over_six" (g = amax/1792, per-block
-    max->6 / max->4 choice).  global_amax: optional 1-element fp32 GPU tensor.
+    policy "max6" (g = amax/2688), "four_over_six" (g = amax/1792, per-block
+    max->6 / max->4 choice) or "if4" (g as max6, per-block FP4 / scaled INT4
+    choice in bit 7 of the scale byte; round to nearest only).  global_amax: optional 1-element fp32 GPU tensor.
     Returns NvResult(codes, scales (E4M3), global_scale fp32[1], choice_bits
     uint8 or None, rotated or None, counters or None)."""
     _check_input(x)
     rows, cols = x.shape
-    pol = {"max6": _lib.FP4Q_SCALE_NV_MAX6, "four_over_six": _lib.FP4Q_SCALE_FOUR_OVER_SIX}[policy]
+    pol = {"max6": _lib.FP4Q_SCALE_NV_MAX6, "four_over_six": _lib.FP4Q_SCALE_FOUR_OVER_SIX,
+           "if4": _lib.FP4Q_SCALE_IF4}[policy]
     a = _args(x, 16, pol, 0, rounding, rotation, seed)
     dev = x.device
     if out is None:
@@ -150,8 +153,8 @@ def fwht(x, transform_size=None, random_signs=False, seed=0, out=None):
 
 def dequantize(fmt, codes, scales, global_scale=None, out_dtype=torch.float32, out=None):
     """Reconstruct [rows, cols] from packed codes and block scales.  fmt is
-    "mxfp4" or "nvfp4" (the latter needs the fp32 global_scale tensor)."""
-    f = {"mxfp4": _lib.FP4Q_MXFP4, "nvfp4": _lib.FP4Q_NVFP4}[fmt]
+    "mxfp4", "nvfp4" or "if4" (the latter two need the fp32 global_scale tensor)."""
+    f = {"mxfp4": _lib.FP4Q_MXFP4, "nvfp4": _lib.FP4Q_NVFP4, "if4": _lib.FP4Q_IF4}[fmt]
     rows, half = codes.shape
     cols = half * 2
     od = {torch.float32: _lib.FP4Q_F32, torch.bfloat16: _lib.FP4Q_BF16}[out_dtype]

@@ -13,8 +13,8 @@ LIB_PATH = os.path.join(HERE, "libfp4q.so")
 
 FP4Q_OK, FP4Q_ERR_INVALID_ARG, FP4Q_ERR_UNSUPPORTED, FP4Q_ERR_WORKSPACE, FP4Q_ERR_NONFINITE, FP4Q_ERR_HIP = range(6)
 FP4Q_F32, FP4Q_BF16 = 0, 1
-FP4Q_MXFP4, FP4Q_NVFP4 = 0, 1
-FP4Q_SCALE_OCP_MAX, FP4Q_SCALE_MANUAL, FP4Q_SCALE_NV_MAX6, FP4Q_SCALE_FOUR_OVER_SIX = 0, 1, 2, 3
+FP4Q_MXFP4, FP4Q_NVFP4, FP4Q_IF4 = 0, 1, 2
+FP4Q_SCALE_OCP_MAX, FP4Q_SCALE_MANUAL, FP4Q_SCALE_NV_MAX6, FP4Q_SCALE_FOUR_OVER_SIX, FP4Q_SCALE_IF4 = 0, 1, 2, 3, 4
 FP4Q_ROUND_RNE, FP4Q_ROUND_STOCHASTIC = 0, 1
 FP4Q_ROT_NONE, FP4Q_ROT_FWHT_ROW, FP4Q_ROT_RHT16 = 0, 1, 2
 

@@ -42,13 +42,15 @@ fp4q_status check_quant(const fp4q_quant_args* a, const void* x, const fp4q_outp
   if (a->in_dtype != FP4Q_F32 && a->in_dtype != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
   if (a->rounding != FP4Q_ROUND_RNE && a->rounding != FP4Q_ROUND_STOCHASTIC) return FP4Q_ERR_INVALID_ARG;
   if (a->rotation < FP4Q_ROT_NONE || a->rotation > FP4Q_ROT_RHT16) return FP4Q_ERR_INVALID_ARG;
-  if (a->scale_policy < FP4Q_SCALE_OCP_MAX || a->scale_policy > FP4Q_SCALE_FOUR_OVER_SIX) return FP4Q_ERR_INVALID_ARG;
+  if (a->scale_policy < FP4Q_SCALE_OCP_MAX || a->scale_policy > FP4Q_SCALE_IF4) return FP4Q_ERR_INVALID_ARG;
   const int want_block = format == FP4Q_MXFP4 ? 32 : 16;
   if (a->block_size != want_block) return FP4Q_ERR_UNSUPPORTED;
   if (format == FP4Q_MXFP4 && a->scale_policy != FP4Q_SCALE_OCP_MAX && a->scale_policy != FP4Q_SCALE_MANUAL)
     return FP4Q_ERR_UNSUPPORTED;
-  if (format == FP4Q_NVFP4 && a->scale_policy != FP4Q_SCALE_NV_MAX6 && a->scale_policy != FP4Q_SCALE_FOUR_OVER_SIX)
+  if (format == FP4Q_NVFP4 && a->scale_policy != FP4Q_SCALE_NV_MAX6 && a->scale_policy != FP4Q_SCALE_FOUR_OVER_SIX &&
+      a->scale_policy != FP4Q_SCALE_IF4)
     return FP4Q_ERR_UNSUPPORTED;
+  if (a->scale_policy == FP4Q_SCALE_IF4 && a->rounding != FP4Q_ROUND_RNE) return FP4Q_ERR_UNSUPPORTED;
   if (a->scale_policy == FP4Q_SCALE_MANUAL && (a->manual_exponent < -127 || a->manual_exponent > 127))
     return FP4Q_ERR_INVALID_ARG;
   if (a->cols % want_block != 0) return FP4Q_ERR_INVALID_ARG;      // incomplete blocks
@@ -80,6 +82,7 @@ QuantLaunch make_launch(const fp4q_quant_args* a, const void* x, const fp4q_outp
   q.manual = a->scale_policy == FP4Q_SCALE_MANUAL;
   q.manual_e = a->manual_exponent;
   q.four_over_six = a->scale_policy == FP4Q_SCALE_FOUR_OVER_SIX;
+  q.if4 = a->scale_policy == FP4Q_SCALE_IF4;
   q.seed = a->seed;
   q.rht_signs = a->rotation == FP4Q_ROT_RHT16 ? (rht_sign_word(a->seed, 0u, 0) & 0xFFFFu) : 0u;
   q.codes = o->codes;
@@ -190,17 +193,17 @@ fp4q_status fp4q_fwht(int64_t rows, int64_t d, int64_t in_row_stride, int32_t in
 fp4q_status fp4q_dequantize(int32_t format, int64_t rows, int64_t cols, int32_t block_size, const uint8_t* codes,
                             const uint8_t* scales, const float* global_scale, int32_t out_dtype, void* out,
                             void* hip_stream) {
-  if (format != FP4Q_MXFP4 && format != FP4Q_NVFP4) return FP4Q_ERR_INVALID_ARG;
+  if (format != FP4Q_MXFP4 && format != FP4Q_NVFP4 && format != FP4Q_IF4) return FP4Q_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0) return FP4Q_ERR_INVALID_ARG;
   if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
   if (block_size != (format == FP4Q_MXFP4 ? 32 : 16)) return FP4Q_ERR_UNSUPPORTED;
   if (cols % block_size != 0) return FP4Q_ERR_INVALID_ARG;
   if (rows * cols == 0) return FP4Q_OK;
   if (!codes || !scales || !out) return FP4Q_ERR_INVALID_ARG;
-  if (format == FP4Q_NVFP4 && !global_scale) return FP4Q_ERR_INVALID_ARG;
+  if (format != FP4Q_MXFP4 && !global_scale) return FP4Q_ERR_INVALID_ARG;
   if (!aligned(codes, 4) || !aligned(out, 16)) return FP4Q_ERR_UNSUPPORTED;
   DequantLaunch dl;
-  dl.format = format == FP4Q_MXFP4 ? 0 : 1;
+  dl.format = format == FP4Q_MXFP4 ? 0 : (format == FP4Q_NVFP4 ? 1 : 2);
   dl.rows = rows;
   dl.cols = cols;
   dl.codes = codes;

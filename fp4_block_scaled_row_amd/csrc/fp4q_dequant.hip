@@ -14,6 +14,11 @@
 // below 2^-100, where the error could underflow, use the fp64 product
 // (value * s * g has <= 31 significant bits).  bf16 outputs are stored
 // non-temporally: they are written once and not read back by this kernel.
+// IF4 ("Adaptive Block-Scaled Data Types" transcript, cues 14 and 17): a
+// block whose scale byte has bit 7 set holds sign-magnitude INT4 nibbles k
+// worth k * 6 s g / 7, looked up in a per-workgroup table of the 8
+// magnitudes of each scale code rounded once to the output type; the other
+// blocks decode as NV.
 #include "fp4q_flat.h"
 
 namespace fp4q {
@@ -43,14 +48,35 @@ __device__ __forceinline__ uint32_t bf16_of_product(float vs, float g) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Output bits (fp32, or bf16 in the low half) of k * 6 * s_c * g / 7 rounded
+// once: the numerator is exact in fp64 and the fp64 quotient is never within
+// 2^-33 (relatively) of an fp32 or bf16 rounding boundary unless the exact
+// value lies on it.  Its fp32 rounding can still land exactly on a bf16
+// midpoint; the fp64 value then says on which side the exact value is.
+template <int OUT>
+__device__ __forceinline__ uint32_t int4_magnitude_bits(int c, int k, float g) {
+  const double q = (double)k * 6.0 * (double)e4m3_value((uint32_t)c) * (double)g / 7.0;
+  const float f = (float)q;
+  const uint32_t b = as_u(f);
+  if constexpr (OUT == kF32) return b;
+  const uint32_t hi = b >> 16;
+  if ((b & 0xFFFFu) != 0x8000u) return (b + 0x7FFFu + (hi & 1u)) >> 16;
+  return q > (double)f ? hi + 1u : (q < (double)f ? hi : hi + (hi & 1u));
+}
+
 template <int FMT, int OUT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int64_t nslots) {
+  __shared__ uint32_t s_i4[FMT == 2 ? 1024 : 1];
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int64_t ntiles = (nslots + 63) >> 6;
   float g = 1.0f;
-  if constexpr (FMT == 1) g = *d.global_scale;
+  if constexpr (FMT != 0) g = *d.global_scale;
+  if constexpr (FMT == 2) {
+    for (int e = threadIdx.x; e < 1024; e += kThreads) s_i4[e] = int4_magnitude_bits<OUT>(e >> 3, e & 7, g);
+    __syncthreads();
+  }
   const float one = e8m0_operand(127u);
   for (int64_t g0 = wave; g0 * kUnroll < ntiles; g0 += nwaves) {
     uint32_t cw[kUnroll], sb[kUnroll];
@@ -94,6 +120,31 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantLaunch d, int6
         }
       } else {
         const bool nan = sb[u] == 0x7Fu || sb[u] == 0xFFu;
+        if constexpr (FMT == 2) {
+          if (sb[u] & 0x80u) {   // INT4 block
+            const uint32_t* row = s_i4 + 8 * (sb[u] & 0x7Fu);
+            if constexpr (OUT == kF32) {
+              float o[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const uint32_t nib = (cw[u] >> (4 * i)) & 15u;
+                o[i] = nan ? as_f(0x7FC00000u) : as_f(row[nib & 7u] | ((nib & 8u) << 28));
+              }
+              store_rotated(static_cast<float*>(d.out), s, o);
+            } else {
+              uint32_t h[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t n0 = (cw[u] >> (8 * i)) & 15u, n1 = (cw[u] >> (8 * i + 4)) & 15u;
+                h[i] = (row[n0 & 7u] | ((n0 & 8u) << 12)) | ((row[n1 & 7u] | ((n1 & 8u) << 12)) << 16);
+              }
+              if (nan) h[0] = h[1] = h[2] = h[3] = 0x7FC07FC0u;
+              const u32x4_t o = {h[0], h[1], h[2], h[3]};
+              __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.out) + (s << 3)));
+            }
+            continue;
+          }
+        }
         const float sd = e4m3_value(sb[u] & 0x7Fu);
         float val[8];
         float2_t p;
@@ -156,6 +207,7 @@ hipError_t launch_t(const DequantLaunch& d, hipStream_t st) {
 hipError_t launch_dequant(const DequantLaunch& d, hipStream_t st) {
   if (d.rows == 0 || d.cols == 0) return hipSuccess;
   if (d.format == 0) return d.out_dtype == kF32 ? launch_t<0, kF32>(d, st) : launch_t<0, kBF16>(d, st);
+  if (d.format == 2) return d.out_dtype == kF32 ? launch_t<2, kF32>(d, st) : launch_t<2, kBF16>(d, st);
   return d.out_dtype == kF32 ? launch_t<1, kF32>(d, st) : launch_t<1, kBF16>(d, st);
 }
 

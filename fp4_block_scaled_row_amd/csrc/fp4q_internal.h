@@ -18,6 +18,7 @@ struct QuantLaunch {
   int manual;                // MX: manual exponent policy
   int manual_e;
   int four_over_six;         // NV
+  int if4;                   // NV: per block FP4 or scaled INT4
   uint64_t seed;
   uint32_t rht_signs;        // 16-bit sign mask of the RHT diagonal
   uint8_t* codes;
@@ -67,7 +68,7 @@ struct FwhtLaunch {
 hipError_t launch_fwht(const FwhtLaunch& f, hipStream_t s);
 
 struct DequantLaunch {
-  int format;                // 0 MX, 1 NV
+  int format;                // 0 MX, 1 NV, 2 IF4
   int64_t rows, cols;
   const uint8_t* codes;
   const uint8_t* scales;

@@ -33,6 +33,7 @@ namespace fp4q {
 namespace {
 
 constexpr int kUnroll = 4;
+constexpr int kPolMax6 = 0, kPolFos = 1, kPolIf4 = 2;   // block scaling policies
 
 template <int IN, int ROT, bool CONTIG>
 __device__ __forceinline__ void load_values(const QuantLaunch& q, const SlotRaw<IN>& r, int lane, float v[8]) {
@@ -98,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
   if (blockIdx.x == 0 && threadIdx.x < 3 && q.counters) q.counters[threadIdx.x] = 0ull;
 }
 
-template <int IN, int ROT, bool SR, bool FOS, bool COUNT, bool CONTIG>
+template <int IN, int ROT, bool SR, int POL, bool COUNT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int npartials) {
+  constexpr bool FOS = POL == kPolFos;
   // bf16 values rounded to nearest: one product per element with the adjusted
   // multiplier of the block's scale code; otherwise (fp32 or rotated values,
   // stochastic rounding) the bracketed products
@@ -107,6 +109,8 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   __shared__ float2 s_inv[128];
   __shared__ float2 s_adj[kAdj ? 128 : 1];
   __shared__ float2 s_eps[8];
+  __shared__ float2 s_i4[POL == kPolIf4 ? 128 : 1];
+  __shared__ float s_dq[POL == kPolIf4 ? 1024 : 1];
   __shared__ uint32_t s_red[kWaves];
   const int lane = threadIdx.x & 63;
 
@@ -129,6 +133,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   nv_context(as_f(amax_bits), FOS, cx);
   if constexpr (kAdj) nv_fill_adjusted_table(s_adj, s_inv, s_eps, cx, threadIdx.x);
   else nv_fill_inverse_table(s_inv, cx, threadIdx.x, kThreads);
+  if constexpr (POL == kPolIf4) if4_fill_tables(s_i4, s_dq, cx, threadIdx.x, kThreads);
   if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
   __syncthreads();
 
@@ -215,6 +220,20 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
           }
         }
       }
+      if constexpr (POL == kPolIf4) {
+        uint32_t sati;
+        const uint32_t ci = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati);
+        float ef = half_sse(v, codes, c6, cx.g);
+        float ei = half_sse_int4(v, ci, s_dq + 8 * c6);
+        const float pf = dpp_xor1_f(ef), pi = dpp_xor1_f(ei);
+        ef = odd ? (pf + ef) : (ef + pf);   // S_lo + S_hi on both lanes
+        ei = odd ? (pi + ei) : (ei + pi);
+        if (ei < ef) {
+          codes = ci;
+          sbyte = c6 | 0x80u;
+          satm = sati;
+        }
+      }
       if (nonfinite) {
         codes = 0u;
         sbyte = 0x7Fu;
@@ -252,7 +271,7 @@ int amax_grid(int64_t nslots) {
   return (int)(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
-template <int IN, int ROT, bool SR, bool FOS, bool COUNT, bool CONTIG>
+template <int IN, int ROT, bool SR, int POL, bool COUNT, bool CONTIG>
 hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   int np = 0;
   if (!q.global_amax) {
@@ -268,22 +287,27 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
-  hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, FOS, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
+  hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, POL, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
   return hipGetLastError();
 }
 
-template <int IN, int ROT, bool SR, bool FOS, bool COUNT>
+template <int IN, int ROT, bool SR, int POL, bool COUNT>
 hipError_t d_contig(const QuantLaunch& q, hipStream_t st) {
-  return q.stride == q.cols ? launch_t<IN, ROT, SR, FOS, COUNT, true>(q, st)
-                            : launch_t<IN, ROT, SR, FOS, COUNT, false>(q, st);
+  return q.stride == q.cols ? launch_t<IN, ROT, SR, POL, COUNT, true>(q, st)
+                            : launch_t<IN, ROT, SR, POL, COUNT, false>(q, st);
 }
-template <int IN, int ROT, bool SR, bool FOS>
+template <int IN, int ROT, bool SR, int POL>
 hipError_t d_count(const QuantLaunch& q, hipStream_t st) {
-  return q.counters ? d_contig<IN, ROT, SR, FOS, true>(q, st) : d_contig<IN, ROT, SR, FOS, false>(q, st);
+  return q.counters ? d_contig<IN, ROT, SR, POL, true>(q, st) : d_contig<IN, ROT, SR, POL, false>(q, st);
 }
 template <int IN, int ROT, bool SR>
 hipError_t d_fos(const QuantLaunch& q, hipStream_t st) {
-  return q.four_over_six ? d_count<IN, ROT, SR, true>(q, st) : d_count<IN, ROT, SR, false>(q, st);
+  if (q.four_over_six) return d_count<IN, ROT, SR, kPolFos>(q, st);
+  if (q.if4) {
+    if constexpr (SR) return hipErrorInvalidValue;   // rejected by the entry point
+    else return d_count<IN, ROT, SR, kPolIf4>(q, st);
+  }
+  return d_count<IN, ROT, SR, kPolMax6>(q, st);
 }
 template <int IN, int ROT>
 hipError_t d_sr(const QuantLaunch& q, hipStream_t st) {

@@ -395,6 +395,114 @@ __device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint
   return acc;
 }
 
+// ---------------------------------------------------------------- IF4
+// "Adaptive Block-Scaled Data Types" transcript, cues 14 and 17: besides its
+// FP4 encoding every 16-block is also encoded as scaled INT4 under the same
+// E4M3 scale s -- integers k in [-7, 7] standing for k * 6 s g / 7, the
+// integer grid stretched by 7/6 so that 7 lands on FP4's 6 -- and keeps the
+// one with the lower block SSE (ties keep FP4), flagged in bit 7 of the
+// scale byte.  Nibbles are sign-magnitude like E2M1 codes.
+
+// s_i4[c] = (7 / (6 s_c g)) (1 -+ 2^-22) (0 for c = 0; unused when
+// exact_all), s_dq[8 c + k] = RN32(k * 6 s_c g / 7): k * 6 * s_c * g is exact
+// in fp64 (at most 33 significant bits) and the fp64 quotient is never
+// within 2^-33 (relatively) of an fp32 rounding boundary unless the exact
+// value lies on it, so converting it gives the single rounding.
+__device__ __forceinline__ void if4_fill_tables(float2* s_i4, float* s_dq, const NvCtx& cx, int tid, int nthreads) {
+  for (int e = tid; e < 128 * 8; e += nthreads) {
+    const int c = e >> 3, k = e & 7;
+    const double sd = (double)e4m3_value((uint32_t)c);
+    s_dq[e] = (float)((double)k * 6.0 * sd * cx.g64 / 7.0);
+    if (k == 0) {
+      float2 m = make_float2(0.0f, 0.0f);
+      if (c != 0 && c != 127 && !cx.exact_all) {
+        const double inv = 7.0 / (6.0 * sd * cx.g64);
+        m = make_float2((float)(inv * (1.0 - 0x1p-22)), (float)(inv * (1.0 + 0x1p-22)));
+      }
+      s_i4[c] = m;
+    }
+  }
+}
+
+// INT4 nibbles (and |q| > 7 saturation flags) of a lane's 8 elements under
+// scale byte c, q = 7 x / (6 s g) rounded to the nearest integer, ties to
+// even, |k| <= 7.  The two bracket products round (rint, monotone) to the
+// same integer except within 2^-21 of a half-integer; there the sign of
+// 7 |x| - (2k + 1) 3 s g, exact in one fp64 FMA (7 |x| and (2k + 1) 3 s
+// have at most 27 and 10 significant bits), decides.  q > 7 is |x| > 6 s g,
+// an exact fp32 FMA sign.  g < 2^-100 takes correctly rounded fp64
+// quotients, which decide exactly.
+template <bool COUNT>
+__device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c, const NvCtx& cx,
+                                                   const float2* s_i4, uint32_t& satmask) {
+  uint32_t codes = 0u, sat = 0u, redo = 0u;
+  const float sd = e4m3_value(c);
+  if (!cx.exact_all) {
+    const float2 m = s_i4[c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = fabsf(v[i]) * m.x, b = fabsf(v[i]) * m.y;
+      const float ra = fminf(rintf(a), 7.0f), rb = fminf(rintf(b), 7.0f);
+      codes |= ((uint32_t)ra | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+      uint32_t r = ra != rb ? 1u : 0u;
+      if constexpr (COUNT) {
+        const uint32_t sa = a > 7.0f ? 1u : 0u, sb = b > 7.0f ? 1u : 0u;
+        sat |= sa << i;
+        r |= sa ^ sb;
+      }
+      redo |= r << i;
+    }
+    if (redo != 0u && c != 0u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((redo >> i) & 1u) {
+          const float ax = fabsf(v[i]);
+          const uint32_t ka = (codes >> (4 * i)) & 7u;
+          uint32_t k = ka;
+          if (ka < 7u) {
+            const double r = fma(-((double)(2u * ka + 1u) * 3.0 * (double)sd), cx.g64, 7.0 * (double)ax);
+            k = r > 0.0 ? ka + 1u : (r < 0.0 ? ka : ka + (ka & 1u));
+          }
+          const uint32_t st = fmaf(-(6.0f * sd), cx.g, ax) > 0.0f ? 1u : 0u;
+          codes = (codes & ~(7u << (4 * i))) | (k << (4 * i));
+          sat = (sat & ~(1u << i)) | (st << i);
+        }
+      }
+    }
+  } else if (c != 0u) {
+    const double den = 6.0 * (double)sd * cx.g64;
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+      const double q = 7.0 * (double)fabsf(v[i]) / den;
+      const uint32_t k = q > 7.0 ? 7u : (uint32_t)rint(q);
+      codes |= (k | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+      sat |= (q > 7.0 ? 1u : 0u) << i;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes |= ((as_u(v[i]) >> 31) << 3) << (4 * i);
+  }
+  satmask = COUNT ? sat : 0u;
+  return codes;
+}
+
+// Half of the INT4 candidate's block SSE in the order of half_sse, with
+// dq = +-s_dq[8 c + k] (dq_row = s_dq + 8 c).
+__device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t codes, const float* dq_row) {
+#pragma clang fp contract(off)
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t nib = (codes >> (4 * i)) & 15u;
+    const float m = dq_row[nib & 7u];
+    const float dq = (nib & 8u) ? -m : m;
+    const float d = v[i] - dq;
+    const float sq = d * d;
+    acc = acc + sq;
+  }
+  return acc;
+}
+
 // The whole max->6 NVFP4 encoding of one slot of raw bf16 data (8 values at
 // flat slot s; the lane pair 2k, 2k+1 holds one 16-block and must execute
 // together): widen, optional RHT16, block amax, scale byte, codes, counters,

@@ -443,7 +443,7 @@ int64_t resident_workgroups() {
 
 // Whether the single-launch kernel takes this call, and its launch shape.
 bool nv_resident_shape(const QuantLaunch& q, int* grid, int* nres) {
-  if (q.in_dtype != kBF16 || q.four_over_six || q.global_amax || q.stride != q.cols || q.nslots == 0) return false;
+  if (q.in_dtype != kBF16 || q.four_over_six || q.if4 || q.global_amax || q.stride != q.cols || q.nslots == 0) return false;
   if (q.rotation != kRotNone || q.stochastic || q.counters) return false;   // those variants stream twice
   const int64_t cap = resident_workgroups();
   if (cap <= 0) return false;

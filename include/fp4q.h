@@ -24,6 +24,13 @@
  *    the max->6 and max->4 scalings has the lower block sum of squared error
  *    (ties keep max->6) and records a choice bit ("Adaptive Block-Scaled Data
  *    Types" transcript, cue 10).
+ *  - IF4: g and the block scale s as for NVFP4 max->6; each 16-block is
+ *    encoded twice, as FP4 and as scaled INT4 (integers -7..7 standing for
+ *    k * 6 s g / 7, i.e. the integer grid stretched by 7/6 so 7 lands on
+ *    FP4's 6), and keeps the one with the lower block sum of squared error
+ *    (ties keep FP4); bit 7 of the block's E4M3 scale byte, unused by
+ *    NVFP4, is set for INT4 ("Adaptive Block-Scaled Data Types" transcript,
+ *    cues 14 and 17).  INT4 nibbles are sign-magnitude like E2M1 codes.
  *  - Stochastic rounding: round |q| up iff it exceeds lo + (u/65536)(hi-lo)
  *    for its neighbouring lattice points, u a 16-bit draw of Philox4x32-10
  *    keyed by (seed, flat element index r*cols + c): field (i mod 8) of
@@ -72,12 +79,13 @@ typedef enum {
 } fp4q_status;
 
 enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 };                       /* element types */
-enum { FP4Q_MXFP4 = 0, FP4Q_NVFP4 = 1 };                    /* formats */
+enum { FP4Q_MXFP4 = 0, FP4Q_NVFP4 = 1, FP4Q_IF4 = 2 };      /* formats (IF4: dequantize only) */
 enum {
   FP4Q_SCALE_OCP_MAX = 0,        /* MX: e = floor(log2(amax/4)), clamp [-127,127], amax 0 -> 0 */
   FP4Q_SCALE_MANUAL = 1,         /* MX: e = manual_exponent for every block, in [-127, 127]   */
   FP4Q_SCALE_NV_MAX6 = 2,        /* NV: g = amax/2688, s = RNE_E4M3(bamax/(6g))               */
-  FP4Q_SCALE_FOUR_OVER_SIX = 3   /* NV: g = amax/1792, per block max->6 or max->4 by lower SSE */
+  FP4Q_SCALE_FOUR_OVER_SIX = 3,  /* NV: g = amax/1792, per block max->6 or max->4 by lower SSE */
+  FP4Q_SCALE_IF4 = 4             /* NV: g, s as NV_MAX6; per block FP4 or 7/6-scaled INT4      */
 };
 enum { FP4Q_ROUND_RNE = 0, FP4Q_ROUND_STOCHASTIC = 1 };
 enum {
@@ -133,8 +141,12 @@ fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args *args, const void *x,
                                 size_t workspace_bytes, void *hip_stream);
 
 /* NVFP4 quantization ("Sub-4-Bit Microscaling", section 2; Four Over Six,
- * transcript cue 10).  block_size 16, policy NV_MAX6 or FOUR_OVER_SIX,
- * rotation NONE or RHT16, rounding RNE or STOCHASTIC.  The tensor amax is
+ * transcript cue 10; IF4, transcript cues 14 and 17).  block_size 16, policy
+ * NV_MAX6, FOUR_OVER_SIX or IF4, rotation NONE or RHT16, rounding RNE or
+ * STOCHASTIC (IF4: RNE only, STOCHASTIC is UNSUPPORTED).  IF4 writes no
+ * choice bits (choice_bits may be NULL): an INT4 block has bit 7 of its
+ * scale byte set; counters count the kept candidate (INT4 saturates at
+ * |7x / (6 s g)| > 7).  The tensor amax is
  * computed in the call (a first pass over x, after rotation) unless
  * `global_amax` (device pointer to one finite non-negative float) is given.
  * amax 0 gives g = 1; a nonzero amax whose g underflows gives g = 2^-149.
@@ -159,9 +171,12 @@ fp4q_status fp4q_fwht(int64_t rows, int64_t d, int64_t in_row_stride, int32_t in
 
 /* Reconstruction ("Encode one MXFP4 block step by step": multiply back by
  * the scale).  MX: value * 2^(b-127), exact.  NV: value * s * g rounded once
- * to the output type.  A NaN scale code gives NaN for its block.  format
- * FP4Q_MXFP4 (block 32) or FP4Q_NVFP4 (block 16, global_scale: device
- * pointer to g); out_dtype FP4Q_F32 or FP4Q_BF16; out is [rows][cols]. */
+ * to the output type.  IF4: a block whose scale byte has bit 7 set holds
+ * INT4 nibbles, k * 6 * s * g / 7 rounded once, s from the low 7 bits; other
+ * blocks as NV.  A NaN scale code (low 7 bits 0x7F for NV and IF4) gives NaN
+ * for its block.  format FP4Q_MXFP4 (block 32), FP4Q_NVFP4 or FP4Q_IF4
+ * (block 16, global_scale: device pointer to g); out_dtype FP4Q_F32 or
+ * FP4Q_BF16; out is [rows][cols]. */
 fp4q_status fp4q_dequantize(int32_t format, int64_t rows, int64_t cols, int32_t block_size,
                             const uint8_t *codes, const uint8_t *scales,
                             const float *global_scale, int32_t out_dtype, void *out,

@@ -102,6 +102,10 @@ def test_mxfp4_rejects(kwargs, status):
     (dict(block=16, policy=_lib.FP4Q_SCALE_OCP_MAX), _lib.FP4Q_ERR_UNSUPPORTED),   # MX policy on NV
     (dict(block=16, policy=_lib.FP4Q_SCALE_NV_MAX6, rotation=_lib.FP4Q_ROT_FWHT_ROW), _lib.FP4Q_ERR_UNSUPPORTED),
     (dict(block=16, policy=_lib.FP4Q_SCALE_NV_MAX6, cols=40), _lib.FP4Q_ERR_INVALID_ARG),
+    (dict(block=16, policy=_lib.FP4Q_SCALE_IF4, rounding=_lib.FP4Q_ROUND_STOCHASTIC), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(block=16, policy=_lib.FP4Q_SCALE_IF4, rotation=_lib.FP4Q_ROT_FWHT_ROW), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(block=32, policy=_lib.FP4Q_SCALE_IF4), _lib.FP4Q_ERR_UNSUPPORTED),       # IF4 needs 16-blocks
+    (dict(block=16, policy=5), _lib.FP4Q_ERR_INVALID_ARG),
 ])
 def test_nvfp4_rejects(kwargs, status):
     lib = _lib_or_skip()
@@ -128,7 +132,9 @@ def test_fwht_and_dequant_reject():
     assert lib.fp4q_fwht(4, 64, 64, 5, FAKE, FAKE, 64, 0, 0, None) == _lib.FP4Q_ERR_INVALID_ARG
     assert lib.fp4q_dequantize(0, 4, 64, 16, FAKE, FAKE, None, 0, FAKE, None) == _lib.FP4Q_ERR_UNSUPPORTED
     assert lib.fp4q_dequantize(1, 4, 64, 16, FAKE, FAKE, None, 0, FAKE, None) == _lib.FP4Q_ERR_INVALID_ARG
-    assert lib.fp4q_dequantize(2, 4, 64, 32, FAKE, FAKE, None, 0, FAKE, None) == _lib.FP4Q_ERR_INVALID_ARG
+    assert lib.fp4q_dequantize(3, 4, 64, 16, FAKE, FAKE, FAKE, 0, FAKE, None) == _lib.FP4Q_ERR_INVALID_ARG
+    assert lib.fp4q_dequantize(2, 4, 64, 32, FAKE, FAKE, FAKE, 0, FAKE, None) == _lib.FP4Q_ERR_UNSUPPORTED
+    assert lib.fp4q_dequantize(2, 4, 64, 16, FAKE, FAKE, None, 0, FAKE, None) == _lib.FP4Q_ERR_INVALID_ARG
     assert lib.fp4q_dequantize(0, 4, 48, 32, FAKE, FAKE, None, 0, FAKE, None) == _lib.FP4Q_ERR_INVALID_ARG
 
 

@@ -553,3 +553,163 @@ def test_nv_fp32_decision_points(rounding, counters):
     assert_same(host(r.codes), c, "codes")
     if counters:
         assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+
+
+# ------------------------------------------------------------------ IF4
+def _if4_check(r, c, s, g, cnt=None):
+    assert host(r.global_scale)[0] == g
+    assert r.choice_bits is None
+    assert_same(host(r.scales), s, "scales (bit 7: INT4)")
+    assert_same(host(r.codes), c, "codes")
+    if cnt is not None:
+        assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rotation", [None, "rht16"])
+def test_if4_small(rows, cols, dtype, rotation):
+    pad = 16 if rows % 2 else 0
+    full = make_input(rows, cols, dtype, rows * 11 + cols, pad=pad)
+    xd = to_dev(full)[:, :cols]
+    for counters in (False, True):
+        r = fq.quantize_nvfp4(xd, policy="if4", rotation=rotation, seed=321, counters=counters,
+                              return_rotated=rotation is not None)
+        if rotation is None:
+            c, s, g, _, cnt = oracle.quantize_nv(full, cols=cols, policy=4)
+        else:
+            rot = host(r.rotated)
+            assert rel_l2(rot, oracle.fwht(np.ascontiguousarray(full[:, :cols]), t=16, random_signs=True,
+                                           seed=321)) <= RTOL_ROT
+            c, s, g, _, cnt = oracle.quantize_nv(rot, policy=4)
+        _if4_check(r, c, s, g, cnt if counters else None)
+
+
+def test_if4_grid_blocks_and_decision_points():
+    """g = 7/1024 (tensor amax 18.375) and block maxima 42 S / 1024 give block
+    scales S exactly, so the INT4 grid k * 6 S / 1024, its half-integer
+    decision points and FP4's grid are exact fp32 numbers.  Blocks mix INT4
+    grid points with elements on, and one ulp either side of, the INT4
+    decision points (exact ties go to the even integer) and the saturation
+    threshold, so that both candidates, the bracket fallbacks and the choice
+    are exercised."""
+    rng = np.random.default_rng(17)
+    S = [0.5, 1.0, 1.25, 2.0, 3.5, 10.0, 104.0, 448.0]
+    rows, nb = 64, 32
+    x = np.zeros((rows, nb * 16), np.float32)
+    for r in range(rows):
+        for b in range(nb):
+            sv = S[(r + b) % len(S)]
+            step = 6.0 * sv / 1024.0
+            blk = np.zeros(16)
+            blk[0] = 7 * step                           # block max: s = S exactly
+            n_grid = int(rng.integers(6, 15))
+            for j in range(1, 16):
+                if j <= n_grid:
+                    t = float(rng.integers(0, 8))
+                else:
+                    t = float(rng.integers(0, 7)) + 0.5 if rng.integers(0, 4) else 7.0
+                v = np.float32(t * step)
+                d = int(rng.integers(-1, 2))
+                if d:
+                    v = np.nextafter(v, np.float32(np.inf if d > 0 else 0.0))
+                blk[j] = min(float(v), 7 * step)
+            blk *= np.where(rng.integers(0, 2, 16) == 1, -1.0, 1.0)
+            blk[0] = 7 * step
+            x[r, b * 16:(b + 1) * 16] = blk
+    x[0, 0] = 18.375
+    c, s, g, _, cnt = oracle.quantize_nv(x, policy=4)
+    assert g == np.float32(7 / 1024)
+    n_int4 = int(np.count_nonzero(s & 0x80))
+    assert n_int4 > rows * nb // 4 and n_int4 < rows * nb    # both candidates are kept somewhere
+    xd = to_dev(x)
+    for counters in (False, True):
+        r = fq.quantize_nvfp4(xd, policy="if4", counters=counters)
+        _if4_check(r, c, s, g, cnt if counters else None)
+    amax = torch.tensor([18.375], dtype=torch.float32, device=xd.device)
+    _if4_check(fq.quantize_nvfp4(xd, policy="if4", global_amax=amax), c, s, g)
+
+
+@pytest.mark.parametrize("amax", [418.0, 168.0, 2.0 ** -95])
+def test_if4_exhaustive_scale_codes_and_magnitudes(amax):
+    a_bits = int(f32_to_bf16_bits(np.array([amax], np.float32))[0])
+    x = _exhaustive_nv_tensor(a_bits)
+    c, s, g, _, cnt = oracle.quantize_nv(x, policy=4)
+    if amax > 1.0:   # (at 2^-95 every squared error underflows in fp32: the SSEs tie and FP4 is kept)
+        assert np.count_nonzero(s & 0x80) > 0
+    _if4_check(fq.quantize_nvfp4(to_dev(x), policy="if4", counters=True), c, s, g, cnt)
+
+
+def test_if4_specials_and_empty():
+    for dtype in ("f32", "bf16"):
+        x = _special_tensor(dtype)
+        c, s, g, _, cnt = oracle.quantize_nv(x, policy=4)
+        _if4_check(fq.quantize_nvfp4(to_dev(x), policy="if4", counters=True), c, s, g, cnt)
+    e = fq.quantize_nvfp4(torch.empty((0, 64), dtype=torch.bfloat16, device=gpu()), policy="if4")
+    assert host(e.global_scale)[0] == 1.0
+    with pytest.raises(fq.Fp4qError):
+        fq.quantize_nvfp4(to_dev(np.zeros((2, 32), np.float32)), policy="if4", rounding="stochastic")
+
+
+def test_if4_rht_grad_8192():
+    """IF4 on the Hadamard-rotated gradient workload, where INT4 is expected to win often."""
+    x = workload("grad_bf16_8192")
+    r = fq.quantize_nvfp4(to_dev(x), policy="if4", rotation="rht16", seed=workloads.SR_SEED, return_rotated=True,
+                          counters=True)
+    rot = host(r.rotated)
+    c, s, g, _, cnt = oracle.quantize_nv(rot, policy=4)
+    _if4_check(r, c, s, g, cnt)
+    assert np.count_nonzero(s & 0x80) > s.size // 4
+
+
+def test_if4_weight_8192x28672_sampled_rows():
+    x = workload("weight_bf16_8192x28672")
+    r = fq.quantize_nvfp4(to_dev(x), policy="if4")
+    amax = oracle.tensor_amax(x)
+    g_ref = np.float32(amax) / np.float32(2688)
+    assert host(r.global_scale)[0] == g_ref
+    codes, scales = host(r.codes), host(r.scales)
+    for r0 in (0, 4095, 8192 - 160):
+        r1 = r0 + 160
+        c, s, g, _, _ = oracle.quantize_nv(x[r0:r1], policy=4, global_amax=amax)
+        assert g == g_ref
+        assert_same(codes[r0:r1], c, "codes rows %d-%d" % (r0, r1))
+        assert_same(scales[r0:r1], s, "scales rows %d-%d" % (r0, r1))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequant_if4_all_codes_and_scales(out_dtype):
+    rng = np.random.default_rng(5)
+    rows, cols = 16, 512
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    codes[0, :128] = np.arange(128, dtype=np.uint8) * 2
+    scales = rng.integers(0, 256, (rows, cols // 16), dtype=np.uint8)
+    scales[0, :] = np.arange(32) * 8 + 1                     # both flag values over the code range
+    scales[1, 0], scales[1, 1] = 0x7F, 0xFF
+    od = oracle.F32 if out_dtype == torch.float32 else oracle.BF16
+    for gs in (np.float32(0.0123457), np.float32(7 / 1024), np.float32(2.0 ** -149), np.float32(1e30)):
+        gdev = torch.tensor([gs], dtype=torch.float32, device=gpu())
+        got = host(fq.dequantize("if4", to_dev(codes), to_dev(scales), gdev, out_dtype=out_dtype))
+        want = oracle.dequantize(oracle.IF4, codes, scales, gs, out_dtype=od)
+        if out_dtype == torch.float32:
+            got, want = bits(got), bits(want)
+            isnan = lambda a: np.isnan(a.view(np.float32))
+        else:
+            isnan = lambda a: np.isnan(bf16_bits_to_f32(a))
+        assert_same(isnan(got), isnan(want), "NaN positions")
+        assert_same(np.where(isnan(got), 0, got), np.where(isnan(want), 0, want), "values g=%r" % gs)
+
+
+def test_if4_round_trip_8192():
+    x = workload("act_bf16_8192")
+    xd = to_dev(x)
+    r = fq.quantize_nvfp4(xd, policy="if4")
+    codes, scales, g = host(r.codes), host(r.scales), host(r.global_scale)[0]
+    rows = slice(0, 256)
+    c, s, g_ref, _, _ = oracle.quantize_nv(x[rows], policy=4, global_amax=oracle.tensor_amax(x))
+    assert g == g_ref
+    assert_same(codes[rows], c, "codes")
+    assert_same(scales[rows], s, "scales")
+    d = host(fq.dequantize("if4", r.codes, r.scales, r.global_scale, out_dtype=torch.bfloat16))
+    want = oracle.dequantize(oracle.IF4, codes[rows], scales[rows], g, out_dtype=oracle.BF16)
+    assert_same(d[rows], want, "bf16 reconstruction")
