@@ -146,7 +146,16 @@ def profile_kernels(dev, reps=5):
     run("C4 Four-Over-Six NVFP4 bf16 8192x28672",
         lambda: fq.quantize_nvfp4(x4, policy="four_over_six", out=o4, workspace=ws),
         n4 * 2 + n4 // 2 + n4 // 16 + 4 + n4 // 128)
-    del x4, o4
+    del o4
+    oi = fq.quantize_nvfp4(x4, policy="if4", workspace=ws)
+    run("IF4 bf16 8192x28672 (weights of C4)",
+        lambda: fq.quantize_nvfp4(x4, policy="if4", out=oi, workspace=ws), n4 * 2 + n4 // 2 + n4 // 16 + 4)
+    del x4
+    yi = torch.empty((oi.codes.shape[0], oi.codes.shape[1] * 2), dtype=torch.bfloat16, device=dev)
+    run("IF4 dequantize -> bf16 8192x28672",
+        lambda: fq.dequantize("if4", oi.codes, oi.scales, oi.global_scale, out_dtype=torch.bfloat16, out=yi),
+        n4 * 2 + n4 // 2 + n4 // 16 + 4)
+    del oi, yi
 
     x1 = dev_tensor("mx_f32_1024")
     o1 = fq.quantize_mxfp4(x1, counters=True)
@@ -165,7 +174,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
-                    help="launch each kernel of the five workloads a few times (for rocprofv3) and print "
+                    help="launch each kernel of the five workloads and of IF4 a few times (for rocprofv3) and print "
                          "event timings as text; no JSON line")
     a = ap.parse_args()
     if a.gpus != 1:
@@ -259,6 +268,21 @@ def main():
         fq.dequantize("nvfp4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=dq_out[k])
     dq_sec = timed(dq_step, a.steps, a.warmup)
 
+    # ---- IF4 of the same tensor (amax pass + encode pass) and its dequantize
+    if4_out = [fq.quantize_nvfp4(x, policy="if4", workspace=ws) for x in xs]
+
+    def if4_step(i):
+        k = i % REPLICAS
+        fq.quantize_nvfp4(xs[k], policy="if4", out=if4_out[k], workspace=ws)
+    if4_sec = timed(if4_step, a.steps, a.warmup)
+
+    def if4_dq_step(i):
+        k = i % REPLICAS
+        o = if4_out[k]
+        fq.dequantize("if4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=dq_out[k])
+    if4_dq_sec = timed(if4_dq_step, a.steps, a.warmup)
+    if4_int4_frac = float((if4_out[0].scales >= 0x80).float().mean())
+
     line = {
         "metric": "quantize GB/s and % HBM peak, 8192² bf16→NVFP4/MXFP4, 1×MI355X",
         "value": round(value, 2),
@@ -294,6 +318,12 @@ def main():
         "dequant_nvfp4_to_bf16": {"value": round(DQ_BYTES / dq_sec / 1e9, 2), "unit": "GB/s",
                                   "ms_per_step": round(dq_sec * 1e3, 5), "bytes_per_step": DQ_BYTES,
                                   "kernel": "dequant_kernel", "traffic": traffic_for("dequant_kernel")},
+        "if4": {"value": round(NV_BYTES / if4_sec / 1e9, 2), "unit": "GB/s",
+                "frac_of_hbm_peak": round(NV_BYTES / if4_sec / 1e9 / HBM_PEAK_GBPS, 4),
+                "ms_per_step": round(if4_sec * 1e3, 5), "bytes_per_step": NV_BYTES,
+                "kernels": "nv_amax_kernel + nv_quant_kernel (IF4 policy)", "int4_block_fraction": round(if4_int4_frac, 4),
+                "dequant_to_bf16": {"value": round(NV_BYTES / if4_dq_sec / 1e9, 2), "unit": "GB/s",
+                                    "ms_per_step": round(if4_dq_sec * 1e3, 5)}},
         "kernel_source_sha": kernel_source_sha(),
     }
     if not a.no_cpu_baseline:

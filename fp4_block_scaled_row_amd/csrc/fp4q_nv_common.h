@@ -403,70 +403,66 @@ __device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint
 // one with the lower block SSE (ties keep FP4), flagged in bit 7 of the
 // scale byte.  Nibbles are sign-magnitude like E2M1 codes.
 
-// s_i4[c] = (7 / (6 s_c g)) (1 -+ 2^-22) (0 for c = 0; unused when
-// exact_all), s_dq[8 c + k] = RN32(k * 6 s_c g / 7): k * 6 * s_c * g is exact
+// s_i4[c] = RN32(7 / (6 s_c g)) (0 for c = 0; unused when exact_all),
+// s_dq[8 c + k] = RN32(k * 6 s_c g / 7): k * 6 * s_c * g is exact
 // in fp64 (at most 33 significant bits) and the fp64 quotient is never
 // within 2^-33 (relatively) of an fp32 rounding boundary unless the exact
 // value lies on it, so converting it gives the single rounding.
-__device__ __forceinline__ void if4_fill_tables(float2* s_i4, float* s_dq, const NvCtx& cx, int tid, int nthreads) {
+__device__ __forceinline__ void if4_fill_tables(float* s_i4, float* s_dq, const NvCtx& cx, int tid, int nthreads) {
   for (int e = tid; e < 128 * 8; e += nthreads) {
     const int c = e >> 3, k = e & 7;
     const double sd = (double)e4m3_value((uint32_t)c);
     s_dq[e] = (float)((double)k * 6.0 * sd * cx.g64 / 7.0);
-    if (k == 0) {
-      float2 m = make_float2(0.0f, 0.0f);
-      if (c != 0 && c != 127 && !cx.exact_all) {
-        const double inv = 7.0 / (6.0 * sd * cx.g64);
-        m = make_float2((float)(inv * (1.0 - 0x1p-22)), (float)(inv * (1.0 + 0x1p-22)));
-      }
-      s_i4[c] = m;
-    }
+    if (k == 0) s_i4[c] = (c != 0 && c != 127 && !cx.exact_all) ? (float)(7.0 / (6.0 * sd * cx.g64)) : 0.0f;
   }
 }
 
 // INT4 nibbles (and |q| > 7 saturation flags) of a lane's 8 elements under
 // scale byte c, q = 7 x / (6 s g) rounded to the nearest integer, ties to
-// even, |k| <= 7.  The two bracket products round (rint, monotone) to the
-// same integer except within 2^-21 of a half-integer; there the sign of
-// 7 |x| - (2k + 1) 3 s g, exact in one fp64 FMA (7 |x| and (2k + 1) 3 s
-// have at most 27 and 10 significant bits), decides.  q > 7 is |x| > 6 s g,
-// an exact fp32 FMA sign.  g < 2^-100 takes correctly rounded fp64
-// quotients, which decide exactly.
+// even, |k| <= 7.  One product a = |x| * RN32(7 / (6 s g)) is within
+// 2^-23 (relatively) of |q|, so rint(a) is the answer unless a lies within
+// 2^-19 of a half-integer (or, when counting, of 7); such a lane is decided
+// exactly: the sign of 7 |x| - (2k + 1) 3 s g is exact in one fp64 FMA
+// (7 |x| and (2k + 1) 3 s have at most 27 and 10 significant bits), and
+// q > 7 is |x| > 6 s g, an exact fp32 FMA sign.  g < 2^-100 takes
+// correctly rounded fp64 quotients, which decide exactly.
 template <bool COUNT>
 __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c, const NvCtx& cx,
-                                                   const float2* s_i4, uint32_t& satmask) {
-  uint32_t codes = 0u, sat = 0u, redo = 0u;
+                                                   const float* s_i4, uint32_t& satmask) {
+  uint32_t codes = 0u, sat = 0u;
   const float sd = e4m3_value(c);
   if (!cx.exact_all) {
-    const float2 m = s_i4[c];
+    const float m = s_i4[c];
+    bool unsure = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float a = fabsf(v[i]) * m.x, b = fabsf(v[i]) * m.y;
-      const float ra = fminf(rintf(a), 7.0f), rb = fminf(rintf(b), 7.0f);
-      codes |= ((uint32_t)ra | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
-      uint32_t r = ra != rb ? 1u : 0u;
+      const float a = fabsf(v[i]) * m;
+      const float r = rintf(a);
+      unsure |= fabsf(a - r) > 0.5f - 0x1p-19f;
+      codes |= ((uint32_t)fminf(r, 7.0f) | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
       if constexpr (COUNT) {
-        const uint32_t sa = a > 7.0f ? 1u : 0u, sb = b > 7.0f ? 1u : 0u;
-        sat |= sa << i;
-        r |= sa ^ sb;
+        sat |= (a > 7.0f ? 1u : 0u) << i;
+        unsure |= fabsf(a - 7.0f) <= 0x1p-17f;
       }
-      redo |= r << i;
     }
-    if (redo != 0u && c != 0u) {
+    if (unsure && c != 0u) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if ((redo >> i) & 1u) {
-          const float ax = fabsf(v[i]);
-          const uint32_t ka = (codes >> (4 * i)) & 7u;
-          uint32_t k = ka;
-          if (ka < 7u) {
-            const double r = fma(-((double)(2u * ka + 1u) * 3.0 * (double)sd), cx.g64, 7.0 * (double)ax);
-            k = r > 0.0 ? ka + 1u : (r < 0.0 ? ka : ka + (ka & 1u));
+        const float ax = fabsf(v[i]);
+        const double x7 = 7.0 * (double)ax;
+        const uint32_t k0 = (codes >> (4 * i)) & 7u;
+        // the product's integer is off by at most one: step from k0 - 1
+        uint32_t k = k0 > 0u ? k0 - 1u : 0u;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (k < 7u) {
+            const double r = fma(-((double)(2u * k + 1u) * 3.0 * (double)sd), cx.g64, x7);
+            if (r > 0.0 || (r == 0.0 && (k & 1u))) ++k;
           }
-          const uint32_t st = fmaf(-(6.0f * sd), cx.g, ax) > 0.0f ? 1u : 0u;
-          codes = (codes & ~(7u << (4 * i))) | (k << (4 * i));
-          sat = (sat & ~(1u << i)) | (st << i);
         }
+        const uint32_t st = fmaf(-(6.0f * sd), cx.g, ax) > 0.0f ? 1u : 0u;
+        codes = (codes & ~(7u << (4 * i))) | (k << (4 * i));
+        sat = (sat & ~(1u << i)) | (st << i);
       }
     }
   } else if (c != 0u) {
