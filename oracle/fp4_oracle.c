@@ -236,10 +236,11 @@ int oracle_rht_sign_negative(uint64_t seed, int64_t j)
 /* ------------------------------------------------------------------ */
 /* Inputs                                                              */
 /* ------------------------------------------------------------------ */
-/* dtype 0: fp32, dtype 1: bf16 stored as its 16 raw bits. */
+/* dtype 0: fp32, dtype 1: bf16 stored as its 16 raw bits, dtype 2: fp64. */
 static double load_elem(const void *x, int dtype, int64_t idx)
 {
     if (dtype == 0) return (double)((const float *)x)[idx];
+    if (dtype == 2) return ((const double *)x)[idx];
     {
         uint32_t b = (uint32_t)((const uint16_t *)x)[idx] << 16;
         float f;
@@ -561,6 +562,28 @@ int oracle_fwht(int64_t rows, int64_t d, int64_t stride, int dtype, const void *
             for (i = 0; i < t; i++) w[i] *= norm;
         }
     }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* SiLU_and_Mul                                                        */
+/* ------------------------------------------------------------------ */
+/* [SUB4] section 3, the online rotation fused into the SwiGLU epilogue
+ * before down_proj: the activation is h = SiLU(gate) * up with
+ * SiLU(g) = g / (1 + e^-g) (reading R-25), here in fp64 with libm exp, one
+ * value per (row, column) of two [rows][stride] inputs of dtype 0/1; the
+ * result is a dense [rows][cols] fp64 array. */
+int oracle_silu_mul(int64_t rows, int64_t cols, int64_t stride, int dtype, const void *gate,
+                    const void *up, double *out)
+{
+    int64_t r, c;
+    if (rows < 0 || cols < 0 || stride < cols || (dtype != 0 && dtype != 1)) return OR_BAD;
+    for (r = 0; r < rows; r++)
+        for (c = 0; c < cols; c++) {
+            double g = load_elem(gate, dtype, r * stride + c);
+            double u = load_elem(up, dtype, r * stride + c);
+            out[r * cols + c] = g / (1.0 + exp(-g)) * u;
+        }
     return OR_OK;
 }
 

@@ -57,6 +57,8 @@ def load():
             lib.oracle_quantize_nv.argtypes = [i64, i64, i64, i32, vp, i32, i32, u64, vp, vp, vp, vp, vp, vp]
             lib.oracle_quantize_nv.restype = i32
             lib.oracle_fwht.argtypes = [i64, i64, i64, i32, vp, vp, i64, i32, u64]
+            lib.oracle_silu_mul.argtypes = [i64, i64, i64, i32, vp, vp, vp]
+            lib.oracle_silu_mul.restype = i32
             lib.oracle_fwht.restype = i32
             lib.oracle_dequantize.argtypes = [i32, i64, i64, i32, vp, vp, vp, i32, vp]
             lib.oracle_dequantize.restype = i32
@@ -170,8 +172,12 @@ def tensor_amax(x):
 
 
 def fwht(x, t=None, random_signs=False, seed=0):
-    """Normalised Walsh-Hadamard transform of each t-chunk of each row (fp64 out)."""
-    x, dt = _as_input(x)
+    """Normalised Walsh-Hadamard transform of each t-chunk of each row (fp64 out).
+    x: float32, uint16 (bf16 bits) or float64."""
+    if np.asarray(x).dtype == np.float64:
+        x, dt = np.ascontiguousarray(x), 2
+    else:
+        x, dt = _as_input(x)
     rows, d = x.shape
     t = d if t is None else t
     y = np.zeros((rows, d), np.float64)
@@ -179,6 +185,20 @@ def fwht(x, t=None, random_signs=False, seed=0):
     if rc != 0:
         raise ValueError("oracle_fwht rejected the arguments")
     return y
+
+
+def silu_mul(gate, up):
+    """SiLU(gate) * up in fp64 for two same-shape float32 or uint16 (bf16 bits) arrays."""
+    gate, dt = _as_input(gate)
+    up, dt2 = _as_input(up)
+    if gate.shape != up.shape or dt != dt2:
+        raise ValueError("silu_mul: gate and up must have the same shape and dtype")
+    rows, cols = gate.shape
+    out = np.zeros((rows, cols), np.float64)
+    rc = load().oracle_silu_mul(rows, cols, cols, dt, _ptr(gate), _ptr(up), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_silu_mul rejected the arguments")
+    return out
 
 
 def dequantize(fmt, codes, scales, global_scale=None, out_dtype=F32):

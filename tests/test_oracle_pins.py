@@ -458,6 +458,34 @@ def test_if4_rejects_stochastic_rounding():
         oracle.quantize_nv(np.zeros((1, 16), np.float32), policy=4, rounding=1)
 
 
+# ---------------------------------------------------------------- SiLU_and_Mul
+def test_silu_mul_closed_forms_and_library():
+    from scipy.special import expit
+    rng = np.random.default_rng(41)
+    g = np.concatenate([rng.standard_normal(500) * 4, [0.0, -0.0, 1e-30, -1e-30, 30.0, -30.0, 80.0, -80.0]])
+    g = g.astype(np.float32)
+    u = rng.standard_normal(g.size).astype(np.float32)
+    one = np.ones_like(g)
+    h = oracle.silu_mul(g[None, :], u[None, :])[0]
+    ref = g.astype(np.float64) * expit(g.astype(np.float64)) * u.astype(np.float64)   # library routine
+    assert np.allclose(h, ref, rtol=1e-14, atol=1e-300)
+    s_pos = oracle.silu_mul(g[None, :], one[None, :])[0]
+    s_neg = oracle.silu_mul(-g[None, :], one[None, :])[0]
+    assert np.allclose(s_pos - s_neg, g.astype(np.float64), rtol=1e-14, atol=1e-300)   # SiLU(x) - SiLU(-x) = x
+    assert s_pos[-8] == 0.0 and s_pos[-4] == pytest.approx(30.0, rel=1e-12)
+    assert abs(s_pos[-1]) < 1e-30                                   # SiLU(-80) ~ -80 e^-80
+    assert s_pos[-6] == pytest.approx(0.5e-30, rel=1e-12)          # SiLU(x) ~ x/2 near 0
+    hb = oracle.silu_mul(f32_to_bf16_bits(g[None, :]), f32_to_bf16_bits(u[None, :]))[0]
+    gb, ub = (bf16_bits_to_f32(f32_to_bf16_bits(a)).astype(np.float64) for a in (g, u))
+    assert np.allclose(hb, gb * expit(gb) * ub, rtol=1e-14, atol=1e-300)
+
+
+def test_fwht_of_fp64_input_matches_dense_hadamard():
+    from scipy.linalg import hadamard
+    x = np.random.default_rng(42).standard_normal((3, 256))
+    assert np.allclose(oracle.fwht(x), x @ hadamard(256) / 16.0, rtol=1e-13, atol=1e-13)
+
+
 # ---------------------------------------------------------------- FWHT / RHT
 def test_fwht_matches_dense_hadamard():
     from scipy.linalg import hadamard

@@ -54,6 +54,9 @@ WORKLOADS = {
                                        "N(0,0.02) bf16 8192x28672, 0.1% of entries x20"),
     "grad_bf16_8192": Workload("grad_bf16_8192", 8192, 8192, "bf16", 105,
                                "Laplace(0,1e-3) bf16 8192x8192 gradients"),
+    "gate_up_bf16_16384x8192": Workload("gate_up_bf16_16384x8192", 16384, 16384, "bf16", 106,
+                                        "[gate | up] bf16 16384x(2x8192): gate N(0,1.5), up N(0,1) with "
+                                        "8 fixed outlier channels x100"),
 }
 
 SR_SEED = 0x5EED  # Philox key of the gradient workload
@@ -79,6 +82,15 @@ def _draw(name, rows, cols, seed):
         x.reshape(-1)[idx] *= 20.0
     elif name == "grad_bf16_8192":
         x = rng.laplace(0.0, 1e-3, size=(rows, cols))
+    elif name == "gate_up_bf16_16384x8192":
+        # gate and up halves of a SwiGLU input row (the up-projection output
+        # carries a few outlier channels, which SiLU_and_Mul keeps)
+        d = cols // 2
+        x = np.empty((rows, cols), np.float32)
+        x[:, :d] = 1.5 * rng.standard_normal((rows, d))
+        x[:, d:] = rng.standard_normal((rows, d))
+        c = rng.choice(d, 8, replace=False)
+        x[:, d + c] *= 100.0
     else:
         raise KeyError(name)
     return x
