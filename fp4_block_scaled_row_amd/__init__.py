@@ -13,6 +13,8 @@ Formats (pages cited by title and section):
     INT4 per block flagged in the scale's sign bit (transcript, cues 14, 17).
   * Rotations: full-row FWHT ("Sub-4-Bit Microscaling", section 3) and the
     16-point random Hadamard transform (transcript, cue 8).
+  * Fused SwiGLU epilogue: SiLU(gate) * up -> row FWHT -> MXFP4 in one kernel
+    ("Sub-4-Bit Microscaling", section 3, the online SiLU_and_Mul rotation).
 """
 from collections import namedtuple
 
@@ -22,7 +24,7 @@ from . import _lib
 from ._lib import Fp4qError, load  # noqa: F401
 
 __all__ = [
-    "quantize_mxfp4", "quantize_nvfp4", "fwht", "dequantize", "workspace_bytes",
+    "quantize_mxfp4", "quantize_nvfp4", "silu_mul_fwht_mxfp4", "fwht", "dequantize", "workspace_bytes",
     "check_counters", "version", "MxResult", "NvResult", "Fp4qError",
 ]
 
@@ -135,6 +137,31 @@ def quantize_nvfp4(x, *, policy="max6", rounding="rne", seed=0, rotation=None, g
                      _ptr(out.rotated), _ptr(out.counters))
     _lib.check(_lib.load().fp4q_quantize_nvfp4(a, _ptr(x), _ptr(global_amax), o, _ptr(workspace), ws_bytes,
                                                _stream()), "fp4q_quantize_nvfp4")
+    return out
+
+
+def silu_mul_fwht_mxfp4(gate, up, *, policy="ocp", manual_exponent=0, rounding="rne", seed=0,
+                        return_rotated=False, counters=False, out=None):
+    """Fused SwiGLU epilogue: MXFP4 of the row FWHT of SiLU(gate) * up, for two
+    same-shape 2-D fp32/bf16 GPU tensors with the same row stride (e.g.
+    x[:, :d] and x[:, d:]).  Returns an MxResult like quantize_mxfp4."""
+    _check_input(gate)
+    _check_input(up)
+    if gate.shape != up.shape or gate.dtype != up.dtype or (gate.shape[0] > 1 and gate.stride(0) != up.stride(0)):
+        raise ValueError("fp4q: gate and up must have the same shape, dtype and row stride")
+    rows, cols = gate.shape
+    pol = {"ocp": _lib.FP4Q_SCALE_OCP_MAX, "manual": _lib.FP4Q_SCALE_MANUAL}[policy]
+    a = _args(gate, 32, pol, manual_exponent, rounding, "fwht_row", seed)
+    dev = gate.device
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        rot = torch.empty((rows, cols), dtype=torch.float32, device=dev) if return_rotated else None
+        cnt = torch.empty(3, dtype=torch.int64, device=dev) if counters else None
+        out = MxResult(codes, scales, rot, cnt)
+    o = _lib.Outputs(_ptr(out.codes), _ptr(out.scales), None, None, _ptr(out.rotated), _ptr(out.counters))
+    _lib.check(_lib.load().fp4q_silu_mul_fwht_mxfp4(a, _ptr(gate), _ptr(up), o, _stream()),
+               "fp4q_silu_mul_fwht_mxfp4")
     return out
 
 

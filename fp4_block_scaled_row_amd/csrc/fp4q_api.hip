@@ -147,6 +147,44 @@ fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args* args, const void* x, cons
   return hip_status(launch_mx_quant(q, s));
 }
 
+fp4q_status fp4q_silu_mul_fwht_mxfp4(const fp4q_quant_args* args, const void* gate, const void* up,
+                                     const fp4q_outputs* out, void* hip_stream) {
+  fp4q_status st = check_quant(args, gate, out, FP4Q_MXFP4);
+  if (st != FP4Q_OK) return st;
+  if (args->rotation != FP4Q_ROT_FWHT_ROW) return FP4Q_ERR_UNSUPPORTED;
+  if (!is_pow2(args->cols) || args->cols < 32 || args->cols > 16384) return FP4Q_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t n = args->rows * args->cols;
+  if (n > 0) {
+    if (!up) return FP4Q_ERR_INVALID_ARG;
+    if (!aligned(up, 16)) return FP4Q_ERR_UNSUPPORTED;
+  }
+  if (out->counters) {
+    hipError_t e = launch_zero_counters(reinterpret_cast<unsigned long long*>(out->counters), s);
+    if (e != hipSuccess) return FP4Q_ERR_HIP;
+  }
+  if (n == 0) return FP4Q_OK;
+  FwhtLaunch f;
+  memset(&f, 0, sizeof(f));
+  f.x = gate;
+  f.up = up;
+  f.rows = args->rows;
+  f.d = args->cols;
+  f.stride = args->in_row_stride;
+  f.in_dtype = args->in_dtype == FP4Q_F32 ? kF32 : kBF16;
+  f.t = (int)args->cols;
+  f.seed = args->seed;
+  f.y = out->rotated;
+  f.quantize = 1;
+  f.stochastic = args->rounding == FP4Q_ROUND_STOCHASTIC;
+  f.manual = args->scale_policy == FP4Q_SCALE_MANUAL;
+  f.manual_e = args->manual_exponent;
+  f.codes = out->codes;
+  f.scales = out->scales;
+  f.counters = reinterpret_cast<unsigned long long*>(out->counters);
+  return hip_status(launch_fwht(f, s));
+}
+
 fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args* args, const void* x, const float* global_amax,
                                 const fp4q_outputs* out, void* workspace, size_t workspace_bytes,
                                 void* hip_stream) {

@@ -19,12 +19,53 @@
 //  * fwht_lds_kernel: any power of two 32 <= t <= 16384, one 256-thread
 //    workgroup per t-chunk, all stages in LDS (also does the seeded signs).
 //  * fwht_small_kernel: t in {2, 4, 8, 16}, per lane / lane pair in registers.
+//
+// The fused SwiGLU epilogue ("Sub-4-Bit Microscaling", section 3: the online
+// rotation inside the SiLU_and_Mul kernel before down_proj) runs the first two
+// kernels on h = SiLU(gate) * up, formed in fp32 as the two inputs are loaded
+// (IN carries kSwiGlu); the activation never goes to memory.
 #include <math.h>
 
 #include "fp4q_flat.h"
 
 namespace fp4q {
 namespace {
+
+constexpr int kSwiGlu = 2;   // IN flag: the input is SiLU_and_Mul(x, up)
+
+// SiLU(g) * u = g / (1 + e^-g) * u in fp32 with the hardware exponential and
+// reciprocal (about an ulp each); e^-g = inf gives -0 for finite g.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ void load8_plain_f32(const void* base, int64_t off, float v[8]) {
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+  const uint4 a = p[0], b = p[1];
+  v[0] = as_f(a.x); v[1] = as_f(a.y); v[2] = as_f(a.z); v[3] = as_f(a.w);
+  v[4] = as_f(b.x); v[5] = as_f(b.y); v[6] = as_f(b.z); v[7] = as_f(b.w);
+}
+
+__device__ __forceinline__ void load8_plain_bf16(const void* base, int64_t off, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+  v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+}
+
+// 8 consecutive fp32 input values at element offset `off` (IN & 1: the
+// element type; IN & kSwiGlu: SiLU_and_Mul of f.x and f.up)
+template <int IN>
+__device__ __forceinline__ void load8(const FwhtLaunch& f, int64_t off, float v[8]) {
+  if constexpr ((IN & 1) == kF32) load8_plain_f32(f.x, off, v);
+  else load8_plain_bf16(f.x, off, v);
+  if constexpr ((IN & kSwiGlu) != 0) {
+    float u[8];
+    if constexpr ((IN & 1) == kF32) load8_plain_f32(f.up, off, u);
+    else load8_plain_bf16(f.up, off, u);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = silu_mul(v[m], u[m]);
+  }
+}
 
 // ---------------------------------------------------------------- d = 8192
 __device__ __forceinline__ int swz8192(int i) {
@@ -42,19 +83,7 @@ __global__ __launch_bounds__(128) void fwht8192_kernel(FwhtLaunch f, float c) {
     float v[8][8];
     // ---- load (layout L) and widen
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t off = row * f.stride + w * 4096 + j * 512 + l * 8;
-      if constexpr (IN == kF32) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(f.x) + off);
-        const uint4 a = p[0], b = p[1];
-        v[j][0] = as_f(a.x); v[j][1] = as_f(a.y); v[j][2] = as_f(a.z); v[j][3] = as_f(a.w);
-        v[j][4] = as_f(b.x); v[j][5] = as_f(b.y); v[j][6] = as_f(b.z); v[j][7] = as_f(b.w);
-      } else {
-        const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(f.x) + off);
-        v[j][0] = bf_lo(a.x); v[j][1] = bf_hi(a.x); v[j][2] = bf_lo(a.y); v[j][3] = bf_hi(a.y);
-        v[j][4] = bf_lo(a.z); v[j][5] = bf_hi(a.z); v[j][6] = bf_lo(a.w); v[j][7] = bf_hi(a.w);
-      }
-    }
+    for (int j = 0; j < 8; ++j) load8<IN>(f, row * f.stride + w * 4096 + j * 512 + l * 8, v[j]);
     // ---- stages on bits 0-2 (m) and 9-11 (j)
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
@@ -158,16 +187,7 @@ __global__ __launch_bounds__(kThreads) void fwht_lds_kernel(FwhtLaunch f, int lo
     for (int sl = tid; sl < (t >> 3); sl += kThreads) {
       const int64_t off = row * f.stride + c0 + sl * 8;
       float v[8];
-      if constexpr (IN == kF32) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(f.x) + off);
-        const uint4 a = p[0], b = p[1];
-        v[0] = as_f(a.x); v[1] = as_f(a.y); v[2] = as_f(a.z); v[3] = as_f(a.w);
-        v[4] = as_f(b.x); v[5] = as_f(b.y); v[6] = as_f(b.z); v[7] = as_f(b.w);
-      } else {
-        const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(f.x) + off);
-        v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
-        v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
-      }
+      load8<IN>(f, off, v);
       if (f.random_signs) {
         const uint32_t word = sgn[(sl * 8) >> 5] >> ((sl * 8) & 31);
 #pragma unroll
@@ -308,6 +328,11 @@ hipError_t launch_fwht(const FwhtLaunch& f, hipStream_t st) {
   const float c = (float)(1.0 / sqrt((double)f.t));
   int log2t = 0;
   while ((1 << log2t) < f.t) ++log2t;
+  if (f.up) {   // fused SiLU_and_Mul: full-row transforms with quantization only
+    if (f.t <= 16 || !f.quantize) return hipErrorInvalidValue;
+    return f.in_dtype == kF32 ? d_quant_opts<kF32 | kSwiGlu, true>(f, st, c, log2t)
+                              : d_quant_opts<kBF16 | kSwiGlu, true>(f, st, c, log2t);
+  }
   if (f.t <= 16) return f.in_dtype == kF32 ? launch_small<kF32>(f, st, c) : launch_small<kBF16>(f, st, c);
   if (f.quantize)
     return f.in_dtype == kF32 ? d_quant_opts<kF32, true>(f, st, c, log2t) : d_quant_opts<kBF16, true>(f, st, c, log2t);

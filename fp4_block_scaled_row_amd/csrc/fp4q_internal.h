@@ -49,7 +49,8 @@ hipError_t launch_nv_resident(const QuantLaunch& q, int grid, int nres, hipStrea
 // Row Walsh-Hadamard transform of rows of length d (fp32 out), optionally
 // fused with MXFP4 quantization of the rotated row.
 struct FwhtLaunch {
-  const void* x;
+  const void* x;             // input, or the gate of SiLU_and_Mul when `up` is set
+  const void* up;            // SiLU_and_Mul: the up input (same shape and stride as x) or null
   int64_t rows, d, stride;
   int in_dtype;
   int t;                     // transform size (power of two, divides d)

@@ -160,6 +160,21 @@ fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args *args, const void *x,
                                 const float *global_amax, const fp4q_outputs *out,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Fused SwiGLU epilogue ("Sub-4-Bit Microscaling", section 3: the online
+ * rotation inside the SiLU_and_Mul kernel right before down_proj): the
+ * activation h = SiLU(gate) * up, SiLU(g) = g / (1 + e^-g), is formed in fp32
+ * as gate and up are read (hardware exponential and reciprocal, within a few
+ * ulps), never stored, rotated by the normalised full-row FWHT and
+ * MXFP4-quantized as fp4q_quantize_mxfp4 does.  gate and up are
+ * [rows][in_row_stride] device arrays of in_dtype sharing the row stride
+ * (e.g. the two halves of a [rows][2 * cols] tensor).  block_size 32, policy
+ * OCP_MAX or MANUAL, rounding RNE or STOCHASTIC, rotation must be FWHT_ROW
+ * and cols a power of two between 32 and 16384 (else UNSUPPORTED).
+ * `rotated`, when given, receives the rotated fp32 values that were
+ * quantized; no workspace. */
+fp4q_status fp4q_silu_mul_fwht_mxfp4(const fp4q_quant_args *args, const void *gate, const void *up,
+                                     const fp4q_outputs *out, void *hip_stream);
+
 /* Normalised Walsh-Hadamard transform of each transform_size-chunk of each
  * row: y[r, c0:c0+t] = (x[r, c0:c0+t] * sigma) H_t * fl32(1/sqrt(t)), fp32
  * out ([rows][d], dense).  transform_size t: a power of two with 2 <= t <=

@@ -25,9 +25,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(fp4q_[a-z0-9_]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_fwht", "fp4q_dequantize"):
+    for n in ("fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_silu_mul_fwht_mxfp4", "fp4q_fwht",
+              "fp4q_dequantize"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -122,6 +123,27 @@ def test_nvfp4_needs_workspace_or_amax():
     a46 = _args(block=16, policy=_lib.FP4Q_SCALE_FOUR_OVER_SIX)
     o = _lib.Outputs(FAKE, FAKE, FAKE, None, None, None)
     assert lib.fp4q_quantize_nvfp4(a46, FAKE, None, o, FAKE, 1 << 20, None) == _lib.FP4Q_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(rotation=_lib.FP4Q_ROT_NONE), _lib.FP4Q_ERR_UNSUPPORTED),           # the fused op always rotates
+    (dict(rotation=_lib.FP4Q_ROT_RHT16), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(rotation=_lib.FP4Q_ROT_FWHT_ROW, cols=96), _lib.FP4Q_ERR_UNSUPPORTED),  # not a power of two
+    (dict(rotation=_lib.FP4Q_ROT_FWHT_ROW, cols=32768), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(rotation=_lib.FP4Q_ROT_FWHT_ROW, block=16), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(rotation=_lib.FP4Q_ROT_FWHT_ROW, policy=_lib.FP4Q_SCALE_NV_MAX6), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(rotation=_lib.FP4Q_ROT_FWHT_ROW, stride=32), _lib.FP4Q_ERR_INVALID_ARG),
+])
+def test_silu_mul_fwht_rejects(kwargs, status):
+    lib = _lib_or_skip()
+    assert lib.fp4q_silu_mul_fwht_mxfp4(_args(**kwargs), FAKE, FAKE, OUTS, None) == status
+
+
+def test_silu_mul_fwht_needs_up():
+    lib = _lib_or_skip()
+    a = _args(rotation=_lib.FP4Q_ROT_FWHT_ROW)
+    assert lib.fp4q_silu_mul_fwht_mxfp4(a, FAKE, None, OUTS, None) == _lib.FP4Q_ERR_INVALID_ARG
+    assert lib.fp4q_silu_mul_fwht_mxfp4(a, FAKE, FAKE + 8, OUTS, None) == _lib.FP4Q_ERR_UNSUPPORTED
 
 
 def test_fwht_and_dequant_reject():

@@ -713,3 +713,40 @@ def test_if4_round_trip_8192():
     d = host(fq.dequantize("if4", r.codes, r.scales, r.global_scale, out_dtype=torch.bfloat16))
     want = oracle.dequantize(oracle.IF4, codes[rows], scales[rows], g, out_dtype=oracle.BF16)
     assert_same(d[rows], want, "bf16 reconstruction")
+
+
+# ------------------------------------------------------------------ fused SwiGLU epilogue
+@pytest.mark.parametrize("rows,d", [(3, 32), (5, 64), (17, 512), (4, 4096), (6, 8192), (2, 16384)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rounding", ["rne", "stochastic"])
+def test_silu_mul_fwht_small(rows, d, dtype, rounding):
+    x = make_input(rows, 2 * d, dtype, rows * 13 + d)            # [gate | up] per row
+    xd = to_dev(x)
+    r = fq.silu_mul_fwht_mxfp4(xd[:, :d], xd[:, d:], rounding=rounding, seed=55, return_rotated=True,
+                               counters=True)
+    rot = host(r.rotated)
+    ref = oracle.fwht(oracle.silu_mul(np.ascontiguousarray(x[:, :d]), np.ascontiguousarray(x[:, d:])))
+    assert rel_l2(rot, ref) <= RTOL_ROT
+    c, s, cnt = oracle.quantize_mx(rot, rounding=int(rounding != "rne"), seed=55)
+    assert_same(host(r.codes), c, "codes of the rotated activation")
+    assert_same(host(r.scales), s, "scales of the rotated activation")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    r2 = fq.silu_mul_fwht_mxfp4(xd[:, :d], xd[:, d:], rounding=rounding, seed=55)
+    assert_same(host(r2.codes), c, "codes without the rotated hook")
+
+
+def test_silu_mul_fwht_16384x8192():
+    x = workload("gate_up_bf16_16384x8192")
+    d = x.shape[1] // 2
+    xd = to_dev(x)
+    r = fq.silu_mul_fwht_mxfp4(xd[:, :d], xd[:, d:], return_rotated=True, counters=True)
+    rot = host(r.rotated)
+    c, s, cnt = oracle.quantize_mx(rot)
+    assert_same(host(r.codes), c, "codes of the rotated activation")
+    assert_same(host(r.scales), s, "scales of the rotated activation")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    rows = np.random.default_rng(1).choice(x.shape[0], 32, replace=False)
+    ref = oracle.fwht(oracle.silu_mul(np.ascontiguousarray(x[rows, :d]), np.ascontiguousarray(x[rows, d:])))
+    assert rel_l2(rot[rows], ref) <= RTOL_ROT
+    r2 = fq.silu_mul_fwht_mxfp4(xd[:, :d], xd[:, d:])
+    assert_same(host(r2.codes), c, "codes without the rotated hook")
