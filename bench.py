@@ -157,6 +157,22 @@ def profile_kernels(dev, reps=5):
         n4 * 2 + n4 // 2 + n4 // 16 + 4)
     del oi, yi
 
+    xg = dev_tensor("gate_up_bf16_16384x8192")
+    d = xg.shape[1] // 2
+    gate, up = xg[:, :d], xg[:, d:]
+    og = fq.silu_mul_fwht_mxfp4(gate, up)
+    ng = gate.numel()
+    run("SiLU_and_Mul + FWHT-8192 + MXFP4 bf16 16384x(2x8192), fused",
+        lambda: fq.silu_mul_fwht_mxfp4(gate, up, out=og), 2 * ng * 2 + ng // 2 + ng // 32)
+    hb = torch.empty_like(gate)
+
+    def unfused():
+        torch.mul(torch.nn.functional.silu(gate), up, out=hb)
+        fq.quantize_mxfp4(hb, rotation="fwht_row", out=og)
+    run("  unfused reference: torch SiLU*up to bf16, then FWHT-8192 + MXFP4", unfused,
+        2 * ng * 2 + ng // 2 + ng // 32)
+    del xg, gate, up, og, hb
+
     x1 = dev_tensor("mx_f32_1024")
     o1 = fq.quantize_mxfp4(x1, counters=True)
     y1 = torch.empty_like(x1)
