@@ -33,7 +33,7 @@ NvResult = namedtuple("NvResult", "codes scales global_scale choice_bits rotated
 
 _ROUND = {"rne": _lib.FP4Q_ROUND_RNE, "stochastic": _lib.FP4Q_ROUND_STOCHASTIC, "sr": _lib.FP4Q_ROUND_STOCHASTIC}
 _ROT = {None: _lib.FP4Q_ROT_NONE, "none": _lib.FP4Q_ROT_NONE, "fwht_row": _lib.FP4Q_ROT_FWHT_ROW,
-        "rht16": _lib.FP4Q_ROT_RHT16}
+        "rht16": _lib.FP4Q_ROT_RHT16, "fwht128": _lib.FP4Q_ROT_FWHT128}
 
 
 def _ptr(t):

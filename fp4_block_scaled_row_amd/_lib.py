@@ -16,7 +16,7 @@ FP4Q_F32, FP4Q_BF16 = 0, 1
 FP4Q_MXFP4, FP4Q_NVFP4, FP4Q_IF4 = 0, 1, 2
 FP4Q_SCALE_OCP_MAX, FP4Q_SCALE_MANUAL, FP4Q_SCALE_NV_MAX6, FP4Q_SCALE_FOUR_OVER_SIX, FP4Q_SCALE_IF4 = 0, 1, 2, 3, 4
 FP4Q_ROUND_RNE, FP4Q_ROUND_STOCHASTIC = 0, 1
-FP4Q_ROT_NONE, FP4Q_ROT_FWHT_ROW, FP4Q_ROT_RHT16 = 0, 1, 2
+FP4Q_ROT_NONE, FP4Q_ROT_FWHT_ROW, FP4Q_ROT_RHT16, FP4Q_ROT_FWHT128 = 0, 1, 2, 3
 
 EXPORTED = [
     "fp4q_workspace_bytes", "fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_silu_mul_fwht_mxfp4", "fp4q_fwht",

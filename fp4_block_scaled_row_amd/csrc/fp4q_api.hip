@@ -41,7 +41,7 @@ fp4q_status check_quant(const fp4q_quant_args* a, const void* x, const fp4q_outp
   if (a->rows < 0 || a->cols < 0 || a->in_row_stride < a->cols) return FP4Q_ERR_INVALID_ARG;
   if (a->in_dtype != FP4Q_F32 && a->in_dtype != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
   if (a->rounding != FP4Q_ROUND_RNE && a->rounding != FP4Q_ROUND_STOCHASTIC) return FP4Q_ERR_INVALID_ARG;
-  if (a->rotation < FP4Q_ROT_NONE || a->rotation > FP4Q_ROT_RHT16) return FP4Q_ERR_INVALID_ARG;
+  if (a->rotation < FP4Q_ROT_NONE || a->rotation > FP4Q_ROT_FWHT128) return FP4Q_ERR_INVALID_ARG;
   if (a->scale_policy < FP4Q_SCALE_OCP_MAX || a->scale_policy > FP4Q_SCALE_IF4) return FP4Q_ERR_INVALID_ARG;
   const int want_block = format == FP4Q_MXFP4 ? 32 : 16;
   if (a->block_size != want_block) return FP4Q_ERR_UNSUPPORTED;
@@ -77,7 +77,8 @@ QuantLaunch make_launch(const fp4q_quant_args* a, const void* x, const fp4q_outp
   q.stride = a->in_row_stride;
   q.nslots = a->rows * a->cols / 8;
   q.in_dtype = a->in_dtype == FP4Q_F32 ? kF32 : kBF16;
-  q.rotation = a->rotation == FP4Q_ROT_RHT16 ? kRotRht16 : kRotNone;
+  q.rotation = a->rotation == FP4Q_ROT_RHT16 ? kRotRht16 : (a->rotation == FP4Q_ROT_FWHT128 ? kRotFwht128 : kRotNone);
+  q.rot_scale = (float)(1.0 / sqrt(128.0));
   q.stochastic = a->rounding == FP4Q_ROUND_STOCHASTIC;
   q.manual = a->scale_policy == FP4Q_SCALE_MANUAL;
   q.manual_e = a->manual_exponent;
@@ -110,6 +111,7 @@ fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args* args, const void* x, cons
   (void)workspace_bytes;
   fp4q_status st = check_quant(args, x, out, FP4Q_MXFP4);
   if (st != FP4Q_OK) return st;
+  if (args->rotation == FP4Q_ROT_FWHT128) return FP4Q_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const int64_t n = args->rows * args->cols;
   if (args->rotation == FP4Q_ROT_FWHT_ROW) {
@@ -191,6 +193,9 @@ fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args* args, const void* x, cons
   fp4q_status st = check_quant(args, x, out, FP4Q_NVFP4);
   if (st != FP4Q_OK) return st;
   if (args->rotation == FP4Q_ROT_FWHT_ROW) return FP4Q_ERR_UNSUPPORTED;
+  if (args->rotation == FP4Q_ROT_FWHT128 &&
+      (args->cols % 128 != 0 || args->rounding != FP4Q_ROUND_RNE || args->scale_policy == FP4Q_SCALE_FOUR_OVER_SIX))
+    return FP4Q_ERR_UNSUPPORTED;
   if (!out->global_scale) return FP4Q_ERR_INVALID_ARG;
   const int64_t n = args->rows * args->cols;
   if (args->scale_policy == FP4Q_SCALE_FOUR_OVER_SIX && n > 0 && !out->choice_bits) return FP4Q_ERR_INVALID_ARG;

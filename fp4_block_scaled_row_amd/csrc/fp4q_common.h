@@ -19,7 +19,7 @@ constexpr int kThreads = 256;   // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
 
 enum InType { kF32 = 0, kBF16 = 1 };
-enum Rot { kRotNone = 0, kRotFwhtRow = 1, kRotRht16 = 2 };
+enum Rot { kRotNone = 0, kRotFwhtRow = 1, kRotRht16 = 2, kRotFwht128 = 3 };
 
 // ----------------------------------------------------------------------------
 // bit casts and widening

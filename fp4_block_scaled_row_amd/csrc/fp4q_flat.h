@@ -93,6 +93,48 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool od
   }
 }
 
+// Partner value across lane bit 2 (xor 4) or bit 3 (xor 8) within a row of
+// 16 lanes: the upper half of each 2N-lane group reads lane - N (row_shr:N,
+// written to its banks only), the lower half lane + N (row_shl:N).
+template <int N>
+__device__ __forceinline__ float dpp_xor_hi_f(float v) {
+  constexpr int kShr = 0x110 + N, kShl = 0x100 + N;
+  constexpr int kUpper = N == 4 ? 0xA : 0xC, kLower = N == 4 ? 0x5 : 0x3;   // bank masks
+  const int up = __builtin_amdgcn_update_dpp(0, (int)as_u(v), kShr, 0xF, kUpper, false);
+  return as_f((uint32_t)__builtin_amdgcn_update_dpp(up, (int)as_u(v), kShl, 0xF, kLower, false));
+}
+
+// Normalised FWHT of each 128-element chunk held by 16 consecutive lanes, 8
+// consecutive elements each: the three butterfly stages of the element bits
+// run in registers, the four of the lane bits across lanes (quad
+// permutations for bits 0 and 1, bank-masked row shifts for bits 2 and 3);
+// the upper member of a pair keeps a - b.  Scaled once by c = fl32(1/sqrt(128)).
+__device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0, b2 = (lane & 4) != 0, b3 = (lane & 8) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float p = dpp_xor1_f(v[i]);
+    v[i] = b0 ? (p - v[i]) : (v[i] + p);
+    p = dpp_xor2_f(v[i]);
+    v[i] = b1 ? (p - v[i]) : (v[i] + p);
+    p = dpp_xor_hi_f<4>(v[i]);
+    v[i] = b2 ? (p - v[i]) : (v[i] + p);
+    p = dpp_xor_hi_f<8>(v[i]);
+    v[i] = b3 ? (p - v[i]) : (v[i] + p);
+    v[i] *= c;
+  }
+}
+
 __device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float v[8]) {
   float4* p = reinterpret_cast<float4*>(rot + (s << 3));
   p[0] = make_float4(v[0], v[1], v[2], v[3]);

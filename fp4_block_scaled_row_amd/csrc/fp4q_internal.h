@@ -21,6 +21,7 @@ struct QuantLaunch {
   int if4;                   // NV: per block FP4 or scaled INT4
   uint64_t seed;
   uint32_t rht_signs;        // 16-bit sign mask of the RHT diagonal
+  float rot_scale;           // FWHT-128: fl32(1 / sqrt(128))
   uint8_t* codes;
   uint8_t* scales;
   float* global_scale;

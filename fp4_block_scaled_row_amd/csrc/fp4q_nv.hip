@@ -39,6 +39,7 @@ template <int IN, int ROT, bool CONTIG>
 __device__ __forceinline__ void load_values(const QuantLaunch& q, const SlotRaw<IN>& r, int lane, float v[8]) {
   widen_slot<IN>(r, v);
   if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
+  if constexpr (ROT == kRotFwht128) fwht128_lanes(v, lane, q.rot_scale);
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -302,9 +303,13 @@ hipError_t d_count(const QuantLaunch& q, hipStream_t st) {
 }
 template <int IN, int ROT, bool SR>
 hipError_t d_fos(const QuantLaunch& q, hipStream_t st) {
-  if (q.four_over_six) return d_count<IN, ROT, SR, kPolFos>(q, st);
+  // (combinations the entry point rejects are not instantiated)
+  if (q.four_over_six) {
+    if constexpr (ROT == kRotFwht128) return hipErrorInvalidValue;
+    else return d_count<IN, ROT, SR, kPolFos>(q, st);
+  }
   if (q.if4) {
-    if constexpr (SR) return hipErrorInvalidValue;   // rejected by the entry point
+    if constexpr (SR) return hipErrorInvalidValue;
     else return d_count<IN, ROT, SR, kPolIf4>(q, st);
   }
   return d_count<IN, ROT, SR, kPolMax6>(q, st);
@@ -315,6 +320,10 @@ hipError_t d_sr(const QuantLaunch& q, hipStream_t st) {
 }
 template <int IN>
 hipError_t d_rot(const QuantLaunch& q, hipStream_t st) {
+  if (q.rotation == kRotFwht128) {
+    if (q.stochastic) return hipErrorInvalidValue;
+    return d_fos<IN, kRotFwht128, false>(q, st);
+  }
   return q.rotation == kRotRht16 ? d_sr<IN, kRotRht16>(q, st) : d_sr<IN, kRotNone>(q, st);
 }
 

@@ -91,7 +91,8 @@ enum { FP4Q_ROUND_RNE = 0, FP4Q_ROUND_STOCHASTIC = 1 };
 enum {
   FP4Q_ROT_NONE = 0,
   FP4Q_ROT_FWHT_ROW = 1,         /* full-row normalised FWHT, cols a power of two (MXFP4 only)  */
-  FP4Q_ROT_RHT16 = 2             /* seeded +-1 diagonal then 16-point normalised FWHT per block */
+  FP4Q_ROT_RHT16 = 2,            /* seeded +-1 diagonal then 16-point normalised FWHT per block */
+  FP4Q_ROT_FWHT128 = 3           /* NVFP4 only: normalised FWHT of every 128-element head chunk  */
 };
 
 typedef struct {
@@ -142,8 +143,12 @@ fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args *args, const void *x,
 
 /* NVFP4 quantization ("Sub-4-Bit Microscaling", section 2; Four Over Six,
  * transcript cue 10; IF4, transcript cues 14 and 17).  block_size 16, policy
- * NV_MAX6, FOUR_OVER_SIX or IF4, rotation NONE or RHT16, rounding RNE or
- * STOCHASTIC (IF4: RNE only, STOCHASTIC is UNSUPPORTED).  IF4 writes no
+ * NV_MAX6, FOUR_OVER_SIX or IF4, rotation NONE, RHT16 or FWHT128, rounding
+ * RNE or STOCHASTIC (IF4: RNE only, STOCHASTIC is UNSUPPORTED).  FWHT128 is
+ * the per-head rotation of a KV cache ("Sub-4-Bit Microscaling", section 3,
+ * the online post-RoPE Q/K rotation): the normalised FWHT of each 128-element
+ * chunk of a row (head dimension 128, no signs), then NVFP4 of the rotated
+ * values; cols must be a multiple of 128, RNE only, policy NV_MAX6 or IF4.  IF4 writes no
  * choice bits (choice_bits may be NULL): an INT4 block has bit 7 of its
  * scale byte set; counters count the kept candidate (INT4 saturates at
  * |7x / (6 s g)| > 7).  The tensor amax is

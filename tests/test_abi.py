@@ -92,6 +92,7 @@ OUTS = _lib.Outputs(FAKE, FAKE, FAKE, FAKE, None, None)
     (dict(policy=_lib.FP4Q_SCALE_MANUAL, manual=128), _lib.FP4Q_ERR_INVALID_ARG),
     (dict(rotation=_lib.FP4Q_ROT_FWHT_ROW, cols=96), _lib.FP4Q_ERR_UNSUPPORTED),  # not a power of two
     (dict(stride=68), _lib.FP4Q_ERR_UNSUPPORTED),                              # unaligned row pitch
+    (dict(rotation=_lib.FP4Q_ROT_FWHT128, cols=128), _lib.FP4Q_ERR_UNSUPPORTED),  # per-head rotation is NV only
 ])
 def test_mxfp4_rejects(kwargs, status):
     lib = _lib_or_skip()
@@ -107,6 +108,12 @@ def test_mxfp4_rejects(kwargs, status):
     (dict(block=16, policy=_lib.FP4Q_SCALE_IF4, rotation=_lib.FP4Q_ROT_FWHT_ROW), _lib.FP4Q_ERR_UNSUPPORTED),
     (dict(block=32, policy=_lib.FP4Q_SCALE_IF4), _lib.FP4Q_ERR_UNSUPPORTED),       # IF4 needs 16-blocks
     (dict(block=16, policy=5), _lib.FP4Q_ERR_INVALID_ARG),
+    (dict(block=16, policy=_lib.FP4Q_SCALE_NV_MAX6, rotation=_lib.FP4Q_ROT_FWHT128, cols=64), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(block=16, policy=_lib.FP4Q_SCALE_NV_MAX6, rotation=_lib.FP4Q_ROT_FWHT128, cols=128,
+          rounding=_lib.FP4Q_ROUND_STOCHASTIC), _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(block=16, policy=_lib.FP4Q_SCALE_FOUR_OVER_SIX, rotation=_lib.FP4Q_ROT_FWHT128, cols=128),
+     _lib.FP4Q_ERR_UNSUPPORTED),
+    (dict(block=16, policy=_lib.FP4Q_SCALE_NV_MAX6, rotation=4), _lib.FP4Q_ERR_INVALID_ARG),
 ])
 def test_nvfp4_rejects(kwargs, status):
     lib = _lib_or_skip()

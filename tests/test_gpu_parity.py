@@ -750,3 +750,40 @@ def test_silu_mul_fwht_16384x8192():
     assert rel_l2(rot[rows], ref) <= RTOL_ROT
     r2 = fq.silu_mul_fwht_mxfp4(xd[:, :d], xd[:, d:])
     assert_same(host(r2.codes), c, "codes without the rotated hook")
+
+
+# ------------------------------------------------------------------ per-head FWHT-128 + NVFP4
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 256), (17, 384), (64, 1024), (5, 4096)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("policy", ["max6", "if4"])
+def test_fwht128_nv_small(rows, cols, dtype, policy):
+    pad = 16 if rows % 2 else 0
+    full = make_input(rows, cols, dtype, rows * 17 + cols, pad=pad)
+    xd = to_dev(full)[:, :cols]
+    ref = oracle.fwht(np.ascontiguousarray(full[:, :cols]), t=128)
+    for counters in (False, True):
+        r = fq.quantize_nvfp4(xd, policy=policy, rotation="fwht128", counters=counters, return_rotated=True)
+        rot = host(r.rotated)
+        assert rel_l2(rot, ref) <= RTOL_ROT
+        c, s, g, _, cnt = oracle.quantize_nv(rot, policy=2 if policy == "max6" else 4)
+        assert host(r.global_scale)[0] == g
+        assert_same(host(r.scales), s, "scales")
+        assert_same(host(r.codes), c, "codes")
+        if counters:
+            assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    r2 = fq.quantize_nvfp4(xd, policy=policy, rotation="fwht128")
+    assert_same(host(r2.codes), c, "codes without the rotated hook")
+
+
+def test_fwht128_nv_act_8192_heads():
+    """The 8192x8192 activation read as 8192 tokens x 64 heads of 128."""
+    x = workload("act_bf16_8192")
+    r = fq.quantize_nvfp4(to_dev(x), rotation="fwht128", return_rotated=True, counters=True)
+    rot = host(r.rotated)
+    c, s, g, _, cnt = oracle.quantize_nv(rot)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    rows = np.random.default_rng(2).choice(x.shape[0], 64, replace=False)
+    assert rel_l2(rot[rows], oracle.fwht(x[rows], t=128)) <= RTOL_ROT
