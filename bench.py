@@ -127,6 +127,10 @@ def profile_kernels(dev, reps=5):
     y = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=dev)
     run("C2 dequantize NVFP4 -> bf16 8192x8192",
         lambda: fq.dequantize("nvfp4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=y), DQ_BYTES)
+    o6 = fq.quantize_nvfp4(x, rotation="fwht128", workspace=ws)
+    run("FWHT-128 per head + NVFP4 bf16 8192x8192 (64 heads of 128)",
+        lambda: fq.quantize_nvfp4(x, rotation="fwht128", out=o6, workspace=ws), NV_BYTES)
+    del o6
     o5 = fq.quantize_nvfp4(x, rotation="rht16", rounding="stochastic", seed=workloads.SR_SEED, workspace=ws)
     run("C5 RHT16 + stochastic NVFP4 bf16 8192x8192",
         lambda: fq.quantize_nvfp4(x, rotation="rht16", rounding="stochastic", seed=workloads.SR_SEED, out=o5,
