@@ -8,5 +8,5 @@ code.  See the header of ``fp4_oracle.c`` for the pages each function follows.
 from .oracle import (  # noqa: F401
     build, load, e2m1_value, e8m0_value, e4m3_value, e4m3_encode, e2m1_round,
     int4_round, mx_exponent, philox4x32_10, sr_draw, rht_sign_negative, quantize_mx,
-    quantize_nv, tensor_amax, fwht, silu_mul, dequantize, MX, NV, IF4, F32, BF16,
+    quantize_nv, tensor_amax, fwht, silu_mul, mx_gemm, dequantize, MX, NV, IF4, F32, BF16,
 )

@@ -566,6 +566,56 @@ int oracle_fwht(int64_t rows, int64_t d, int64_t stride, int dtype, const void *
 }
 
 /* ------------------------------------------------------------------ */
+/* MXFP4 GEMM                                                          */
+/* ------------------------------------------------------------------ */
+/* The consumer of two MXFP4 tensors ([SUB4] section 3: Y = X W^T with both
+ * operands quantized): C[m][n] = sum_k A[m][k] B[n][k] over the
+ * reconstructed values (value * 2^(b - 127), [MXA] "Encode one MXFP4 block
+ * step by step"), A [M][K] and B [N][K] in the quantizer's layout (codes
+ * [rows][K/2], scales [rows][K/32]).  Every product is exact in fp64 and the
+ * sum is taken in fp64 in k order (reading R-27); absc[m][n] = sum_k
+ * |A[m][k] B[n][k]| bounds the rounding of any other summation order.  A NaN
+ * scale code (255) makes its terms NaN.  rows0/nrows select the rows of A
+ * (and of C) to compute. */
+int oracle_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes, const uint8_t *a_scales,
+                   const uint8_t *b_codes, const uint8_t *b_scales, int64_t row0, int64_t nrows,
+                   double *c, double *absc)
+{
+    int64_t m, n, k;
+    double *arow, *brow;
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || row0 < 0 || nrows < 0 || row0 + nrows > M) return OR_BAD;
+    arow = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    brow = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    if (!arow || !brow) {
+        free(arow);
+        free(brow);
+        return OR_BAD;
+    }
+    for (m = row0; m < row0 + nrows; m++) {
+        for (k = 0; k < K; k++) {
+            int code = (a_codes[m * (K / 2) + k / 2] >> (4 * (k & 1))) & 15;
+            int sb = a_scales[m * (K / 32) + k / 32];
+            arow[k] = sb == 255 ? NAN : oracle_e2m1_value(code) * oracle_e8m0_value(sb);
+        }
+        for (n = 0; n < N; n++) {
+            double s = 0.0, sa = 0.0;
+            for (k = 0; k < K; k++) {
+                int code = (b_codes[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 15;
+                int sb = b_scales[n * (K / 32) + k / 32];
+                brow[k] = sb == 255 ? NAN : oracle_e2m1_value(code) * oracle_e8m0_value(sb);
+                s += arow[k] * brow[k];
+                sa += fabs(arow[k] * brow[k]);
+            }
+            c[(m - row0) * N + n] = s;
+            if (absc) absc[(m - row0) * N + n] = sa;
+        }
+    }
+    free(arow);
+    free(brow);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* SiLU_and_Mul                                                        */
 /* ------------------------------------------------------------------ */
 /* [SUB4] section 3, the online rotation fused into the SwiGLU epilogue

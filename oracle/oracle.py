@@ -58,6 +58,8 @@ def load():
             lib.oracle_quantize_nv.restype = i32
             lib.oracle_fwht.argtypes = [i64, i64, i64, i32, vp, vp, i64, i32, u64]
             lib.oracle_silu_mul.argtypes = [i64, i64, i64, i32, vp, vp, vp]
+            lib.oracle_mx_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, i64, i64, vp, vp]
+            lib.oracle_mx_gemm.restype = i32
             lib.oracle_silu_mul.restype = i32
             lib.oracle_fwht.restype = i32
             lib.oracle_dequantize.argtypes = [i32, i64, i64, i32, vp, vp, vp, i32, vp]
@@ -185,6 +187,27 @@ def fwht(x, t=None, random_signs=False, seed=0):
     if rc != 0:
         raise ValueError("oracle_fwht rejected the arguments")
     return y
+
+
+def mx_gemm(a_codes, a_scales, b_codes, b_scales, rows=None):
+    """C = A B^T over reconstructed MXFP4 values (fp64), with sum |a b| per output.
+    A: codes [M, K/2], scales [M, K/32]; B likewise [N, ...].  rows: optional
+    (row0, nrows) of A to compute.  Returns (C, absC), both [nrows, N] fp64."""
+    ac = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    asc = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    bc = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    bsc = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    M, K = ac.shape[0], ac.shape[1] * 2
+    N = bc.shape[0]
+    if bc.shape[1] * 2 != K or asc.shape != (M, K // 32) or bsc.shape != (N, K // 32):
+        raise ValueError("mx_gemm: inconsistent shapes")
+    row0, nrows = (0, M) if rows is None else rows
+    c = np.zeros((nrows, N), np.float64)
+    absc = np.zeros((nrows, N), np.float64)
+    rc = load().oracle_mx_gemm(M, N, K, _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), row0, nrows, _ptr(c), _ptr(absc))
+    if rc != 0:
+        raise ValueError("oracle_mx_gemm rejected the arguments")
+    return c, absc
 
 
 def silu_mul(gate, up):

@@ -486,6 +486,42 @@ def test_fwht_of_fp64_input_matches_dense_hadamard():
     assert np.allclose(oracle.fwht(x), x @ hadamard(256) / 16.0, rtol=1e-13, atol=1e-13)
 
 
+# ---------------------------------------------------------------- MXFP4 GEMM
+def test_mx_gemm_matches_dequantized_matmul():
+    rng = np.random.default_rng(51)
+    a = rng.standard_t(4, (7, 96)).astype(np.float32)
+    b = (rng.standard_normal((5, 96)) * 0.02).astype(np.float32)
+    ac, asc, _ = oracle.quantize_mx(a)
+    bc, bsc, _ = oracle.quantize_mx(b)
+    ad = oracle.dequantize(oracle.MX, ac, asc, out_dtype=oracle.F32).astype(np.float64)
+    bd = oracle.dequantize(oracle.MX, bc, bsc, out_dtype=oracle.F32).astype(np.float64)
+    c, absc = oracle.mx_gemm(ac, asc, bc, bsc)
+    ref = ad @ bd.T                                   # library matmul on the exact reconstructions
+    assert np.allclose(c, ref, rtol=1e-13, atol=1e-300)
+    assert np.allclose(absc, np.abs(ad) @ np.abs(bd).T, rtol=1e-13, atol=1e-300)
+    c2, _ = oracle.mx_gemm(ac, asc, bc, bsc, rows=(3, 2))
+    assert np.array_equal(c2, c[3:5])
+
+
+def test_mx_gemm_closed_forms():
+    K = 64
+    ones = np.full((2, K // 2), 0x22, np.uint8)            # every element code 2 = 1.0
+    s127 = np.full((2, K // 32), 127, np.uint8)
+    rng = np.random.default_rng(52)
+    bc = rng.integers(0, 256, (3, K // 2), dtype=np.uint8)
+    bs = np.array([[127, 129], [126, 127], [130, 120]], np.uint8)
+    c, _ = oracle.mx_gemm(ones, s127, bc, bs)
+    vals = np.array([oracle.e2m1_value(i) for i in range(16)])
+    bcodes = codes_of(bc)
+    for n in range(3):
+        want = sum(vals[bcodes[n, k]] * 2.0 ** (int(bs[n, k // 32]) - 127) for k in range(K))
+        assert c[0, n] == want and c[1, n] == want       # row sums of B
+    nan_scales = s127.copy()
+    nan_scales[0, 1] = 255
+    c, _ = oracle.mx_gemm(ones, nan_scales, bc, bs)
+    assert np.isnan(c[0]).all() and not np.isnan(c[1]).any()
+
+
 # ---------------------------------------------------------------- FWHT / RHT
 def test_fwht_matches_dense_hadamard():
     from scipy.linalg import hadamard
