@@ -24,7 +24,8 @@ from . import _lib
 from ._lib import Fp4qError, load  # noqa: F401
 
 __all__ = [
-    "quantize_mxfp4", "quantize_nvfp4", "silu_mul_fwht_mxfp4", "fwht", "dequantize", "workspace_bytes",
+    "quantize_mxfp4", "quantize_nvfp4", "silu_mul_fwht_mxfp4", "fwht", "dequantize", "mxfp4_gemm",
+    "workspace_bytes",
     "check_counters", "version", "MxResult", "NvResult", "Fp4qError",
 ]
 
@@ -190,6 +191,26 @@ def dequantize(fmt, codes, scales, global_scale=None, out_dtype=torch.float32, o
                                            _ptr(scales), _ptr(global_scale), od, _ptr(y), _stream()),
                "fp4q_dequantize")
     return y
+
+
+def mxfp4_gemm(a, b, out_dtype=torch.float32, out=None):
+    """C = A B^T for two MxResult-like operands (codes [rows, K/2], scales
+    [rows, K/32]): A [M, K] and B [N, K] (e.g. activations and a weight
+    quantized by quantize_mxfp4).  K must be a multiple of 128."""
+    ac, asc = a[0], a[1]
+    bc, bsc = b[0], b[1]
+    M, K = ac.shape[0], ac.shape[1] * 2
+    N = bc.shape[0]
+    if bc.shape[1] * 2 != K or asc.shape != (M, K // 32) or bsc.shape != (N, K // 32):
+        raise ValueError("fp4q: inconsistent GEMM operand shapes")
+    for t in (ac, asc, bc, bsc):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("fp4q: GEMM operands must be contiguous uint8 GPU tensors")
+    od = {torch.float32: _lib.FP4Q_F32, torch.bfloat16: _lib.FP4Q_BF16}[out_dtype]
+    c = torch.empty((M, N), dtype=out_dtype, device=ac.device) if out is None else out
+    _lib.check(_lib.load().fp4q_mxfp4_gemm(M, N, K, _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), od, _ptr(c),
+                                           _stream()), "fp4q_mxfp4_gemm")
+    return c
 
 
 def check_counters(counters):

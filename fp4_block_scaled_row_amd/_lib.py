@@ -20,7 +20,7 @@ FP4Q_ROT_NONE, FP4Q_ROT_FWHT_ROW, FP4Q_ROT_RHT16, FP4Q_ROT_FWHT128 = 0, 1, 2, 3
 
 EXPORTED = [
     "fp4q_workspace_bytes", "fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_silu_mul_fwht_mxfp4", "fp4q_fwht",
-    "fp4q_dequantize", "fp4q_check_counters", "fp4q_status_string", "fp4q_version",
+    "fp4q_dequantize", "fp4q_mxfp4_gemm", "fp4q_check_counters", "fp4q_status_string", "fp4q_version",
 ]
 
 
@@ -73,6 +73,8 @@ def load():
         lib.fp4q_fwht.restype = C.c_int
         lib.fp4q_dequantize.argtypes = [i32, i64, i64, i32, vp, vp, vp, i32, vp, vp]
         lib.fp4q_dequantize.restype = C.c_int
+        lib.fp4q_mxfp4_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp, vp]
+        lib.fp4q_mxfp4_gemm.restype = C.c_int
         lib.fp4q_check_counters.argtypes = [vp]
         lib.fp4q_check_counters.restype = C.c_int
         lib.fp4q_status_string.argtypes = [C.c_int]

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libfp4q.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["fp4q_api.hip", "fp4q_mx.hip", "fp4q_nv.hip", "fp4q_nv_resident.hip", "fp4q_fwht.hip",
+SOURCES = ["fp4q_api.hip", "fp4q_mx.hip", "fp4q_nv.hip", "fp4q_nv_resident.hip", "fp4q_fwht.hip", "fp4q_gemm.hip",
            "fp4q_dequant.hip"]
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",

@@ -257,6 +257,31 @@ fp4q_status fp4q_dequantize(int32_t format, int64_t rows, int64_t cols, int32_t 
   return hip_status(launch_dequant(dl, static_cast<hipStream_t>(hip_stream)));
 }
 
+fp4q_status fp4q_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int32_t out_dtype, void* c,
+                            void* hip_stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return FP4Q_ERR_INVALID_ARG;
+  if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP4Q_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FP4Q_OK;
+  if (!c || (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales))) return FP4Q_ERR_INVALID_ARG;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return FP4Q_ERR_UNSUPPORTED;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
+      !aligned(c, 4))
+    return FP4Q_ERR_UNSUPPORTED;
+  GemmLaunch g;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.b_codes = b_codes;
+  g.b_scales = b_scales;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.c = c;
+  g.out_bf16 = out_dtype == FP4Q_BF16;
+  return hip_status(launch_mx_gemm(g, static_cast<hipStream_t>(hip_stream)));
+}
+
 fp4q_status fp4q_check_counters(const uint64_t* host_counters) {
   if (!host_counters) return FP4Q_ERR_INVALID_ARG;
   return host_counters[2] != 0 ? FP4Q_ERR_NONFINITE : FP4Q_OK;

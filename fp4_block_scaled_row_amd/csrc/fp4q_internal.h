@@ -80,6 +80,18 @@ struct DequantLaunch {
 };
 hipError_t launch_dequant(const DequantLaunch& d, hipStream_t s);
 
+// MXFP4 x MXFP4 GEMM: C[M][N] = A[M][K] B[N][K]^T (K a multiple of 128).
+struct GemmLaunch {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int64_t M, N, K;
+  void* c;
+  int out_bf16;
+};
+hipError_t launch_mx_gemm(const GemmLaunch& g, hipStream_t s);
+
 int device_cu_count();
 
 }  // namespace fp4q

@@ -202,6 +202,21 @@ fp4q_status fp4q_dequantize(int32_t format, int64_t rows, int64_t cols, int32_t 
                             const float *global_scale, int32_t out_dtype, void *out,
                             void *hip_stream);
 
+/* MXFP4 GEMM, the consumer of two quantized operands ("Sub-4-Bit
+ * Microscaling", section 3: Y = X W^T with X and W both 4-bit block-scaled;
+ * section 2: block scales applied inside the matrix instruction):
+ * C[m][n] = sum_k A[m][k] B[n][k] over the reconstructed values of A
+ * ([M][K]: a_codes [M][K/2], a_scales [M][K/32]) and B ([N][K]: b_codes,
+ * b_scales), exactly the planes fp4q_quantize_mxfp4 writes (B is the
+ * [N][K] weight, so C = A B^T).  Products are exact; the sum is fp32 in the
+ * matrix instructions' order.  C is dense [M][N] fp32 or bf16 (out_dtype,
+ * rounded to nearest-even).  K must be a multiple of 128 (else UNSUPPORTED;
+ * not a multiple of 32: INVALID_ARG); code planes 16-byte aligned, scale
+ * planes and C 4-byte aligned.  A NaN scale (0xFF) makes its terms NaN. */
+fp4q_status fp4q_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes, const uint8_t *a_scales,
+                            const uint8_t *b_codes, const uint8_t *b_scales, int32_t out_dtype, void *c,
+                            void *hip_stream);
+
 /* Host-side check of counters copied back from the device: FP4Q_ERR_NONFINITE
  * when counters[2] != 0, else FP4Q_OK (NULL -> FP4Q_ERR_INVALID_ARG). */
 fp4q_status fp4q_check_counters(const uint64_t *host_counters);

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_silu_mul_fwht_mxfp4", "fp4q_fwht",
-              "fp4q_dequantize"):
+              "fp4q_dequantize", "fp4q_mxfp4_gemm"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -151,6 +151,18 @@ def test_silu_mul_fwht_needs_up():
     a = _args(rotation=_lib.FP4Q_ROT_FWHT_ROW)
     assert lib.fp4q_silu_mul_fwht_mxfp4(a, FAKE, None, OUTS, None) == _lib.FP4Q_ERR_INVALID_ARG
     assert lib.fp4q_silu_mul_fwht_mxfp4(a, FAKE, FAKE + 8, OUTS, None) == _lib.FP4Q_ERR_UNSUPPORTED
+
+
+def test_mxfp4_gemm_rejects():
+    lib = _lib_or_skip()
+    F = FAKE
+    assert lib.fp4q_mxfp4_gemm(4, 4, 80, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_INVALID_ARG   # K % 32
+    assert lib.fp4q_mxfp4_gemm(4, 4, 96, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_UNSUPPORTED   # K % 128
+    assert lib.fp4q_mxfp4_gemm(-1, 4, 128, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_INVALID_ARG
+    assert lib.fp4q_mxfp4_gemm(4, 4, 128, F, F, F, F, 7, F, None) == _lib.FP4Q_ERR_INVALID_ARG
+    assert lib.fp4q_mxfp4_gemm(4, 4, 128, None, F, F, F, 0, F, None) == _lib.FP4Q_ERR_INVALID_ARG
+    assert lib.fp4q_mxfp4_gemm(4, 4, 128, F + 8, F, F, F, 0, F, None) == _lib.FP4Q_ERR_UNSUPPORTED
+    assert lib.fp4q_mxfp4_gemm(0, 4, 128, None, None, None, None, 0, None, None) == _lib.FP4Q_OK
 
 
 def test_fwht_and_dequant_reject():

@@ -787,3 +787,62 @@ def test_fwht128_nv_act_8192_heads():
     assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
     rows = np.random.default_rng(2).choice(x.shape[0], 64, replace=False)
     assert rel_l2(rot[rows], oracle.fwht(x[rows], t=128)) <= RTOL_ROT
+
+
+# ------------------------------------------------------------------ MXFP4 GEMM
+def _gemm_check(c_gpu, c_ref, absc, K, extra_rel=0.0):
+    """fp32 accumulation of exact products in any order is within K 2^-24 sum|a b|
+    of the exact sum (bf16 output adds half an ulp of the result)."""
+    c_gpu = c_gpu.astype(np.float64)
+    tol = K * 2.0 ** -24 * absc + extra_rel * np.abs(c_ref)
+    bad = np.abs(c_gpu - c_ref) > tol
+    assert not bad.any(), "%d of %d outside the bound; worst at %s" % (
+        bad.sum(), bad.size, np.unravel_index(np.argmax(np.abs(c_gpu - c_ref) - tol), bad.shape))
+    rel = np.abs(c_gpu - c_ref) / np.maximum(absc, 1e-300)
+    return float(rel.max())
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (33, 17, 128), (130, 257, 256), (256, 128, 1024), (97, 300, 4096),
+                                   (5, 7, 0)])
+def test_mxfp4_gemm_small(M, N, K):
+    a = make_input(M, K, "bf16", M * 7 + K) if K else np.zeros((M, 0), np.uint16)
+    b = make_input(N, K, "f32", N * 11 + K) if K else np.zeros((N, 0), np.float32)
+    if K == 0:
+        qa = (torch.zeros((M, 0), dtype=torch.uint8, device=gpu()), torch.zeros((M, 0), dtype=torch.uint8, device=gpu()))
+        qb = (torch.zeros((N, 0), dtype=torch.uint8, device=gpu()), torch.zeros((N, 0), dtype=torch.uint8, device=gpu()))
+        assert not host(fq.mxfp4_gemm(qa, qb)).any()
+        return
+    qa = fq.quantize_mxfp4(to_dev(a))
+    qb = fq.quantize_mxfp4(to_dev(b))
+    ref, absc = oracle.mx_gemm(host(qa.codes), host(qa.scales), host(qb.codes), host(qb.scales))
+    _gemm_check(host(fq.mxfp4_gemm(qa, qb)), ref, absc, K)
+    c16 = bf16_bits_to_f32(host(fq.mxfp4_gemm(qa, qb, out_dtype=torch.bfloat16)))
+    _gemm_check(c16, ref, absc, K, extra_rel=2.0 ** -8)
+
+
+def test_mxfp4_gemm_nan_scale_and_exact_case():
+    M, N, K = 64, 64, 256
+    ac = np.full((M, K // 2), 0x22, np.uint8)                   # all 1.0
+    asc = np.full((M, K // 32), 127, np.uint8)
+    rng = np.random.default_rng(61)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    bsc = rng.integers(120, 135, (N, K // 32), dtype=np.uint8)
+    asc[3, 5] = 255                                             # NaN scale: row 3 is NaN
+    ref, _ = oracle.mx_gemm(ac, asc, bc, bsc)
+    c = host(fq.mxfp4_gemm((to_dev(ac), to_dev(asc)), (to_dev(bc), to_dev(bsc))))
+    assert np.isnan(c[3]).all() and not np.isnan(np.delete(c, 3, axis=0)).any()
+    # row sums of B: every partial sum is a short dyadic number, exact in fp32
+    ok = np.delete(np.arange(M), 3)
+    assert np.array_equal(c[ok].astype(np.float64), ref[ok])
+
+
+def test_mxfp4_gemm_8192_sampled_rows():
+    a = workload("act_bf16_8192")
+    w = np.ascontiguousarray(workloads.make("weight_bf16_8192x28672", rows=8192, cols=8192))
+    qa = fq.quantize_mxfp4(to_dev(a))
+    qb = fq.quantize_mxfp4(to_dev(w))
+    c = host(fq.mxfp4_gemm(qa, qb))
+    ac, asc, bc, bsc = host(qa.codes), host(qa.scales), host(qb.codes), host(qb.scales)
+    for r0 in (0, 4093, 8192 - 3):
+        ref, absc = oracle.mx_gemm(ac, asc, bc, bsc, rows=(r0, 3))
+        _gemm_check(c[r0:r0 + 3], ref, absc, 8192)
