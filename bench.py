@@ -177,6 +177,33 @@ def profile_kernels(dev, reps=5):
         2 * ng * 2 + ng // 2 + ng // 32)
     del xg, gate, up, og, hb
 
+    # MXFP4 GEMM: C = A W^T, A the 8192x8192 activation, W 8192x8192 of the weight recipe
+    xa = dev_tensor("act_bf16_8192")
+    wn = workloads.make("weight_bf16_8192x28672", rows=8192, cols=8192)
+    xw = torch.from_numpy(wn.view(np.int16)).to(dev).view(torch.bfloat16)
+    qa, qw = fq.quantize_mxfp4(xa), fq.quantize_mxfp4(xw)
+    cg = torch.empty((8192, 8192), dtype=torch.float32, device=dev)
+    flops = 2.0 * 8192 ** 3
+
+    def run_flops(label, fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print("%-58s %9.2f us  %8.1f TFLOP/s" % (label, us, flops / us / 1e6), flush=True)
+
+    run_flops("MXFP4 GEMM 8192x8192x8192 -> fp32", lambda: fq.mxfp4_gemm(qa, qw, out=cg))
+    cb = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    run_flops("MXFP4 GEMM 8192x8192x8192 -> bf16", lambda: fq.mxfp4_gemm(qa, qw, out_dtype=torch.bfloat16, out=cb))
+    wt = xw.t().contiguous()
+    run_flops("  reference: torch bf16 matmul 8192x8192x8192", lambda: torch.matmul(xa, wt, out=cb))
+    del xa, xw, qa, qw, cg, cb, wt
+
     x1 = dev_tensor("mx_f32_1024")
     o1 = fq.quantize_mxfp4(x1, counters=True)
     y1 = torch.empty_like(x1)
