@@ -35,19 +35,36 @@ constexpr int kWaveTile = kTile / 2;   // 128: a 2x2 arrangement of waves
 constexpr int kSub = kWaveTile / 32;   // 4x4 instructions per wave
 constexpr int kKStep = 128;
 constexpr int kRowBytes = kKStep / 2;     // 64 bytes of nibbles per row and stage
-constexpr int kLdsStride = kRowBytes + 16;
 constexpr int kXcds = 8;
 constexpr int kGroupRows = 8;
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS stage buffer: A codes (256 rows x 64 bytes, the four 16-byte chunks of
+// a row permuted by (row >> 1) mod 4 to spread reads over the banks), B
+// codes, then the 4 scale bytes of each A row and of each B row.
+constexpr int kCodeBytes = kTile * kRowBytes;               // 16 KiB
+constexpr int kStageBytes = 2 * kCodeBytes + 2 * kTile * 4;
+constexpr int kLoadsPerStage = 2 * (kCodeBytes / 1024 / 4) + 2;   // per lane: 4 + 4 codes, 1 + 1 scales
+
+__device__ __forceinline__ int chunk_of(int row, int part) { return part ^ ((row >> 1) & 3); }
+
+// s_waitcnt with vmcnt <= n (expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m, int tiles_n, int ntiles) {
-  __shared__ __align__(16) uint8_t s_a[2][kTile * kLdsStride];
-  __shared__ __align__(16) uint8_t s_b[2][kTile * kLdsStride];
-  __shared__ uint32_t s_sa[2][kTile];   // the 4 scale bytes of a row for the stage's 4 K-blocks
-  __shared__ uint32_t s_sb[2][kTile];
+  // three stage buffers as separate objects, so that reads of one are not
+  // ordered after the direct-to-LDS loads still in flight into the others
+  __shared__ __align__(16) uint8_t s_st0[kStageBytes];
+  __shared__ __align__(16) uint8_t s_st1[kStageBytes];
+  __shared__ __align__(16) uint8_t s_st2[kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   // XCD-contiguous tile order: workgroup w runs on XCD w mod 8
@@ -63,33 +80,26 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
 
   const int64_t kb = g.K / 2, ksb = g.K / 32;
   const int nstage = (int)(g.K / kKStep);
-  constexpr int kChunks = kTile * 4 / 256;   // 16-byte chunks per thread and operand
-  uint4 ra[kChunks], rb[kChunks];
-  uint32_t rsa = 0u, rsb = 0u;
-  auto gload = [&](int st) {
+  // rows past M or N read a valid row instead; their results are not stored
+  auto issue = [&](int st, uint8_t* buf) {
     const int64_t kbyte = (int64_t)st * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + 256 * i;   // row c / 4, part c mod 4
-      const int row = c >> 2, part = c & 3;
-      const int64_t ma = m0 + row, nb = n0 + row;
-      ra[i] = ma < g.M ? *reinterpret_cast<const uint4*>(g.a_codes + ma * kb + kbyte + part * 16) : make_uint4(0, 0, 0, 0);
-      rb[i] = nb < g.N ? *reinterpret_cast<const uint4*>(g.b_codes + nb * kb + kbyte + part * 16) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kCodeBytes / 1024 / 4; ++i) {
+      const int region = wv * (kCodeBytes / 1024 / 4) + i;   // 16 rows x 64 bytes
+      const int row = region * 16 + (lane >> 2);
+      const int part = chunk_of(row, lane & 3);
+      const int64_t ra = min(m0 + row, g.M - 1), rb = min(n0 + row, g.N - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.a_codes + ra * kb + kbyte + part * 16),
+                                       (lds_void_t*)(buf + region * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.b_codes + rb * kb + kbyte + part * 16),
+                                       (lds_void_t*)(buf + kCodeBytes + region * 1024), 16, 0, 0);
     }
-    const int64_t ra_ = m0 + tid, rb_ = n0 + tid;   // one A row and one B row of scale bytes per thread
-    rsa = ra_ < g.M ? *reinterpret_cast<const uint32_t*>(g.a_scales + ra_ * ksb + (int64_t)st * 4) : 0x7F7F7F7Fu;
-    rsb = rb_ < g.N ? *reinterpret_cast<const uint32_t*>(g.b_scales + rb_ * ksb + (int64_t)st * 4) : 0x7F7F7F7Fu;
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 2, part = c & 3;
-      *reinterpret_cast<uint4*>(&s_a[buf][row * kLdsStride + part * 16]) = ra[i];
-      *reinterpret_cast<uint4*>(&s_b[buf][row * kLdsStride + part * 16]) = rb[i];
-    }
-    s_sa[buf][tid] = rsa;
-    s_sb[buf][tid] = rsb;
+    const int row = wv * 64 + lane;
+    const int64_t ra = min(m0 + row, g.M - 1), rb = min(n0 + row, g.N - 1);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.a_scales + ra * ksb + (int64_t)st * 4),
+                                     (lds_void_t*)(buf + 2 * kCodeBytes + wv * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.b_scales + rb * ksb + (int64_t)st * 4),
+                                     (lds_void_t*)(buf + 2 * kCodeBytes + kTile * 4 + wv * 256), 4, 0, 0);
   };
 
   const int wr = wv >> 1, wc = wv & 1;
@@ -101,14 +111,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (nstage > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstage) gload(st + 1);
+  auto compute = [&](const uint8_t* buf) {
+    const uint32_t* sa_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes);
+    const uint32_t* sb_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes + kTile * 4);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int part = 2 * kk + (lane >> 5);   // this lane's 32 K positions of the 64-K step
@@ -117,13 +122,13 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
         const int arow = kWaveTile * wr + 32 * u + (lane & 31);
-        const uint4 va = *reinterpret_cast<const uint4*>(&s_a[buf][arow * kLdsStride + part * 16]);
+        const uint4 va = *reinterpret_cast<const uint4*>(buf + arow * kRowBytes + chunk_of(arow, part) * 16);
         a[u] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-        sa[u] = (int)((s_sa[buf][arow] >> (8 * part)) & 0xFFu);
+        sa[u] = (int)((sa_row[arow] >> (8 * part)) & 0xFFu);
         const int brow = kWaveTile * wc + 32 * u + (lane & 31);
-        const uint4 vb = *reinterpret_cast<const uint4*>(&s_b[buf][brow * kLdsStride + part * 16]);
+        const uint4 vb = *reinterpret_cast<const uint4*>(buf + kCodeBytes + brow * kRowBytes + chunk_of(brow, part) * 16);
         b[u] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        sb[u] = (int)((s_sb[buf][brow] >> (8 * part)) & 0xFFu);
+        sb[u] = (int)((sb_row[brow] >> (8 * part)) & 0xFFu);
       }
 #pragma unroll
       for (int i = 0; i < kSub; ++i)
@@ -131,10 +136,31 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
         for (int j = 0; j < kSub; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
     }
-    if (st + 1 < nstage) {
-      lstore(buf ^ 1);
-      __syncthreads();
+  };
+  // one pipeline step: refill the buffer of stage st + 2 (last read at stage
+  // st - 1, hence the first barrier), wait for this thread's loads of stage
+  // st, make everyone's visible (second barrier), compute stage st.  The
+  // barriers carry no memory fence: the loads are waited for explicitly.
+  auto step = [&](int st, uint8_t* cur, uint8_t* fill) {
+    __builtin_amdgcn_s_barrier();
+    if (st + 2 < nstage) {
+      issue(st + 2, fill);
+      wait_vm<2 * kLoadsPerStage>();
+    } else if (st + 1 < nstage) {
+      wait_vm<kLoadsPerStage>();
+    } else {
+      wait_vm<0>();
     }
+    __builtin_amdgcn_s_barrier();
+    compute(cur);
+  };
+
+  if (nstage > 0) issue(0, s_st0);
+  if (nstage > 1) issue(1, s_st1);
+  for (int st = 0; st < nstage; st += 3) {
+    step(st, s_st0, s_st2);
+    if (st + 1 < nstage) step(st + 1, s_st1, s_st0);
+    if (st + 2 < nstage) step(st + 2, s_st2, s_st1);
   }
 
 #pragma unroll
