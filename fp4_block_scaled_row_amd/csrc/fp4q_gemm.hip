@@ -17,10 +17,10 @@
 // four waves (one per SIMD) a 128x128 quarter: 4x4 instructions per 64-K
 // step on 256 accumulator registers, so every operand fetched from LDS feeds
 // four instructions.  K advances 128 per stage: the A and B tiles (256 rows x
-// 64 bytes, rows padded to 80 bytes in LDS to spread the 16-byte reads over
-// the banks) and their scale bytes go through LDS, double-buffered, with the
-// next stage's global loads
-// in flight during the current stage's matrix instructions.  Workgroups are
+// 64 bytes) and their scale bytes are loaded straight into LDS (direct-to-LDS
+// global loads), into a ring of four stage buffers kept three stages ahead of
+// the one being multiplied; one fence-free barrier per stage, the loads
+// being waited for explicitly.  Workgroups are
 // numbered so that each XCD walks a contiguous range of C tiles, in groups of
 // 8 tile rows traversed column by column, so that the workgroups resident on
 // one XCD at a time share both A row tiles and B column tiles in its L2.
@@ -60,11 +60,12 @@ __device__ __forceinline__ void wait_vm() {
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m, int tiles_n, int ntiles) {
-  // three stage buffers as separate objects, so that reads of one are not
+  // four stage buffers as separate objects, so that reads of one are not
   // ordered after the direct-to-LDS loads still in flight into the others
   __shared__ __align__(16) uint8_t s_st0[kStageBytes];
   __shared__ __align__(16) uint8_t s_st1[kStageBytes];
   __shared__ __align__(16) uint8_t s_st2[kStageBytes];
+  __shared__ __align__(16) uint8_t s_st3[kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   // XCD-contiguous tile order: workgroup w runs on XCD w mod 8
@@ -114,53 +115,62 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
   auto compute = [&](const uint8_t* buf) {
     const uint32_t* sa_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes);
     const uint32_t* sb_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes + kTile * 4);
+    // both 64-K steps' operands are read up front, so the second step's
+    // reads complete under the first step's matrix instructions
+    v8i_t a[2][kSub], b[2][kSub];
+    int sa[2][kSub], sb[2][kSub];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int part = 2 * kk + (lane >> 5);   // this lane's 32 K positions of the 64-K step
-      v8i_t a[kSub], b[kSub];
-      int sa[kSub], sb[kSub];
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
         const int arow = kWaveTile * wr + 32 * u + (lane & 31);
         const uint4 va = *reinterpret_cast<const uint4*>(buf + arow * kRowBytes + chunk_of(arow, part) * 16);
-        a[u] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-        sa[u] = (int)((sa_row[arow] >> (8 * part)) & 0xFFu);
+        a[kk][u] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
+        sa[kk][u] = (int)((sa_row[arow] >> (8 * part)) & 0xFFu);
         const int brow = kWaveTile * wc + 32 * u + (lane & 31);
         const uint4 vb = *reinterpret_cast<const uint4*>(buf + kCodeBytes + brow * kRowBytes + chunk_of(brow, part) * 16);
-        b[u] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        sb[u] = (int)((sb_row[brow] >> (8 * part)) & 0xFFu);
+        b[kk][u] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
+        sb[kk][u] = (int)((sb_row[brow] >> (8 * part)) & 0xFFu);
       }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < kSub; ++i)
 #pragma unroll
         for (int j = 0; j < kSub; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[kk][j], acc[i][j], 4, 4, 0,
+                                                                      sa[kk][i], 0, sb[kk][j]);
   };
-  // one pipeline step: refill the buffer of stage st + 2 (last read at stage
-  // st - 1, hence the first barrier), wait for this thread's loads of stage
-  // st, make everyone's visible (second barrier), compute stage st.  The
-  // barriers carry no memory fence: the loads are waited for explicitly.
+  // one pipeline step: wait for this thread's loads of stage st (stages
+  // st + 1 and st + 2 stay in flight), one barrier -- after it every wave's
+  // loads of stage st are in LDS and every wave is done with stage st - 1 --
+  // then refill stage st - 1's buffer with stage st + 3 and compute stage st.
+  // The barrier carries no memory fence: the loads are waited for explicitly.
   auto step = [&](int st, uint8_t* cur, uint8_t* fill) {
+    if (st + 2 < nstage) wait_vm<2 * kLoadsPerStage>();
+    else if (st + 1 < nstage) wait_vm<kLoadsPerStage>();
+    else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    if (st + 2 < nstage) {
-      issue(st + 2, fill);
-      wait_vm<2 * kLoadsPerStage>();
-    } else if (st + 1 < nstage) {
-      wait_vm<kLoadsPerStage>();
-    } else {
-      wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();
+    if (st + 3 < nstage) issue(st + 3, fill);
     compute(cur);
   };
 
   if (nstage > 0) issue(0, s_st0);
   if (nstage > 1) issue(1, s_st1);
-  for (int st = 0; st < nstage; st += 3) {
-    step(st, s_st0, s_st2);
+  if (nstage > 2) issue(2, s_st2);
+  // unrolled over two rotations of the ring: the compiler orders the first
+  // read of an iteration after every load in flight, once per iteration
+  for (int st = 0; st < nstage; st += 8) {
+    step(st, s_st0, s_st3);
     if (st + 1 < nstage) step(st + 1, s_st1, s_st0);
     if (st + 2 < nstage) step(st + 2, s_st2, s_st1);
+    if (st + 3 < nstage) step(st + 3, s_st3, s_st2);
+    if (st + 4 < nstage) step(st + 4, s_st0, s_st3);
+    if (st + 5 < nstage) step(st + 5, s_st1, s_st0);
+    if (st + 6 < nstage) step(st + 6, s_st2, s_st1);
+    if (st + 7 < nstage) step(st + 7, s_st3, s_st2);
   }
 
 #pragma unroll
