@@ -588,51 +588,66 @@ __device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCt
   q.scales[s >> 1] = (uint8_t)scale;
 }
 
-// Lean max->6 round-to-nearest encoding of one raw bf16 slot (8 values, no
-// rotation, no counters), free of branches so that the compiler can overlap
-// consecutive slots.  The block amax comes from packed 16-bit maxima of the
-// bf16 bit patterns (the lane pair 2k, 2k+1 holds one 16-block and must
-// execute together).  The scale byte comes from its brackets, the codes from
-// one product with the adjusted multiplier of that byte; both are stored
-// (both lanes of a pair store the same byte).  Returns true when the slot must
-// be recomputed exactly with nv_fix_slot_fma: the scale brackets disagree, the
-// scale code is flagged, or the block holds a non-finite value.
-__device__ __forceinline__ bool nv_fast_slot(const NvCtx& cx, const float2* s_adj, const uint4& w,
-                                             uint32_t* codes_at, uint8_t* scale_at) {
+// Largest bf16 magnitude bit pattern of the 8 values of a raw slot (sign
+// bits cleared, non-finite patterns included), from packed 16-bit maxima.
+__device__ __forceinline__ uint32_t slot_max16(const uint4& w) {
   ushort2_t m = __builtin_bit_cast(ushort2_t, w.x & 0x7FFF7FFFu);
   m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.y & 0x7FFF7FFFu));
   m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.z & 0x7FFF7FFFu));
   m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.w & 0x7FFF7FFFu));
-  uint32_t bm = m.x > m.y ? m.x : m.y;
-  bm = max(bm, dpp_u32<kQuadXor1>(bm));
+  return m.x > m.y ? m.x : m.y;
+}
+
+// Lean max->6 round-to-nearest encoding of two raw bf16 slots of one lane
+// (no rotation, no counters), free of branches.  The lane pair 2k, 2k+1 holds
+// 16-block A in its first slots (w0) and 16-block B in its second slots
+// (w1); the even lane works out the scale of A, the odd lane that of B, and
+// each passes the other the multiplier it needs, so that the per-block work
+// is done once per block instead of once per lane.  The scale byte comes from
+// its two brackets, the codes from one product with the adjusted multiplier
+// of that byte (nv_fill_adjusted_table).  Returns the codes of w0 and w1 and,
+// in *scale, the byte of the block this lane worked out; the result *need is
+// 1 when that block must be recomputed exactly (nv_fix_slot_fma): its scale
+// brackets disagree or its scale code is flagged.  A block holding a
+// non-finite value needs no test of its own: its products are inf or NaN,
+// which convert to the NaN scale code (flagged); a finite block never
+// reaches that code, since its quotient stays below 448 (1 + 2^-21), far
+// from the overflow point 464.
+__device__ __forceinline__ void nv_fast_pair(const NvCtx& cx, const float2* s_adj, const uint4& w0, const uint4& w1,
+                                             uint32_t m0, uint32_t m1, bool odd, uint32_t& codes0, uint32_t& codes1,
+                                             uint32_t& scale, uint32_t& need) {
+  const uint32_t own = odd ? m1 : m0, give = odd ? m0 : m1;
+  const uint32_t bm = max(own, dpp_u32<kQuadXor1>(give));
   const float bamax = as_f(bm << 16);
-  // scale byte from both brackets (non-negative operands: sign bits clear; a
-  // non-finite block saturates here and is redone by the fix-up)
-  const float tl = fminf(bamax * cx.inv6_lo, 448.0f);
-  const float th = fminf(bamax * cx.inv6_hi, 448.0f);
   // (the old operand of a packing conversion only fills bytes that are
   // overwritten or ignored: a dead value avoids a register copy)
+  const float tl = bamax * cx.inv6_lo, th = bamax * cx.inv6_hi;
   const uint32_t sb2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, (int)as_u(th), false);
   const uint32_t c = sb2 & 0x7Fu;
-  const float2 mf = s_adj[c];   // adjusted multiplier of this scale code, flag
+  const float2 mf = s_adj[c];   // adjusted multiplier of this scale code, flag (0.0 or 1.0)
+  // the upper bracket's byte is the lower one's or the next: their difference is 0 or 1
+  need = ((((sb2 >> 8) & 0xFFu) - (sb2 & 0xFFu)) | (as_u(mf.y) >> 29)) & 1u;
+  scale = c;
+  const float sw = as_f(dpp_u32<kQuadXor1>(as_u(mf.x)));
+  const float ma = odd ? sw : mf.x, mb = odd ? mf.x : sw;
   const float one = e8m0_operand(127u);
-  uint32_t ca = 0u;
-#define FP4Q_PAIR(K, WK)                                                                          \
+  uint32_t ca = 0u, cb = 0u;
+#define FP4Q_PAIR(C, M, K, WK)                                                                    \
   {                                                                                               \
-    const float al = bf_lo(WK) * mf.x, ah = bf_hi(WK) * mf.x;                                     \
-    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(al) : ca, al, ah, one, K);        \
+    const float al = bf_lo(WK) * M, ah = bf_hi(WK) * M;                                           \
+    C = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(al) : C, al, ah, one, K);          \
   }
-  FP4Q_PAIR(0, w.x)
-  FP4Q_PAIR(1, w.y)
-  FP4Q_PAIR(2, w.z)
-  FP4Q_PAIR(3, w.w)
+  FP4Q_PAIR(ca, ma, 0, w0.x)
+  FP4Q_PAIR(ca, ma, 1, w0.y)
+  FP4Q_PAIR(ca, ma, 2, w0.z)
+  FP4Q_PAIR(ca, ma, 3, w0.w)
+  FP4Q_PAIR(cb, mb, 0, w1.x)
+  FP4Q_PAIR(cb, mb, 1, w1.y)
+  FP4Q_PAIR(cb, mb, 2, w1.z)
+  FP4Q_PAIR(cb, mb, 3, w1.w)
 #undef FP4Q_PAIR
-  // codes non-temporal: they stream out during the encode instead of piling
-  // up as dirty L2 lines that drain after it (scale bytes stay cached: their
-  // partial lines are better merged in L2)
-  __builtin_nontemporal_store(ca, codes_at);
-  *scale_at = (uint8_t)c;
-  return ((sb2 ^ (sb2 >> 8)) & 0xFFu) != 0u || mf.y != 0.0f || bm >= 0x7F80u;
+  codes0 = ca;
+  codes1 = cb;
 }
 
 }  // namespace fp4q

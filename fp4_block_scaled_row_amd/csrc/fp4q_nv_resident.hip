@@ -53,12 +53,10 @@ constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// (the same slot_max16 expression as phase 2's: the compiler keeps the
+// 16-bit maxima of the register slots from here instead of recomputing them)
 __device__ __forceinline__ uint32_t raw_finite_absmax(const uint4& w) {
-  ushort2_t m = __builtin_bit_cast(ushort2_t, w.x & 0x7FFF7FFFu);
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.y & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.z & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w.w & 0x7FFF7FFFu));
-  uint32_t mx = m.x > m.y ? m.x : m.y;
+  uint32_t mx = slot_max16(w);
   if (mx >= 0x7F80u) {   // a non-finite value is present: take the finite max only
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     mx = 0u;
@@ -113,69 +111,107 @@ __device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, uint32_t ls, 
 
 // Phase-2 state of one thread.  GUARD is false when every workgroup holds
 // exactly kMaxSlots full slot rows: then no slot needs a bounds test and the
-// encoding is straight-line code.  redo: bit j set when this thread must
-// recompute its slot j exactly (about one element in 2000 on Student-t
-// data: bf16 inputs put many quotients within 2^-22 of a rounding boundary).
+// encoding is straight-line code.  Slot rows are taken two at a time (rows j
+// and j + 1, j even): the lane pair 2k, 2k+1 holds block k of row j and block
+// k of row j + 1, the even lane works out the first block's scale, the odd
+// lane the second's (nv_fast_pair).  redo: bit j set when the block this lane
+// worked out for rows j, j+1 must be recomputed exactly (about one element in
+// 2000 on Student-t data: bf16 inputs put many quotients within 2^-22 of a
+// rounding boundary); exact_slots() turns it into per-slot bits.
 template <bool GUARD>
 struct Phase2 {
   const NvCtx& cx;
   const float2* s_adj;
-  uint8_t* codes_wg;     // this workgroup's first code byte
-  uint8_t* scales_wg;    // this workgroup's first scale byte
-  int wbase, lane, tid, nres;
+  uint32_t* codes_lane;   // code word of this lane's slot in row 0 (row j: + 64 j)
+  uint8_t* scale_lane;    // scale byte of the block this lane works out for rows 0, 1 (rows j, j+1: + 32 j)
+  int wbase, lane, nres;
   uint32_t n_valid;
+  bool odd;
   uint32_t redo;
 
-  __device__ __forceinline__ void slot(int j, uint4 w) {
-    if (GUARD && j >= nres) return;
-    const uint32_t ls = slot_of(wbase, j, lane);
-    uint32_t* cp = reinterpret_cast<uint32_t*>(codes_wg + (size_t)ls * 4u);
-    uint8_t* sp = scales_wg + (ls >> 1);
-    bool need = false;
+  __device__ __forceinline__ void pair(int j, uint4 w0, uint4 w1, uint32_t m0, uint32_t m1) {
+    bool v0 = true, v1 = true;
     if constexpr (GUARD) {
-      if (ls < n_valid) need = nv_fast_slot(cx, s_adj, w, cp, sp);
-    } else {
-      need = nv_fast_slot(cx, s_adj, w, cp, sp);
+      // both lanes of a block agree (valid slot counts are even); a slot past
+      // the end holds zeros, which encode to a zero block that needs no redo
+      v0 = j < nres && slot_of(wbase, j, lane) < n_valid;
+      v1 = j + 1 < nres && slot_of(wbase, j + 1, lane) < n_valid;
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      if (!v0) { w0 = z; m0 = 0u; }
+      if (!v1) { w1 = z; m1 = 0u; }
     }
-    // (materialised in a VGPR at once: 32 pending lane masks would exhaust
+    uint32_t c0, c1, sc, need;
+    nv_fast_pair(cx, s_adj, w0, w1, m0, m1, odd, c0, c1, sc, need);
+    // codes non-temporal: they stream out during the encode instead of piling
+    // up as dirty L2 lines that drain after it (scale bytes stay cached: their
+    // partial lines are better merged in L2)
+    if (!GUARD || v0) __builtin_nontemporal_store(c0, codes_lane + 64 * j);
+    if (!GUARD || v1) __builtin_nontemporal_store(c1, codes_lane + 64 * (j + 1));
+    if (!GUARD || (odd ? v1 : v0)) scale_lane[32 * j] = (uint8_t)sc;
+    // (materialised in a VGPR at once: 16 pending lane masks would exhaust
     // the scalar registers)
-    uint32_t bit = need ? (1u << j) : 0u;
+    uint32_t bit = need << j;
     asm volatile("" : "+v"(bit));
     redo |= bit;
   }
+
+  // Per-slot redo bits: slot j of a lane belongs to the block its pair worked
+  // out in the even lane (j even) or in the odd lane (j odd).
+  __device__ __forceinline__ uint32_t exact_slots() const {
+    const uint32_t mine = redo & 0x55555555u;
+    const uint32_t other = dpp_u32<kQuadXor1>(redo) & 0x55555555u;
+    return odd ? (other | (mine << 1)) : (mine | (other << 1));
+  }
 };
 
-template <class P, int RS, int... J>
-__device__ __forceinline__ void encode_reg_slots(P& p, const uint4 (&r)[RS], std::integer_sequence<int, J...>) {
-  (p.slot(J, r[J]), ...);
-}
+// Phase-2 slot sources: slot j of a lane comes from its registers (j <
+// reg_slots), from LDS (the next kLdsSlots), or from the re-read ring (the
+// rest, prefetched kAhead slots ahead; compile-time indices throughout).
+template <bool GUARD>
+struct SlotSource {
+  static constexpr int kRs = reg_slots<GUARD>();
+  static constexpr int kRe = reread_slots<GUARD>();
+  const uint4 (&r)[kRs];
+  const uint4* s_data;
+  uint4 (&pre)[kAhead];
+  const uint16_t* wg_x;
+  int wbase, lane, tid, nres;
+  uint32_t n_valid;
 
-template <int RS, class P, int... J>
-__device__ __forceinline__ void encode_lds_slots(P& p, const uint4* s_data, std::integer_sequence<int, J...>) {
-  (p.slot(RS + J, s_data[J * kResThreads + p.tid]), ...);
-}
-
-// the re-read slots with a kAhead-deep prefetch ring (compile-time indices)
-template <bool GUARD, class P, int... K>
-__device__ __forceinline__ void encode_reread_slots(P& p, uint4 (&pre)[kAhead], const uint16_t* wg_x,
-                                                    std::integer_sequence<int, K...>) {
-  constexpr int j0 = reg_slots<GUARD>() + kLdsSlots;
-  auto one = [&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    const uint4 w = pre[k % kAhead];
-    if constexpr (k + kAhead < reread_slots<GUARD>()) {
-      const int jn = j0 + k + kAhead;
-      const uint32_t ls = slot_of(p.wbase, jn, p.lane);
-      if constexpr (GUARD) {
-        pre[k % kAhead] = load_cached(wg_x, ls, jn < p.nres && ls < p.n_valid);
-      } else {
-        const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
-        pre[k % kAhead] = make_uint4(a.x, a.y, a.z, a.w);
+  template <int J>
+  __device__ __forceinline__ uint4 get() {
+    if constexpr (J < kRs) {
+      return r[J];
+    } else if constexpr (J < kRs + kLdsSlots) {
+      return s_data[(J - kRs) * kResThreads + tid];
+    } else {
+      constexpr int k = J - kRs - kLdsSlots;
+      const uint4 w = pre[k % kAhead];
+      if constexpr (k + kAhead < kRe) {
+        const int jn = J + kAhead;
+        const uint32_t ls = slot_of(wbase, jn, lane);
+        if constexpr (GUARD) {
+          pre[k % kAhead] = load_cached(wg_x, ls, jn < nres && ls < n_valid);
+        } else {
+          const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
+          pre[k % kAhead] = make_uint4(a.x, a.y, a.z, a.w);
+        }
       }
+      return w;
     }
-    p.slot(j0 + k, w);
+  }
+};
+
+template <bool GUARD, int... P>
+__device__ __forceinline__ void encode_pairs(Phase2<GUARD>& p2, SlotSource<GUARD>& src,
+                                             std::integer_sequence<int, P...>) {
+  auto one = [&](auto pc) {
+    constexpr int j = 2 * decltype(pc)::value;
+    const uint4 w0 = src.template get<j>();
+    const uint4 w1 = src.template get<j + 1>();
+    p2.pair(j, w0, w1, slot_max16(w0), slot_max16(w1));
   };
-  (one(std::integral_constant<int, K>{}), ...);
+  (one(std::integral_constant<int, P>{}), ...);
 }
 
 // Tensor maximum (finite bf16 magnitudes, as an fp32 bit pattern) from a scan
@@ -358,18 +394,21 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
       pre[k] = make_uint4(a.x, a.y, a.z, a.w);
     }
   }
-  Phase2<GUARD> p2{cx, s_adj, q.codes + (base << 2), q.scales + (base >> 1), wbase, lane2, wv * 64 + lane2, nres,
-                   n_valid, 0u};
-  encode_reg_slots(p2, r, std::make_integer_sequence<int, kRegSlots>{});
-  encode_lds_slots<kRegSlots>(p2, s_data, std::make_integer_sequence<int, kLdsSlots>{});
-  encode_reread_slots<GUARD>(p2, pre, wg_x, std::make_integer_sequence<int, reread_slots<GUARD>()>{});
+  const bool odd = (lane2 & 1) != 0;
+  Phase2<GUARD> p2{cx, s_adj,
+                   reinterpret_cast<uint32_t*>(q.codes + (base << 2)) + wbase + lane2,
+                   q.scales + (base >> 1) + (wbase >> 1) + (lane2 >> 1) + (odd ? 32 : 0),
+                   wbase, lane2, nres, n_valid, odd, 0u};
+  SlotSource<GUARD> src{r, s_data, pre, wg_x, wbase, lane2, wv * 64 + lane2, nres, n_valid};
+  static_assert(kMaxSlots % 2 == 0, "slot rows are encoded in pairs");
+  encode_pairs(p2, src, std::make_integer_sequence<int, kMaxSlots / 2>{});
   // Exact recomputations, after this thread's fast stores (program order per
   // address keeps the exact values last).  The context is rebuilt from LDS so
   // that phase 2 keeps only the two bracket factors in registers.  With
   // g < 2^-100 every slot is redone on inputs and g scaled by 2^100 (exact
   // power-of-two scaling: the quotients are unchanged and nothing underflows).
   asm volatile("" ::: "memory");
-  uint32_t redo = p2.redo;
+  uint32_t redo = p2.exact_slots();
   NvCtx cf;
   nv_context(as_f(s_amax), false, cf);
   float xscale = 1.0f;
