@@ -109,11 +109,18 @@ __device__ __forceinline__ void nv_fill_inverse_table(float2* s_inv, const NvCtx
 // a strict bracket of the exact reciprocal with the fp32 reciprocal's 2^-23
 // error -- for the exact path, for every E4M3 code; c = 0 gives (0, 0)
 // (every code of such a block is a signed zero), c = 127 (NaN scale) is
-// flagged.  s_eps: 8 entries of scratch.  Every thread of the workgroup calls
-// this (it synchronises); the workgroup has at least 128 threads.  Requires
-// g >= 2^-100 for meaningful entries.
+// flagged.  The flag is in the sign bit of the second member (-0.0 flagged,
+// +0.0 not), so that its bits test as an integer.
+// NCODES = 256 adds flagged entries for the byte values 128..255 (a negative
+// or NaN conversion result), so that a raw conversion byte can index the
+// table; s_br always has 128 entries.  s_eps: 8 entries of scratch.  Every
+// thread of the workgroup calls this (it synchronises); the workgroup has at
+// least NCODES threads.  Requires g >= 2^-100 for meaningful entries.
+template <int NCODES = 128>
 __device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_br, float2* s_eps, const NvCtx& cx,
                                                        int tid) {
+  static_assert(NCODES == 128 || NCODES == 256, "one entry per E4M3 code, or per byte value");
+  const float flag = as_f(0x80000000u);
   const float g = cx.g;
   if (tid < 64) {
     const int cls = tid >> 3, k = tid & 7;
@@ -141,15 +148,15 @@ __device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_
     lo = fmaxf(lo, as_f(dpp_u32<kRowHalfMirror>(as_u(lo))));
     hi = fminf(hi, as_f(dpp_u32<kRowHalfMirror>(as_u(hi))));
     if (k == 0)
-      s_eps[cls] = (lo + 0x1p-21f <= hi - 0x1p-21f) ? make_float2(0.5f * (lo + hi), 0.0f) : make_float2(0.0f, 1.0f);
+      s_eps[cls] = (lo + 0x1p-21f <= hi - 0x1p-21f) ? make_float2(0.5f * (lo + hi), 0.0f) : make_float2(0.0f, flag);
   }
   __syncthreads();
-  if (tid < 128) {
+  if (tid < NCODES) {
     const uint32_t c = (uint32_t)tid;
-    float2 adj = make_float2(0.0f, 1.0f), br = make_float2(0.0f, 0.0f);
+    float2 adj = make_float2(0.0f, flag), br = make_float2(0.0f, 0.0f);
     if (c == 0u) {
       adj = make_float2(0.0f, 0.0f);
-    } else if (c != 127u) {
+    } else if (c < 127u) {
       const float sd = e4m3_value(c);
       const float2 e = s_eps[(as_u(sd) >> 20) & 7u];   // significand class of s_c
       const float inv = 1.0f / (sd * g);
@@ -157,7 +164,7 @@ __device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_
       adj = make_float2(inv * (1.0f + e.x), e.y);
     }
     s_adj[c] = adj;
-    s_br[c] = br;
+    if (c < 128u) s_br[c] = br;
   }
 }
 
@@ -349,7 +356,7 @@ template <bool COUNT>
 __device__ __forceinline__ uint32_t nv_encode_adj(const float v[8], uint32_t c, const NvCtx& cx, const float2* s_adj,
                                                   const float2* s_br, uint32_t& satmask) {
   const float2 mf = s_adj[c];
-  if (mf.y != 0.0f || cx.exact_all) {
+  if (as_u(mf.y) != 0u || cx.exact_all) {
     const U4 none = {0u, 0u, 0u, 0u};
     return nv_encode<false, COUNT>(v, c, cx, s_br, none, satmask);
   }
@@ -600,34 +607,33 @@ __device__ __forceinline__ uint32_t slot_max16(const uint4& w) {
 
 // Lean max->6 round-to-nearest encoding of two raw bf16 slots of one lane
 // (no rotation, no counters), free of branches.  The lane pair 2k, 2k+1 holds
-// 16-block A in its first slots (w0) and 16-block B in its second slots
-// (w1); the even lane works out the scale of A, the odd lane that of B, and
-// each passes the other the multiplier it needs, so that the per-block work
-// is done once per block instead of once per lane.  The scale byte comes from
-// its two brackets, the codes from one product with the adjusted multiplier
-// of that byte (nv_fill_adjusted_table).  Returns the codes of w0 and w1 and,
-// in *scale, the byte of the block this lane worked out; the result *need is
-// 1 when that block must be recomputed exactly (nv_fix_slot_fma): its scale
-// brackets disagree or its scale code is flagged.  A block holding a
-// non-finite value needs no test of its own: its products are inf or NaN,
-// which convert to the NaN scale code (flagged); a finite block never
-// reaches that code, since its quotient stays below 448 (1 + 2^-21), far
-// from the overflow point 464.
+// 16-block A in its first slots (w0) and 16-block B in its second slots (w1);
+// the even lane works out the scale of A, the odd lane that of B (bamax: the
+// largest magnitude of that block, non-finite values included), and each
+// passes the other the multiplier it needs, so that the per-block work is done
+// once per block instead of once per lane.
+// The scale byte comes from its two brackets, the codes from one product with
+// the adjusted multiplier of that byte (nv_fill_adjusted_table with 256
+// entries).  Returns the codes of w0 and w1 and, in *scale, the raw conversion
+// byte of the block this lane worked out (its scale byte unless the block is
+// redone); bit 31 of *need is set when that block must be recomputed exactly
+// (nv_fix_slot_fma): its scale brackets disagree or its byte is flagged (the
+// other bits are unspecified).  A block holding a non-finite value needs no
+// test of its own: its products are inf or NaN, which convert to a NaN byte
+// (flagged); a finite block never gets one, since its quotient stays below
+// 448 (1 + 2^-21), far from the overflow point 464.
 __device__ __forceinline__ void nv_fast_pair(const NvCtx& cx, const float2* s_adj, const uint4& w0, const uint4& w1,
-                                             uint32_t m0, uint32_t m1, bool odd, uint32_t& codes0, uint32_t& codes1,
+                                             float bamax, bool odd, uint32_t& codes0, uint32_t& codes1,
                                              uint32_t& scale, uint32_t& need) {
-  const uint32_t own = odd ? m1 : m0, give = odd ? m0 : m1;
-  const uint32_t bm = max(own, dpp_u32<kQuadXor1>(give));
-  const float bamax = as_f(bm << 16);
   // (the old operand of a packing conversion only fills bytes that are
   // overwritten or ignored: a dead value avoids a register copy)
   const float tl = bamax * cx.inv6_lo, th = bamax * cx.inv6_hi;
   const uint32_t sb2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tl, th, (int)as_u(th), false);
-  const uint32_t c = sb2 & 0x7Fu;
-  const float2 mf = s_adj[c];   // adjusted multiplier of this scale code, flag (0.0 or 1.0)
-  // the upper bracket's byte is the lower one's or the next: their difference is 0 or 1
-  need = ((((sb2 >> 8) & 0xFFu) - (sb2 & 0xFFu)) | (as_u(mf.y) >> 29)) & 1u;
-  scale = c;
+  const float2 mf = s_adj[sb2 & 0xFFu];   // adjusted multiplier of this byte, flag (sign bit)
+  // the upper bracket's byte is the lower one's or the next: their low bits
+  // tell them apart (bit 8 and bit 0 of sb2, both moved to bit 31)
+  need = (__builtin_amdgcn_alignbit(sb2, sb2, 9) ^ (sb2 << 31)) | as_u(mf.y);
+  scale = sb2;
   const float sw = as_f(dpp_u32<kQuadXor1>(as_u(mf.x)));
   const float ma = odd ? sw : mf.x, mb = odd ? mf.x : sw;
   const float one = e8m0_operand(127u);

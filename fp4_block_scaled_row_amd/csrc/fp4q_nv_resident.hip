@@ -53,10 +53,9 @@ constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// (the same slot_max16 expression as phase 2's: the compiler keeps the
-// 16-bit maxima of the register slots from here instead of recomputing them)
-__device__ __forceinline__ uint32_t raw_finite_absmax(const uint4& w) {
-  uint32_t mx = slot_max16(w);
+// Largest finite bf16 magnitude bit pattern of a raw slot whose raw 16-bit
+// maximum (slot_max16) is mx.
+__device__ __forceinline__ uint32_t finite_max16(const uint4& w, uint32_t mx) {
   if (mx >= 0x7F80u) {   // a non-finite value is present: take the finite max only
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     mx = 0u;
@@ -67,7 +66,11 @@ __device__ __forceinline__ uint32_t raw_finite_absmax(const uint4& w) {
       if (hi < 0x7F80u) mx = max(mx, hi);
     }
   }
-  return mx << 16;   // fp32 bit pattern of the max
+  return mx;
+}
+
+__device__ __forceinline__ uint32_t raw_finite_absmax(const uint4& w) {
+  return finite_max16(w, slot_max16(w)) << 16;   // fp32 bit pattern of the max
 }
 
 // Slot j of a lane is workgroup slot wbase + 64 j + lane, with wbase = 64 nres
@@ -94,12 +97,6 @@ __device__ __forceinline__ void load_reg_slots(uint4 (&r)[RS], const uint16_t* w
   (one(std::integral_constant<int, J>{}), ...);
 }
 
-template <int RS, int... J>
-__device__ __forceinline__ uint32_t reg_slots_absmax(const uint4 (&r)[RS], std::integer_sequence<int, J...>) {
-  uint32_t acc = 0u;
-  ((acc = max(acc, raw_finite_absmax(r[J]))), ...);
-  return acc;
-}
 
 __device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, uint32_t ls, bool valid) {
   if (valid) {
@@ -114,10 +111,11 @@ __device__ __forceinline__ uint4 load_cached(const uint16_t* wg_x, uint32_t ls, 
 // encoding is straight-line code.  Slot rows are taken two at a time (rows j
 // and j + 1, j even): the lane pair 2k, 2k+1 holds block k of row j and block
 // k of row j + 1, the even lane works out the first block's scale, the odd
-// lane the second's (nv_fast_pair).  redo: bit j set when the block this lane
-// worked out for rows j, j+1 must be recomputed exactly (about one element in
-// 2000 on Student-t data: bf16 inputs put many quotients within 2^-22 of a
-// rounding boundary); exact_slots() turns it into per-slot bits.
+// lane the second's (nv_fast_pair).  need: a shift register, one bit per
+// pair of rows shifted in at the bottom, set when the block this lane worked
+// out for those rows must be recomputed exactly (about one element in 2000 on
+// Student-t data: bf16 inputs put many quotients within 2^-22 of a rounding
+// boundary); exact_slots() turns it into per-slot bits.
 template <bool GUARD>
 struct Phase2 {
   const NvCtx& cx;
@@ -127,40 +125,41 @@ struct Phase2 {
   int wbase, lane, nres;
   uint32_t n_valid;
   bool odd;
-  uint32_t redo;
+  uint32_t need;
 
-  __device__ __forceinline__ void pair(int j, uint4 w0, uint4 w1, uint32_t m0, uint32_t m1) {
+  // bamax: the largest magnitude of the block this lane works out (0 for a
+  // block past the end, which then needs no redo; its codes are not stored)
+  __device__ __forceinline__ void pair(int j, const uint4& w0, const uint4& w1, float bamax) {
     bool v0 = true, v1 = true;
     if constexpr (GUARD) {
-      // both lanes of a block agree (valid slot counts are even); a slot past
-      // the end holds zeros, which encode to a zero block that needs no redo
+      // both lanes of a block agree (valid slot counts are even)
       v0 = j < nres && slot_of(wbase, j, lane) < n_valid;
       v1 = j + 1 < nres && slot_of(wbase, j + 1, lane) < n_valid;
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      if (!v0) { w0 = z; m0 = 0u; }
-      if (!v1) { w1 = z; m1 = 0u; }
     }
-    uint32_t c0, c1, sc, need;
-    nv_fast_pair(cx, s_adj, w0, w1, m0, m1, odd, c0, c1, sc, need);
+    uint32_t c0, c1, sc, nd;
+    nv_fast_pair(cx, s_adj, w0, w1, bamax, odd, c0, c1, sc, nd);
     // codes non-temporal: they stream out during the encode instead of piling
     // up as dirty L2 lines that drain after it (scale bytes stay cached: their
     // partial lines are better merged in L2)
     if (!GUARD || v0) __builtin_nontemporal_store(c0, codes_lane + 64 * j);
     if (!GUARD || v1) __builtin_nontemporal_store(c1, codes_lane + 64 * (j + 1));
     if (!GUARD || (odd ? v1 : v0)) scale_lane[32 * j] = (uint8_t)sc;
-    // (materialised in a VGPR at once: 16 pending lane masks would exhaust
-    // the scalar registers)
-    uint32_t bit = need << j;
-    asm volatile("" : "+v"(bit));
-    redo |= bit;
+    need = __builtin_amdgcn_alignbit(need, nd, 31);   // (need << 1) | bit 31 of nd
   }
 
-  // Per-slot redo bits: slot j of a lane belongs to the block its pair worked
-  // out in the even lane (j even) or in the odd lane (j odd).
+  // Per-slot redo bits after all kMaxSlots / 2 pairs: slot j of a lane belongs
+  // to the block its pair worked out in the even lane (j even) or in the odd
+  // lane (j odd).
   __device__ __forceinline__ uint32_t exact_slots() const {
-    const uint32_t mine = redo & 0x55555555u;
-    const uint32_t other = dpp_u32<kQuadXor1>(redo) & 0x55555555u;
-    return odd ? (other | (mine << 1)) : (mine | (other << 1));
+    static_assert(kMaxSlots == 32, "16 pairs: one 16-bit shift register");
+    // pair p sits at bit 15 - p: reverse, then spread bit p to bit 2p
+    uint32_t m = __builtin_bitreverse32(need) >> 16;
+    m = (m | (m << 8)) & 0x00FF00FFu;
+    m = (m | (m << 4)) & 0x0F0F0F0Fu;
+    m = (m | (m << 2)) & 0x33333333u;
+    m = (m | (m << 1)) & 0x55555555u;
+    const uint32_t other = dpp_u32<kQuadXor1>(m);
+    return odd ? (other | (m << 1)) : (m | (other << 1));
   }
 };
 
@@ -203,15 +202,100 @@ struct SlotSource {
 };
 
 template <bool GUARD, int... P>
-__device__ __forceinline__ void encode_pairs(Phase2<GUARD>& p2, SlotSource<GUARD>& src,
+__device__ __forceinline__ void encode_pairs(Phase2<GUARD>& p2, SlotSource<GUARD>& src, const uint32_t (&bmp)[kMaxSlots / 4],
                                              std::integer_sequence<int, P...>) {
   auto one = [&](auto pc) {
-    constexpr int j = 2 * decltype(pc)::value;
-    const uint4 w0 = src.template get<j>();
-    const uint4 w1 = src.template get<j + 1>();
-    p2.pair(j, w0, w1, slot_max16(w0), slot_max16(w1));
+    constexpr int p = decltype(pc)::value;
+    const uint4 w0 = src.template get<2 * p>();
+    const uint4 w1 = src.template get<2 * p + 1>();
+    const uint32_t h = bmp[p >> 1];
+    p2.pair(2 * p, w0, w1, as_f((p & 1) ? (h & 0xFFFF0000u) : (h << 16)));
   };
   (one(std::integral_constant<int, P>{}), ...);
+}
+
+// Phase-1 view of a lane's slot j: its registers, its LDS entries (all loads
+// complete) or its re-read slots; a slot past the end reads as zeros.
+template <bool GUARD, int RS, int SC>
+struct Phase1Slots {
+  const uint4 (&r)[RS];
+  const uint4* s_data;
+  const uint4 (&sc)[SC];
+  int wbase, lane, tid, nres;
+  uint32_t n_valid;
+
+  template <int J>
+  __device__ __forceinline__ uint4 get() const {
+    if constexpr (J < RS) {
+      return r[J];
+    } else if constexpr (J < RS + kLdsSlots) {
+      const uint4 w = s_data[(J - RS) * kResThreads + tid];
+      if constexpr (GUARD) {
+        // (an entry past the end holds a copy of an earlier slot or nothing)
+        if (!(J < nres && slot_of(wbase, J, lane) < n_valid)) return make_uint4(0u, 0u, 0u, 0u);
+      }
+      return w;
+    } else {
+      return sc[J - RS - kLdsSlots];
+    }
+  }
+};
+
+// The block maxima phase 2 needs, from the on-chip copies: for every pair of
+// rows, the largest magnitude (raw 16-bit pattern, non-finite included) of
+// the block this lane works out, packed two pairs per word (pair p in the
+// upper half of bmp[p / 2] when p is odd).  Returns the largest magnitude over
+// the lane's slots, non-finite included (the caller takes the finite maximum
+// apart when that is non-finite).  Straight-line code; the re-read slots go
+// first, so that their registers are free before the LDS entries are read.
+template <int RS, class S, int... P>
+__device__ __forceinline__ uint32_t block_maxima(const S& slots, bool odd, uint32_t (&bmp)[kMaxSlots / 4],
+                                                 std::integer_sequence<int, P...>) {
+  uint32_t acc = 0u;
+#pragma unroll
+  for (int k = 0; k < kMaxSlots / 4; ++k) bmp[k] = 0u;
+  auto one = [&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    const uint32_t m0 = slot_max16(slots.template get<2 * p>());
+    const uint32_t m1 = slot_max16(slots.template get<2 * p + 1>());
+    acc = max(acc, max(m0, m1));
+    const uint32_t own = odd ? m1 : m0, give = odd ? m0 : m1;
+    const uint32_t bm = max(own, dpp_u32<kQuadXor1>(give));
+    bmp[p >> 1] |= (p & 1) ? bm << 16 : bm;   // (pairs are visited out of order)
+    // (one pair at a time: interleaving them only lengthens live ranges)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int kFirstReread = RS + kLdsSlots;
+  auto reread = [&](auto pc) { if constexpr (2 * decltype(pc)::value >= kFirstReread) one(pc); };
+  auto in_regs = [&](auto pc) { if constexpr (2 * decltype(pc)::value + 1 < RS) one(pc); };
+  auto rest = [&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (!(2 * p >= kFirstReread) && !(2 * p + 1 < RS)) one(pc);
+  };
+  (reread(std::integral_constant<int, P>{}), ...);
+  (in_regs(std::integral_constant<int, P>{}), ...);
+  (rest(std::integral_constant<int, P>{}), ...);
+  // (the packed words are formed here: left to itself the compiler carries
+  // the 32 halves into phase 2 and spills them)
+#pragma unroll
+  for (int k = 0; k < kMaxSlots / 4; ++k) asm volatile("" : "+v"(bmp[k]));
+  return acc;
+}
+
+// Largest finite magnitude (16-bit pattern) over a lane's slots, read again
+// from the input: the rare case of a lane holding a non-finite value.
+__device__ __forceinline__ uint32_t lane_finite_max16(const uint16_t* wg_x, int wbase, int lane, int nres,
+                                                   uint32_t n_valid) {
+  uint32_t acc = 0u;
+  for (int j = 0; j < nres; ++j) {
+    const uint32_t ls = slot_of(wbase, j, lane);
+    if (ls < n_valid) {
+      const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
+      const uint4 w = make_uint4(a.x, a.y, a.z, a.w);
+      acc = max(acc, finite_max16(w, slot_max16(w)));
+    }
+  }
+  return acc;
 }
 
 // Tensor maximum (finite bf16 magnitudes, as an fp32 bit pattern) from a scan
@@ -263,7 +347,7 @@ template <bool GUARD>
 __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(QuantLaunch q, int nres, unsigned char* ws,
                                                                      uint32_t epoch) {
   __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 36,864 bytes (four workgroups per CU)
-  __shared__ float2 s_adj[128];   // adjusted multiplier and flag per scale code
+  __shared__ float2 s_adj[256];   // adjusted multiplier and flag per conversion byte
   __shared__ float2 s_br[128];    // brackets of 1 / (s g) per scale code
   __shared__ float2 s_eps[8];     // multiplier adjustment per significand class
   __shared__ uint32_t s_red[kResThreads / 64];
@@ -305,9 +389,11 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(slot_ptr(wg_x, slot_of(wbase, j, lane))),
                                        (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
   }
-  // the re-read slots: all loads in flight before the first use (a use
-  // between loads would wait for every load issued before it)
+  // the re-read slots: all loads in flight before the first use (with
+  // global->LDS loads in flight, the first use of a loaded register waits for
+  // every load issued)
   uint32_t acc = 0u;
+  uint32_t bmp[kMaxSlots / 4];
   {
     constexpr int kScan = reread_slots<GUARD>();
     uint4 sc[kScan];
@@ -315,17 +401,25 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     for (int k = 0; k < kScan; ++k) {
       const int j = kRegSlots + kLdsSlots + k;
       const uint32_t ls = slot_of(wbase, j, lane);
-      sc[k] = load_cached(wg_x, ls, (!GUARD || j < nres) && ls < n_valid);
+      if constexpr (GUARD) {
+        sc[k] = load_cached(wg_x, ls, j < nres && ls < n_valid);
+      } else {
+        // (unconditional: a load under a branch makes the compiler wait for
+        // every load before it)
+        const u32x4_t a = load16<false>(slot_ptr(wg_x, ls));
+        sc[k] = make_uint4(a.x, a.y, a.z, a.w);
+      }
     }
-#pragma unroll
-    for (int k = 0; k < kScan; ++k) acc = max(acc, raw_finite_absmax(sc[k]));
+    // (nothing scheduled above this point: an early use would stop the issue)
+    __builtin_amdgcn_sched_barrier(0);
+    // a wave reads only the LDS entries its own loads wrote: the wait for its
+    // loads suffices
+    __builtin_amdgcn_s_waitcnt(0);
+    const Phase1Slots<GUARD, kRegSlots, kScan> slots{r, s_data, sc, wbase, lane, tid, nres, n_valid};
+    acc = block_maxima<kRegSlots>(slots, (lane & 1) != 0, bmp, std::make_integer_sequence<int, kMaxSlots / 2>{});
   }
-  acc = max(acc, reg_slots_absmax(r, std::make_integer_sequence<int, kRegSlots>{}));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
-    if (slot_of(wbase, j, lane) < n_valid) acc = max(acc, raw_finite_absmax(s_data[(j - kRegSlots) * kResThreads + tid]));
-  }
+  if (acc >= 0x7F80u) acc = lane_finite_max16(wg_x, wbase, lane, nres, n_valid);
+  acc <<= 16;   // fp32 bit pattern
   acc = wave_max_u32(acc);
   if (lane == 0) s_red[wv] = acc;
   __syncthreads();
@@ -370,7 +464,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
 
   NvCtx cx;
   nv_context(as_f(amax_bits), false, cx);
-  nv_fill_adjusted_table(s_adj, s_br, s_eps, cx, tid);
+  nv_fill_adjusted_table<256>(s_adj, s_br, s_eps, cx, tid);
   if (tid == 0) {
     s_amax = amax_bits;
     if (blockIdx.x == (unsigned)G - 1u && q.global_scale) *q.global_scale = cx.g;
@@ -401,7 +495,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
                    wbase, lane2, nres, n_valid, odd, 0u};
   SlotSource<GUARD> src{r, s_data, pre, wg_x, wbase, lane2, wv * 64 + lane2, nres, n_valid};
   static_assert(kMaxSlots % 2 == 0, "slot rows are encoded in pairs");
-  encode_pairs(p2, src, std::make_integer_sequence<int, kMaxSlots / 2>{});
+  encode_pairs(p2, src, bmp, std::make_integer_sequence<int, kMaxSlots / 2>{});
   // Exact recomputations, after this thread's fast stores (program order per
   // address keeps the exact values last).  The context is rebuilt from LDS so
   // that phase 2 keeps only the two bracket factors in registers.  With
@@ -416,7 +510,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     xscale = 0x1p100f;
     nv_context_g(cf.g * xscale, cf);
     __syncthreads();
-    nv_fill_adjusted_table(s_adj, s_br, s_eps, cf, tid);
+    nv_fill_adjusted_table<256>(s_adj, s_br, s_eps, cf, tid);
     __syncthreads();
     redo = 0u;
     for (int j = 0; j < nres; ++j) redo |= (slot_of(wbase, j, lane2) < n_valid ? 1u : 0u) << j;

@@ -408,6 +408,22 @@ def test_nv_single_read_full_workgroups():
     _nv_single(x)
 
 
+def test_nv_single_read_full_workgroups_nonfinite():
+    """Full workgroups with NaN and inf planted in slots held in registers, in
+    LDS and re-read from memory, in several workgroups (the block maxima are
+    taken on chip; a lane holding a non-finite value takes its finite maximum
+    apart).  Slot s of a 256-thread workgroup w with 32 slots per thread is
+    flat slot 8192 w + 2048 wave + 64 j + lane (8 elements each)."""
+    x = workloads.random_tensor(4096, 16384, "bf16", 78, scale=2.0)
+    flat = x.reshape(-1)
+    plant = [(5, 2, 3, 7, 0x7FC0), (100, 1, 20, 40, 0x7F80), (700, 3, 29, 63, 0xFF80),
+             (1023, 0, 31, 0, 0xFFC1), (400, 0, 16, 1, 0x7F80), (401, 3, 17, 62, 0x7FC0)]
+    for wg, wave, j, lane, bits in plant:
+        slot = 8192 * wg + 2048 * wave + 64 * j + lane
+        flat[slot * 8 + (wg % 8)] = bits
+    _nv_single(x)
+
+
 def test_nv_single_read_specials_and_ties():
     _nv_single(_special_tensor("bf16"))
     mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
