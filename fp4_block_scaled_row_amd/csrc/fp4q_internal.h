@@ -34,12 +34,16 @@ struct QuantLaunch {
 
 constexpr int kAmaxPartialsMax = 1024;  // workgroups of the NV amax pass
 // NVFP4 workspace layout (bytes): [0, 64) header of the single-launch kernel
-// (word 1: tensor max, word 2: wait limit override), [64, 64 + 8 * 1024) its
+// (word 2: wait limit override), [64, 64 + 8 * 1024) its
 // per-workgroup flags, [8256, 8256 + 4 * 1024) the amax partials of the
-// two-pass kernels.
+// two-pass kernels, [16384, 16384 + 4096 * 16) sixteen copies of the result
+// word of the single-launch kernel, 4 KiB apart.
 constexpr size_t kWsFlagsOffsetBytes = 64;
 constexpr size_t kWsPartialsOffsetBytes = kWsFlagsOffsetBytes + 8 * kAmaxPartialsMax;
-constexpr size_t kNvWorkspaceBytes = 16384;
+constexpr size_t kWsResultsOffsetBytes = 16384;
+constexpr size_t kWsResultStrideBytes = 4096;
+constexpr int kWsResultCopies = 16;
+constexpr size_t kNvWorkspaceBytes = kWsResultsOffsetBytes + kWsResultStrideBytes * kWsResultCopies;
 
 hipError_t launch_zero_counters(unsigned long long* counters, hipStream_t s);
 hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t s);

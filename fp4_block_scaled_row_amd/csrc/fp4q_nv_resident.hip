@@ -12,9 +12,10 @@
 //           maximum (cached loads, so that phase 2 finds them closer);
 //  barrier  every workgroup publishes (epoch, chunk max) in a 64-bit flag of
 //           its own; the last workgroup polls all flags in parallel, folds the
-//           maxima and publishes (epoch, tensor max) in one word the others
-//           poll -- no contended counter, relaxed atomics only (each word
-//           carries its own payload);
+//           maxima and writes (epoch, tensor max) into sixteen copies of a
+//           result word, 4 KiB apart, each polled by a sixteenth of the
+//           workgroups -- no contended counter and no single hot word,
+//           relaxed atomics only (each word carries its own payload);
 //  phase 2  codes and scales from the on-chip slots, then from the re-read
 //           slots (prefetched ahead), in straight-line code; slots that need
 //           the exact path are recomputed at the end.
@@ -323,9 +324,10 @@ __device__ uint32_t scan_tensor_amax(const QuantLaunch& q, uint32_t* s_red) {
 // limit is 1 ms of the 100 MHz counter unless *limit_word is nonzero (tests
 // set it to a few ticks to drive the fallback scan); it is read only once a
 // wait has begun, so its latency hides inside the wait.  The pause between
-// polls doubles up to about 0.4 us: every poll reaches the device-wide
-// coherence point, and a thousand waiting workgroups polling flat out would
-// slow down the ones still streaming their input.
+// polls doubles up to MAXPAUSE sleeps of 64 cycles: every poll reaches the
+// device-wide coherence point, and workgroups polling flat out would slow
+// down the ones still streaming their input.
+template <int MAXPAUSE>
 __device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, const uint64_t* limit_word, uint64_t& f) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -335,7 +337,7 @@ __device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, co
   int pause = 1;
   for (int it = 0; it < kSpinLimit; ++it) {
     for (int k = 0; k < pause; ++k) __builtin_amdgcn_s_sleep(1);
-    pause = pause < 16 ? 2 * pause : 16;
+    pause = pause < MAXPAUSE ? 2 * pause : MAXPAUSE;
     f = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(f >> 32) == epoch) return true;
     if (__builtin_amdgcn_s_memrealtime() - t0 > limit) return false;
@@ -356,8 +358,10 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
   const int G = gridDim.x;
-  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);   // [1] tensor max word, [2] wait limit override
+  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);   // [2] wait limit override
   uint64_t* flags = reinterpret_cast<uint64_t*>(ws + kWsFlagsOffsetBytes);   // one per workgroup
+  constexpr int kResultWords = (int)(kWsResultStrideBytes / 8);
+  uint64_t* results = reinterpret_cast<uint64_t*>(ws + kWsResultsOffsetBytes);   // kWsResultCopies copies
   const int64_t chunk = (int64_t)kResThreads * nres;
   const int64_t base = (int64_t)blockIdx.x * chunk;
   const int64_t rem = q.nslots - base;
@@ -438,7 +442,8 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     uint32_t m = 0u;
     for (int i = tid; i < G; i += kResThreads) {
       uint64_t f = 0;
-      if (!wait_epoch(flags + i, epoch, hdr + 2, f)) s_timeout = 1u;
+      // (the master polls briskly: its wait is the critical path)
+      if (!wait_epoch<2>(flags + i, epoch, hdr + 2, f)) s_timeout = 1u;
       m = max(m, (uint32_t)f);
     }
     m = wave_max_u32(m);
@@ -449,13 +454,16 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
 #pragma unroll
     for (int w = 0; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
     if (s_timeout) m = scan_tensor_amax(q, s_red);
-    if (tid == 0) __hip_atomic_store(hdr + 1, ((uint64_t)epoch << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t word = ((uint64_t)epoch << 32) | m;
+    if (tid < kWsResultCopies)
+      __hip_atomic_store(results + (size_t)tid * kResultWords, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     amax_bits = m;
   } else {
     __syncthreads();   // s_red is reused below
     if (tid == 0) {
       uint64_t f = 0;
-      if (wait_epoch(hdr + 1, epoch, hdr + 2, f)) s_red[0] = (uint32_t)f;
+      const uint64_t* mine = results + (size_t)(blockIdx.x % kWsResultCopies) * kResultWords;
+      if (wait_epoch<4>(mine, epoch, hdr + 2, f)) s_red[0] = (uint32_t)f;
       else s_timeout = 1u;
     }
     __syncthreads();

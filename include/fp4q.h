@@ -121,15 +121,16 @@ typedef struct {
 } fp4q_outputs;
 
 /* Bytes of device workspace a quantize call needs (0 if none).  The NVFP4
- * workspace (16 KiB) belongs to the caller, must be zero-filled before its
+ * workspace (80 KiB) belongs to the caller, must be zero-filled before its
  * first use and is then kept consistent by the library; calls that share one
  * workspace must be ordered (same stream, or synchronised).  Layout: bytes
- * [8, 16) the tensor-maximum word of the single-read kernel, [16, 24) an
+ * [16, 24) an
  * optional wait limit of that kernel's grid-wide exchange in ticks of the
  * 100 MHz GPU clock (0: 1 ms; a small value makes every wait run out and the
  * kernel fall back to scanning the tensor itself, which tests use), [64,
  * 8256) per-workgroup flags, [8256, 12352) the per-workgroup maxima of the
- * two-pass kernels. */
+ * two-pass kernels, [16384, 81920) sixteen copies of the single-read
+ * kernel's result word, 4 KiB apart. */
 size_t fp4q_workspace_bytes(const fp4q_quant_args *args);
 
 /* MXFP4 quantization of x ([rows][in_row_stride] of in_dtype).  block_size
