@@ -623,7 +623,7 @@ __device__ __forceinline__ uint32_t slot_max16(const uint4& w) {
 // (flagged); a finite block never gets one, since its quotient stays below
 // 448 (1 + 2^-21), far from the overflow point 464.
 __device__ __forceinline__ void nv_fast_pair(const NvCtx& cx, const float2* s_adj, const uint4& w0, const uint4& w1,
-                                             float bamax, bool odd, uint32_t& codes0, uint32_t& codes1,
+                                             float bamax, uint32_t& codes0, uint32_t& codes1,
                                              uint32_t& scale, uint32_t& need) {
   // (the old operand of a packing conversion only fills bytes that are
   // overwritten or ignored: a dead value avoids a register copy)
@@ -634,8 +634,8 @@ __device__ __forceinline__ void nv_fast_pair(const NvCtx& cx, const float2* s_ad
   // tell them apart (bit 8 and bit 0 of sb2, both moved to bit 31)
   need = (__builtin_amdgcn_alignbit(sb2, sb2, 9) ^ (sb2 << 31)) | as_u(mf.y);
   scale = sb2;
-  const float sw = as_f(dpp_u32<kQuadXor1>(as_u(mf.x)));
-  const float ma = odd ? sw : mf.x, mb = odd ? mf.x : sw;
+  // the multiplier of block A (worked out by the even lane) and of block B
+  const float ma = as_f(dpp_u32<kQuadEven>(as_u(mf.x))), mb = as_f(dpp_u32<kQuadOdd>(as_u(mf.x)));
   const float one = e8m0_operand(127u);
   uint32_t ca = 0u, cb = 0u;
 #define FP4Q_PAIR(C, M, K, WK)                                                                    \

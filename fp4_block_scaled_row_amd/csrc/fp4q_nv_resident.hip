@@ -138,7 +138,7 @@ struct Phase2 {
       v1 = j + 1 < nres && slot_of(wbase, j + 1, lane) < n_valid;
     }
     uint32_t c0, c1, sc, nd;
-    nv_fast_pair(cx, s_adj, w0, w1, bamax, odd, c0, c1, sc, nd);
+    nv_fast_pair(cx, s_adj, w0, w1, bamax, c0, c1, sc, nd);
     // codes non-temporal: they stream out during the encode instead of piling
     // up as dirty L2 lines that drain after it (scale bytes stay cached: their
     // partial lines are better merged in L2)
