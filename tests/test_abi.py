@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 from fp4_block_scaled_row_amd import _lib
@@ -185,3 +186,17 @@ def test_empty_tensors_are_no_ops():
     assert lib.fp4q_fwht(0, 64, 64, 1, None, None, 64, 0, 0, None) == _lib.FP4Q_OK
     assert lib.fp4q_quantize_mxfp4(_args(rows=0), None, _lib.Outputs(None, None, None, None, None, None),
                                    None, 0, None) == _lib.FP4Q_OK
+
+
+def test_tensor_scale_product_equals_quotient():
+    """The single-read kernel forms g = RN32(amax / 2688) as RN32(RN64(amax * RN64(1/2688))):
+    the two agree for every positive finite bf16 amax and for a seeded sample of fp32 amax
+    (the quotient is never within 2^-30 of an fp32 rounding boundary unless exact)."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint32) << 16
+    rng = np.random.default_rng(5)
+    more = rng.integers(1, 0x7F800000, size=1 << 20, dtype=np.uint32)
+    for b in (bits, more):
+        a = b.view(np.float32).astype(np.float64)
+        q = (a / 2688.0).astype(np.float32)
+        p = (a * (1.0 / 2688.0)).astype(np.float32)
+        assert np.array_equal(q.view(np.uint32), p.view(np.uint32))
