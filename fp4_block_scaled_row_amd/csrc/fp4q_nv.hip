@@ -264,6 +264,101 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   if constexpr (COUNT) flush_counters(q.counters, n_sat, n_und, n_nf);
 }
 
+// Streaming max->6 round-to-nearest encode of contiguous bf16 (no rotation,
+// no counters): the paired encode of the single-read kernel without its
+// on-chip phase.  A wave takes four 64-slot tiles per iteration, two pairs
+// of tiles; lanes 2k and 2k+1 hold block k of both tiles of a pair, the even
+// lane works out the first tile's block scale and the odd lane the second's
+// (nv_fast_pair).  Blocks that need the exact path are redone at the end of
+// each iteration (program order per address keeps the exact values last);
+// with g < 2^-100 every block is, on inputs and g scaled by 2^100.
+__global__ __launch_bounds__(kThreads) void nv_fast_kernel(QuantLaunch q, int npartials) {
+  __shared__ float2 s_adj[256];
+  __shared__ float2 s_br[128];
+  __shared__ float2 s_eps[8];
+  __shared__ uint32_t s_red[kWaves];
+  const int lane = threadIdx.x & 63;
+  uint32_t amax_bits;
+  if (q.global_amax) {
+    amax_bits = as_u(fabsf(*q.global_amax));
+  } else {
+    uint32_t m = 0u;
+    for (int i = threadIdx.x; i < npartials; i += kThreads) m = max(m, q.partials[i]);
+    m = wave_max_u32(m);
+    if (lane == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, s_red[w]);
+    amax_bits = m;
+  }
+  NvCtx cx;
+  nv_context(as_f(amax_bits), false, cx);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
+  const bool exact_all = cx.exact_all;
+  float xscale = 1.0f;
+  if (exact_all) {
+    xscale = 0x1p100f;
+    nv_context_g(cx.g * xscale, cx);
+  }
+  nv_fill_adjusted_table<256>(s_adj, s_br, s_eps, cx, threadIdx.x);
+  __syncthreads();
+
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  const bool odd = (lane & 1) != 0;
+  const uint16_t* xs = static_cast<const uint16_t*>(q.x);
+  for (int64_t grp = wave; grp * 4 < ntiles; grp += nwaves) {
+    const int64_t t0 = grp * 4;
+    uint4 w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t s = ((t0 + r) << 6) + lane;
+      if (s < q.nslots) {
+        const u32x4_t a = load16<true>(xs + (s << 3));
+        w[r] = make_uint4(a.x, a.y, a.z, a.w);
+      } else {
+        w[r] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    uint32_t redo = 0u;   // bit r: this lane's slot in tile t0 + r is redone
+    if (exact_all) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) redo |= ((((t0 + r) << 6) + lane) < q.nslots ? 1u : 0u) << r;
+    } else {
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint4 w0 = w[2 * p], w1 = w[2 * p + 1];
+        const uint32_t m0 = slot_max16(w0), m1 = slot_max16(w1);
+        const uint32_t own = odd ? m1 : m0, give = odd ? m0 : m1;
+        const uint32_t bm = max(own, dpp_u32<kQuadXor1>(give));
+        uint32_t c0, c1, sc, nd;
+        nv_fast_pair(cx, s_adj, w0, w1, as_f(bm << 16), c0, c1, sc, nd);
+        const int64_t s0 = ((t0 + 2 * p) << 6) + lane, s1 = s0 + 64;
+        if (s0 < q.nslots) __builtin_nontemporal_store(c0, reinterpret_cast<uint32_t*>(q.codes) + s0);
+        if (s1 < q.nslots) __builtin_nontemporal_store(c1, reinterpret_cast<uint32_t*>(q.codes) + s1);
+        // the block this lane worked out: tile t0 + 2p + odd, block lane / 2
+        const int64_t tb = t0 + 2 * p + (odd ? 1 : 0);
+        if ((tb << 6) + (lane & ~1) < q.nslots) q.scales[(tb << 5) + (lane >> 1)] = (uint8_t)sc;
+        mine |= (nd >> 31) << (2 * p);
+      }
+      // slot r of a lane belongs to the block its pair worked out in the even
+      // lane (r even) or the odd lane (r odd)
+      const uint32_t other = dpp_u32<kQuadXor1>(mine);
+      redo = odd ? (other | (mine << 1)) : (mine | (other << 1));
+    }
+    while (redo != 0u) {
+      const int r = __builtin_ctz(redo);
+      redo &= redo - 1u;
+      const int64_t s = ((t0 + r) << 6) + lane;
+      const u32x4_t a = load16<false>(xs + ((s & ~(int64_t)1) << 3)), b = load16<false>(xs + ((s | 1) << 3));
+      nv_fix_slot_fma(q, cx, s_br, xscale, s, a, b);
+    }
+  }
+}
+
 int amax_grid(int64_t nslots) {
   const int64_t ntiles = (nslots + 63) >> 6;
   int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
@@ -288,7 +383,12 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
-  hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, POL, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
+  if constexpr (IN == kBF16 && ROT == kRotNone && !SR && POL == kPolMax6 && !COUNT && CONTIG) {
+    static_assert(kUnroll == 4, "nv_fast_kernel takes four tiles per wave iteration");
+    hipLaunchKernelGGL(nv_fast_kernel, dim3(grid), dim3(kThreads), 0, st, q, np);
+  } else {
+    hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, POL, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
+  }
   return hipGetLastError();
 }
 

@@ -54,35 +54,6 @@ constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// The context of round-to-nearest max->6 quantization (g and the bracket
-// factors of 1 / (6 g)) in a short dependency chain: every workgroup computes
-// it between learning the tensor maximum and its first encode.
-//   g = RN32(amax / 2688): amax / 2688 = (M / 21) 2^k with M the 24-bit
-//   significand of amax; that quotient is an fp32 value or lies at least
-//   2^-30 (relative) from every fp32 rounding boundary (a boundary has 25
-//   significant bits, so M / 21 on it would make M a multiple of 21 times a
-//   25-bit odd number), and the fp64 product with RN64(1 / 2688) is within
-//   2^-52 of it: both round to the same fp32 value.
-//   1 / (6 g): the fp64 hardware reciprocal refined by one Newton step
-//   (relative error near 2^-53, against 2^-53 for a division), far inside
-//   the 2^-22 by which the brackets stand off: they remain strict brackets.
-// The fields used here match nv_context(amax, false, ...): g exactly, the
-// brackets up to an ulp.
-__device__ __forceinline__ void nv_context_rne6(float amax, NvCtx& cx) {
-  float g = (amax == 0.0f) ? 1.0f : (float)((double)amax * (1.0 / 2688.0));
-  if (g == 0.0f) g = 0x1p-149f;
-  cx.g = g;
-  cx.g64 = (double)g;
-  cx.mg6 = 6.0 * cx.g64;
-  const double r0 = __builtin_amdgcn_rcp(cx.mg6);
-  cx.inv6 = fma(r0, fma(-cx.mg6, r0, 1.0), r0);
-  cx.inv6_lo = (float)(cx.inv6 * (1.0 - 0x1p-22));
-  cx.inv6_hi = (float)(cx.inv6 * (1.0 + 0x1p-22));
-  cx.mg4 = cx.inv4 = 0.0;   // (Four Over Six only)
-  cx.inv4_lo = cx.inv4_hi = 0.0f;
-  cx.exact_all = !(g >= 0x1p-100f);
-}
-
 // Largest finite bf16 magnitude bit pattern of a raw slot whose raw 16-bit
 // maximum (slot_max16) is mx.
 __device__ __forceinline__ uint32_t finite_max16(const uint4& w, uint32_t mx) {

@@ -402,6 +402,32 @@ def test_nv_single_read_shapes(rows, cols):
     _nv_single(workloads.random_tensor(rows, cols, "bf16", rows + 3 * cols, scale=2.0, dist="t"))
 
 
+def _nv_caller_amax(x):
+    """Contiguous bf16, max->6, RNE, no counters, caller amax: the streaming
+    paired encode."""
+    xd = to_dev(x)
+    amax = oracle.tensor_amax(x)
+    amax_dev = torch.tensor([amax], dtype=torch.float32, device=xd.device)
+    r = fq.quantize_nvfp4(xd, global_amax=amax_dev)
+    c, s, g, _, _ = oracle.quantize_nv(x, global_amax=amax)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales (caller amax)")
+    assert_same(host(r.codes), c, "codes (caller amax)")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 64), (17, 96), (64, 256), (33, 544), (1000, 1024),
+                                       (2048, 4096), (4097, 2048)])
+def test_nv_caller_amax_shapes(rows, cols):
+    _nv_caller_amax(workloads.random_tensor(rows, cols, "bf16", 7 * rows + cols, scale=2.0, dist="t"))
+
+
+def test_nv_caller_amax_specials_and_tiny():
+    _nv_caller_amax(_special_tensor("bf16"))
+    rng = np.random.default_rng(31)
+    for e in (-133, -101, 100):
+        _nv_caller_amax(f32_to_bf16_bits(np.ldexp(rng.standard_t(4, (8, 64)), e).astype(np.float32)))
+
+
 def test_nv_single_read_full_workgroups():
     """64 Mi elements in a shape other than the headline: every workgroup full."""
     x = workloads.random_tensor(4096, 16384, "bf16", 77, scale=2.0)
