@@ -8,17 +8,20 @@
 //  phase 1  each workgroup owns a contiguous chunk of up to 32 sixteen-byte
 //           slots per thread, each wave a contiguous run of them.  The first
 //           reg_slots() go to VGPRs (non-temporal loads), the next kLdsSlots to
-//           LDS (direct global->LDS loads), the rest are only scanned for the
-//           maximum (cached loads, so that phase 2 finds them closer);
+//           LDS (direct global->LDS loads), the rest are loaded only for their
+//           maxima (cached loads, so that phase 2 finds them closer).  Once
+//           the data is in, each lane also keeps the block maxima phase 2
+//           will need (block_maxima);
 //  barrier  every workgroup publishes (epoch, chunk max) in a 64-bit flag of
 //           its own; the last workgroup polls all flags in parallel, folds the
 //           maxima and writes (epoch, tensor max) into sixteen copies of a
 //           result word, 4 KiB apart, each polled by a sixteenth of the
 //           workgroups -- no contended counter and no single hot word,
 //           relaxed atomics only (each word carries its own payload);
-//  phase 2  codes and scales from the on-chip slots, then from the re-read
-//           slots (prefetched ahead), in straight-line code; slots that need
-//           the exact path are recomputed at the end.
+//  phase 2  codes and scales, two slot rows at a time (nv_fast_pair: a lane
+//           pair works out one block scale per lane), from the on-chip slots,
+//           then from the re-read slots (prefetched ahead), in straight-line
+//           code; slots that need the exact path are recomputed at the end.
 //
 // The launch is an ordinary one with at most kResPerCu workgroups per CU.
 // Results never depend on the workgroups being resident together: every wait
@@ -40,8 +43,9 @@ namespace {
 
 constexpr int kResThreads = 256;
 constexpr int kResPerCu = 4;               // workgroups resident per CU
-// slots held in VGPRs: as many as fit in 128 registers without spilling (the
-// bounds-tested variant needs a few more registers of its own)
+// slots held in VGPRs within 128 registers (the bounds-tested variant needs a
+// few more registers of its own; one more slot fits the full variant but
+// measured no faster)
 template <bool GUARD>
 constexpr int reg_slots() { return GUARD ? 15 : 17; }
 constexpr int kLdsSlots = 9;
