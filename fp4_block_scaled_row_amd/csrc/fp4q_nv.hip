@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   constexpr bool kAdj = IN == kBF16 && ROT == kRotNone && !SR;
   __shared__ float2 s_inv[128];
   __shared__ float2 s_adj[kAdj ? 128 : 1];
-  __shared__ float2 s_eps[8];
+  __shared__ float4 s_eps[8];
   __shared__ float s_i4[POL == kPolIf4 ? 128 : 1];
   __shared__ float s_dq[POL == kPolIf4 ? 1024 : 1];
   __shared__ uint32_t s_red[kWaves];
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
 __global__ __launch_bounds__(kThreads) void nv_fast_kernel(QuantLaunch q, int npartials) {
   __shared__ float2 s_adj[256];
   __shared__ float2 s_br[128];
-  __shared__ float2 s_eps[8];
+  __shared__ float4 s_eps[8];
   __shared__ uint32_t s_red[kWaves];
   const int lane = threadIdx.x & 63;
   uint32_t amax_bits;

@@ -146,38 +146,48 @@ __device__ __forceinline__ void nv_fill_inverse_table(float2* s_inv, const NvCtx
 // thread of the workgroup calls this (it synchronises); the workgroup has at
 // least NCODES threads.  Requires g >= 2^-100 for meaningful entries.
 template <int NCODES = 128>
-__device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_br, float2* s_eps, const NvCtx& cx,
+__device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_br, float4* s_eps, const NvCtx& cx,
                                                        int tid) {
   static_assert(NCODES == 128 || NCODES == 256, "one entry per E4M3 code, or per byte value");
   const float flag = as_f(0x80000000u);
   const float g = cx.g;
   if (tid < 64) {
+    // straight-line code: this runs between learning g and the first encode
     const int cls = tid >> 3, k = tid & 7;
     const float sd = 1.0f + 0.125f * (float)cls;
-    const float p = k < 4 ? 0.25f + 0.5f * (float)k : (k == 4 ? 2.5f : (k == 5 ? 3.5f : (k == 6 ? 5.0f : 6.0f)));
-    const bool tie_up = k == 1 || k == 3 || k == 5;
-    float lo = -0x1p-14f, hi = 0x1p-14f;
+    // decision points 0.25 0.75 1.25 1.75 2.5 3.5 5 6, times 4 one per byte
+    const float p = 0.25f * (float)(uint32_t)((0x18140E0A07050301ull >> (8 * k)) & 0xFFu);
+    const bool tie_up = ((0x2Au >> k) & 1u) != 0u;    // 0.75, 1.75, 3.5: the even code is above
     const float ps = p * sd;                           // exact
     const float th = ps * g;
     const float tl = fmaf(ps, g, -th);                 // T = th + tl exactly
     const uint32_t tb = as_u(th);
     const float a = as_f(((tb + 0x7FFFu + ((tb >> 16) & 1u)) >> 16) << 16);   // nearest bf16
     const float diff = (a - th) - tl;
-    if (fabsf(diff) < 0x1p-12f * th) {
-      const float d = diff * __builtin_amdgcn_rcpf(th);
-      if (d > 0.0f || (d == 0.0f && tie_up)) lo = fmaxf(lo, (0x1p-22f - d) * (1.0f - d));
-      else hi = fminf(hi, (-0x1p-22f - d) * (1.0f - d));
-    }
+    const bool near = fabsf(diff) < 0x1p-12f * th;
+    const float d = diff * __builtin_amdgcn_rcpf(th);
+    const bool up = d > 0.0f || (d == 0.0f && tie_up);
+    const float lc = (0x1p-22f - d) * (1.0f - d), hc = (-0x1p-22f - d) * (1.0f - d);
+    float lo = -0x1p-14f, hi = 0x1p-14f;
+    if (near && up && lc > lo) lo = lc;                // (selects: no NaN can occur)
+    if (near && !up && hc < hi) hi = hc;
     // fold the 8 consecutive lanes of this class: quad exchanges, then the
     // mirror within each half-row pairs quad 0 with quad 1
-    lo = fmaxf(lo, dpp_xor1_f(lo));
-    hi = fminf(hi, dpp_xor1_f(hi));
-    lo = fmaxf(lo, dpp_xor2_f(lo));
-    hi = fminf(hi, dpp_xor2_f(hi));
-    lo = fmaxf(lo, as_f(dpp_u32<kRowHalfMirror>(as_u(lo))));
-    hi = fminf(hi, as_f(dpp_u32<kRowHalfMirror>(as_u(hi))));
-    if (k == 0)
-      s_eps[cls] = (lo + 0x1p-21f <= hi - 0x1p-21f) ? make_float2(0.5f * (lo + hi), 0.0f) : make_float2(0.0f, flag);
+    float t = dpp_xor1_f(lo), u = dpp_xor1_f(hi);
+    lo = t > lo ? t : lo;
+    hi = u < hi ? u : hi;
+    t = dpp_xor2_f(lo), u = dpp_xor2_f(hi);
+    lo = t > lo ? t : lo;
+    hi = u < hi ? u : hi;
+    t = as_f(dpp_u32<kRowHalfMirror>(as_u(lo))), u = as_f(dpp_u32<kRowHalfMirror>(as_u(hi)));
+    lo = t > lo ? t : lo;
+    hi = u < hi ? u : hi;
+    if (k == 0) {
+      // the class's reciprocal, computed beside the folds
+      const float inv = 1.0f / (sd * g);
+      s_eps[cls] = (lo + 0x1p-21f <= hi - 0x1p-21f) ? make_float4(0.5f * (lo + hi), 0.0f, inv, 0.0f)
+                                                    : make_float4(0.0f, flag, inv, 0.0f);
+    }
   }
   __syncthreads();
   if (tid < NCODES) {
@@ -187,8 +197,11 @@ __device__ __forceinline__ void nv_fill_adjusted_table(float2* s_adj, float2* s_
       adj = make_float2(0.0f, 0.0f);
     } else if (c < 127u) {
       const float sd = e4m3_value(c);
-      const float2 e = s_eps[(as_u(sd) >> 20) & 7u];   // significand class of s_c
-      const float inv = 1.0f / (sd * g);
+      const float4 e = s_eps[(as_u(sd) >> 20) & 7u];   // significand class of s_c
+      // s_c = 2^k sigma with sigma the class significand: RN(1 / RN(s_c g)) is
+      // 2^-k RN(1 / RN(sigma g)) while no product or quotient leaves the
+      // normal range (g >= 2^-100; the table is not used otherwise)
+      const float inv = cx.exact_all ? 1.0f / (sd * g) : __builtin_ldexpf(e.z, 127 - (int)(as_u(sd) >> 23));
       br = make_float2(inv * (1.0f - 0x1p-22f), inv * (1.0f + 0x1p-22f));
       adj = make_float2(inv * (1.0f + e.x), e.y);
     }

@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 36,864 bytes (four workgroups per CU)
   __shared__ float2 s_adj[256];   // adjusted multiplier and flag per conversion byte
   __shared__ float2 s_br[128];    // brackets of 1 / (s g) per scale code
-  __shared__ float2 s_eps[8];     // multiplier adjustment per significand class
+  __shared__ float4 s_eps[8];     // multiplier adjustment per significand class
   __shared__ uint32_t s_red[kResThreads / 64];
   __shared__ uint32_t s_timeout;
   __shared__ uint32_t s_amax;
