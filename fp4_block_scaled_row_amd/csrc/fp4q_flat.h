@@ -85,12 +85,13 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool od
       v[i + h] = a - b;
     }
   }
+  // (the even lane takes v + p, the odd lane p - v: one FMA with a sign)
+  const float sg1 = odd_lane ? -1.0f : 1.0f;
+  float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = dpp_xor1_f(v[i]);
-    v[i] = odd_lane ? (p - v[i]) : (v[i] + p);
-    v[i] *= 0.25f;
-  }
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor1_f(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(sg1, v[i], p[i]) * 0.25f;
 }
 
 // Partner value across lane bit 2 (xor 4) or bit 3 (xor 8) within a row of
@@ -120,19 +121,29 @@ __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
       v[i + h] = a - b;
     }
   }
-  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0, b2 = (lane & 4) != 0, b3 = (lane & 8) != 0;
+  // the lower member of a pair takes v + p, the upper p - v: one FMA with a
+  // per-lane sign (s v is exact, so it rounds as the sum or difference);
+  // stage by stage over the 8 elements, so that no exchange waits on the
+  // element it follows
+  const float s0 = (lane & 1) ? -1.0f : 1.0f, s1 = (lane & 2) ? -1.0f : 1.0f;
+  const float s2 = (lane & 4) ? -1.0f : 1.0f, s3 = (lane & 8) ? -1.0f : 1.0f;
+  float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float p = dpp_xor1_f(v[i]);
-    v[i] = b0 ? (p - v[i]) : (v[i] + p);
-    p = dpp_xor2_f(v[i]);
-    v[i] = b1 ? (p - v[i]) : (v[i] + p);
-    p = dpp_xor_hi_f<4>(v[i]);
-    v[i] = b2 ? (p - v[i]) : (v[i] + p);
-    p = dpp_xor_hi_f<8>(v[i]);
-    v[i] = b3 ? (p - v[i]) : (v[i] + p);
-    v[i] *= c;
-  }
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor1_f(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(s0, v[i], p[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor2_f(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(s1, v[i], p[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor_hi_f<4>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(s2, v[i], p[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor_hi_f<8>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(s3, v[i], p[i]) * c;
 }
 
 __device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float v[8]) {

@@ -131,11 +131,12 @@ __global__ __launch_bounds__(128) void fwht8192_kernel(FwhtLaunch f, float c) {
           u[r] = a + b;
           u[r + h] = a - b;
         }
-    const bool odd = (l & 1) != 0;
+    // (the even lane takes u + p, the odd lane p - u: one FMA with a sign)
+    const float sg = (l & 1) ? -1.0f : 1.0f;
 #pragma unroll
     for (int r = 0; r < 64; ++r) {
       const float p = dpp_xor1_f(u[r]);
-      u[r] = (odd ? (p - u[r]) : (u[r] + p)) * c;
+      u[r] = fmaf(sg, u[r], p) * c;
     }
     // ---- transpose M -> L
     __syncthreads();
