@@ -263,6 +263,7 @@ fp4q_status fp4q_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return FP4Q_ERR_INVALID_ARG;
   if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP4Q_ERR_UNSUPPORTED;
+  if (K > ((int64_t)1 << 23)) return FP4Q_ERR_UNSUPPORTED;   // 32-bit buffer offsets
   if (M == 0 || N == 0) return FP4Q_OK;
   if (!c || (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales))) return FP4Q_ERR_INVALID_ARG;
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return FP4Q_ERR_UNSUPPORTED;

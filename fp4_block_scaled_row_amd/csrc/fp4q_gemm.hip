@@ -17,10 +17,12 @@
 // four waves (one per SIMD) a 128x128 quarter: 4x4 instructions per 64-K
 // step on 256 accumulator registers, so every operand fetched from LDS feeds
 // four instructions.  K advances 128 per stage: the A and B tiles (256 rows x
-// 64 bytes) and their scale bytes are loaded straight into LDS (direct-to-LDS
-// global loads), into a ring of four stage buffers kept three stages ahead of
-// the one being multiplied; one fence-free barrier per stage, the loads
-// being waited for explicitly.  Workgroups are
+// 64 bytes) and their scale bytes are loaded straight into LDS (buffer loads
+// with the LDS destination: in that form, unlike the flat one, the compiler
+// lets an LDS read wait only for the loads it depends on), into a ring of
+// four stage buffers kept three stages ahead of the one being multiplied;
+// one fence-free barrier per stage, the loads being waited for explicitly.
+// Buffer offsets are 32-bit: K is at most 2^23.  Workgroups are
 // numbered so that each XCD walks a contiguous range of C tiles, in groups of
 // 8 tile rows traversed column by column, so that the workgroups resident on
 // one XCD at a time share both A row tiles and B column tiles in its L2.
@@ -52,6 +54,20 @@ constexpr int kLoadsPerStage = 2 * (kCodeBytes / 1024 / 4) + 2;   // per lane: 4
 
 __device__ __forceinline__ int chunk_of(int row, int part) { return part ^ ((row >> 1) & 3); }
 
+// Direct-to-LDS loads through a buffer descriptor at base (bytes long), of 16
+// or 4 bytes per lane: lane l writes lds + 16 l (4 l); off is this lane's
+// byte offset from base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
+}
+__device__ __forceinline__ void buf_lds16(const uint8_t* base, int64_t bytes, lds_void_t* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base, bytes), lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void buf_lds4(const uint8_t* base, int64_t bytes, lds_void_t* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base, bytes), lds, 4, off, 0, 0, 0);
+}
+
 // s_waitcnt with vmcnt <= n (expcnt and lgkmcnt not waited for)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -82,6 +98,12 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
   const int64_t kb = g.K / 2, ksb = g.K / 32;
   const int nstage = (int)(g.K / kKStep);
   // rows past M or N read a valid row instead; their results are not stored
+  // buffer bases at the tile's first row; offsets below 256 kb + kb < 2^31
+  const uint8_t* a_c = g.a_codes + m0 * kb;
+  const uint8_t* b_c = g.b_codes + n0 * kb;
+  const uint8_t* a_s = g.a_scales + m0 * ksb;
+  const uint8_t* b_s = g.b_scales + n0 * ksb;
+  const int64_t na_c = (g.M - m0) * kb, nb_c = (g.N - n0) * kb, na_s = (g.M - m0) * ksb, nb_s = (g.N - n0) * ksb;
   auto issue = [&](int st, uint8_t* buf) {
     const int64_t kbyte = (int64_t)st * kRowBytes;
 #pragma unroll
@@ -89,18 +111,14 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
       const int region = wv * (kCodeBytes / 1024 / 4) + i;   // 16 rows x 64 bytes
       const int row = region * 16 + (lane >> 2);
       const int part = chunk_of(row, lane & 3);
-      const int64_t ra = min(m0 + row, g.M - 1), rb = min(n0 + row, g.N - 1);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.a_codes + ra * kb + kbyte + part * 16),
-                                       (lds_void_t*)(buf + region * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.b_codes + rb * kb + kbyte + part * 16),
-                                       (lds_void_t*)(buf + kCodeBytes + region * 1024), 16, 0, 0);
+      const int64_t ra = min(m0 + row, g.M - 1) - m0, rb = min(n0 + row, g.N - 1) - n0;
+      buf_lds16(a_c, na_c, (lds_void_t*)(buf + region * 1024), (int)(ra * kb + kbyte + part * 16));
+      buf_lds16(b_c, nb_c, (lds_void_t*)(buf + kCodeBytes + region * 1024), (int)(rb * kb + kbyte + part * 16));
     }
     const int row = wv * 64 + lane;
-    const int64_t ra = min(m0 + row, g.M - 1), rb = min(n0 + row, g.N - 1);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.a_scales + ra * ksb + (int64_t)st * 4),
-                                     (lds_void_t*)(buf + 2 * kCodeBytes + wv * 256), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(g.b_scales + rb * ksb + (int64_t)st * 4),
-                                     (lds_void_t*)(buf + 2 * kCodeBytes + kTile * 4 + wv * 256), 4, 0, 0);
+    const int64_t ra = min(m0 + row, g.M - 1) - m0, rb = min(n0 + row, g.N - 1) - n0;
+    buf_lds4(a_s, na_s, (lds_void_t*)(buf + 2 * kCodeBytes + wv * 256), (int)(ra * ksb + (int64_t)st * 4));
+    buf_lds4(b_s, nb_s, (lds_void_t*)(buf + 2 * kCodeBytes + kTile * 4 + wv * 256), (int)(rb * ksb + (int64_t)st * 4));
   };
 
   const int wr = wv >> 1, wc = wv & 1;
@@ -112,13 +130,12 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute = [&](const uint8_t* buf) {
+  // a stage's operands, both 64-K steps
+  v8i_t a[2][kSub], b[2][kSub];
+  int sa[2][kSub], sb[2][kSub];
+  auto read = [&](const uint8_t* buf) {
     const uint32_t* sa_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes);
     const uint32_t* sb_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes + kTile * 4);
-    // both 64-K steps' operands are read up front, so the second step's
-    // reads complete under the first step's matrix instructions
-    v8i_t a[2][kSub], b[2][kSub];
-    int sa[2][kSub], sb[2][kSub];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int part = 2 * kk + (lane >> 5);   // this lane's 32 K positions of the 64-K step
@@ -134,34 +151,41 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
         sb[kk][u] = (int)((sb_row[brow] >> (8 * part)) & 0xFFu);
       }
     }
+  };
+  auto mma = [&](int kk) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int i = 0; i < kSub; ++i)
 #pragma unroll
-      for (int i = 0; i < kSub; ++i)
-#pragma unroll
-        for (int j = 0; j < kSub; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[kk][j], acc[i][j], 4, 4, 0,
-                                                                      sa[kk][i], 0, sb[kk][j]);
+      for (int j = 0; j < kSub; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk][i], b[kk][j], acc[i][j], 4, 4, 0,
+                                                                    sa[kk][i], 0, sb[kk][j]);
   };
   // one pipeline step: wait for this thread's loads of stage st (stages
   // st + 1 and st + 2 stay in flight), one barrier -- after it every wave's
   // loads of stage st are in LDS and every wave is done with stage st - 1 --
-  // then refill stage st - 1's buffer with stage st + 3 and compute stage st.
-  // The barrier carries no memory fence: the loads are waited for explicitly.
+  // then read stage st's operands, multiply the first 64-K step (its operands
+  // arrive first), refill stage st - 1's buffer with stage st + 3 and
+  // multiply the second step.  Every LDS read of the step is issued before
+  // the refill, so none of them waits for it.  The barrier carries no memory
+  // fence: the loads are waited for explicitly.
   auto step = [&](int st, uint8_t* cur, uint8_t* fill) {
     if (st + 2 < nstage) wait_vm<2 * kLoadsPerStage>();
     else if (st + 1 < nstage) wait_vm<kLoadsPerStage>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
+    read(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
     if (st + 3 < nstage) issue(st + 3, fill);
-    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
   };
 
   if (nstage > 0) issue(0, s_st0);
   if (nstage > 1) issue(1, s_st1);
   if (nstage > 2) issue(2, s_st2);
-  // unrolled over two rotations of the ring: the compiler orders the first
-  // read of an iteration after every load in flight, once per iteration
+  // (unrolled over two rotations of the ring)
   for (int st = 0; st < nstage; st += 8) {
     step(st, s_st0, s_st3);
     if (st + 1 < nstage) step(st + 1, s_st1, s_st0);

@@ -7,11 +7,12 @@
 //
 //  phase 1  each workgroup owns a contiguous chunk of up to 32 sixteen-byte
 //           slots per thread, each wave a contiguous run of them.  The first
-//           reg_slots() go to VGPRs (non-temporal loads), the next kLdsSlots to
-//           LDS (direct global->LDS loads), the rest are loaded only for their
-//           maxima (cached loads, so that phase 2 finds them closer).  Once
-//           the data is in, each lane also keeps the block maxima phase 2
-//           will need (block_maxima);
+//           reg_slots() stay in VGPRs, the next kLdsSlots go to LDS (both
+//           non-temporal loads into VGPRs; the LDS-bound ones are issued first
+//           and written to LDS once their maxima are taken), the rest are
+//           loaded only for their maxima (cached loads, so that phase 2 finds
+//           them closer).  Each lane folds the block maxima phase 2 will need
+//           as its loads land (block_maxima);
 //  barrier  every workgroup publishes (epoch, chunk max) in a 64-bit flag of
 //           its own; the last workgroup polls all flags in parallel, folds the
 //           maxima and writes (epoch, tensor max) into sixteen copies of a
@@ -56,7 +57,6 @@ constexpr int kAhead = 4;                                      // re-read prefet
 constexpr uint64_t kWaitTicks = 100000;    // 1 ms of the 100 MHz real-time counter (default)
 constexpr int kSpinLimit = 1 << 24;        // backstop on the number of polls
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Largest finite bf16 magnitude bit pattern of a raw slot whose raw 16-bit
 // maximum (slot_max16) is mx.
@@ -86,13 +86,14 @@ __device__ __forceinline__ uint32_t slot_of(int wbase, int j, int lane) { return
 
 __device__ __forceinline__ const uint16_t* slot_ptr(const uint16_t* wg_x, uint32_t ls) { return wg_x + (size_t)ls * 8u; }
 
-template <bool GUARD, int RS, int... J>
-__device__ __forceinline__ void load_reg_slots(uint4 (&r)[RS], const uint16_t* wg_x, int wbase, int lane,
-                                               int nres, uint32_t n_valid, std::integer_sequence<int, J...>) {
+// Non-temporal loads of slots FIRST .. FIRST + N - 1 into r (zeros past the end).
+template <bool GUARD, int FIRST, int N, int... J>
+__device__ __forceinline__ void load_slots(uint4 (&r)[N], const uint16_t* wg_x, int wbase, int lane,
+                                           int nres, uint32_t n_valid, std::integer_sequence<int, J...>) {
   auto one = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    const uint32_t ls = slot_of(wbase, j, lane);
-    if (!GUARD || (j < nres && ls < n_valid)) {
+    const uint32_t ls = slot_of(wbase, FIRST + j, lane);
+    if (!GUARD || (FIRST + j < nres && ls < n_valid)) {
       const u32x4_t a = load16<true>(slot_ptr(wg_x, ls));
       r[j] = make_uint4(a.x, a.y, a.z, a.w);
     } else {
@@ -219,46 +220,38 @@ __device__ __forceinline__ void encode_pairs(Phase2<GUARD>& p2, SlotSource<GUARD
   (one(std::integral_constant<int, P>{}), ...);
 }
 
-// Phase-1 view of a lane's slot j: its registers, its LDS entries (all loads
-// complete) or its re-read slots; a slot past the end reads as zeros.
-template <bool GUARD, int RS, int SC>
+// Phase-1 view of a lane's slot j: its registers, the registers that stage
+// its LDS entries, or its re-read slots; a slot past the end reads as zeros.
+template <int RS, int SC>
 struct Phase1Slots {
   const uint4 (&r)[RS];
-  const uint4* s_data;
+  const uint4 (&st)[kLdsSlots];
   const uint4 (&sc)[SC];
-  int wbase, lane, tid, nres;
-  uint32_t n_valid;
 
   template <int J>
   __device__ __forceinline__ uint4 get() const {
     if constexpr (J < RS) {
       return r[J];
     } else if constexpr (J < RS + kLdsSlots) {
-      const uint4 w = s_data[(J - RS) * kResThreads + tid];
-      if constexpr (GUARD) {
-        // (an entry past the end holds a copy of an earlier slot or nothing)
-        if (!(J < nres && slot_of(wbase, J, lane) < n_valid)) return make_uint4(0u, 0u, 0u, 0u);
-      }
-      return w;
+      return st[J - RS];
     } else {
       return sc[J - RS - kLdsSlots];
     }
   }
 };
 
-// The block maxima phase 2 needs, from the on-chip copies: for every pair of
-// rows, the largest magnitude (raw 16-bit pattern, non-finite included) of
-// the block this lane works out, packed two pairs per word (pair p in the
-// upper half of bmp[p / 2] when p is odd).  Returns the largest magnitude over
+// The block maxima phase 2 needs: for every pair of rows, the largest
+// magnitude (raw 16-bit pattern, non-finite included) of the block this lane
+// works out, packed two pairs per word (pair p in the upper half of bmp[p / 2]
+// when p is odd; bmp starts at zero).  acc collects the largest magnitude over
 // the lane's slots, non-finite included (the caller takes the finite maximum
-// apart when that is non-finite).  Straight-line code; the re-read slots go
-// first, so that their registers are free before the LDS entries are read.
-template <int RS, class S, int... P>
-__device__ __forceinline__ uint32_t block_maxima(const S& slots, bool odd, uint32_t (&bmp)[kMaxSlots / 4],
-                                                 std::integer_sequence<int, P...>) {
-  uint32_t acc = 0u;
-#pragma unroll
-  for (int k = 0; k < kMaxSlots / 4; ++k) bmp[k] = 0u;
+// apart when that is non-finite).  STAGED visits the pairs held wholly in the
+// LDS-bound registers; otherwise the rest, in the order their loads land:
+// register pairs, pairs that straddle registers and LDS, re-read pairs.
+// Straight-line code; the compiler waits for each load at its first use.
+template <int RS, bool STAGED, class S, int... P>
+__device__ __forceinline__ void block_maxima(const S& slots, bool odd, uint32_t (&bmp)[kMaxSlots / 4], uint32_t& acc,
+                                             std::integer_sequence<int, P...>) {
   auto one = [&](auto pc) {
     constexpr int p = decltype(pc)::value;
     const uint32_t m0 = slot_max16(slots.template get<2 * p>());
@@ -271,20 +264,19 @@ __device__ __forceinline__ uint32_t block_maxima(const S& slots, bool odd, uint3
     __builtin_amdgcn_sched_barrier(0);
   };
   constexpr int kFirstReread = RS + kLdsSlots;
-  auto reread = [&](auto pc) { if constexpr (2 * decltype(pc)::value >= kFirstReread) one(pc); };
-  auto in_regs = [&](auto pc) { if constexpr (2 * decltype(pc)::value + 1 < RS) one(pc); };
-  auto rest = [&](auto pc) {
-    constexpr int p = decltype(pc)::value;
-    if constexpr (!(2 * p >= kFirstReread) && !(2 * p + 1 < RS)) one(pc);
-  };
-  (reread(std::integral_constant<int, P>{}), ...);
-  (in_regs(std::integral_constant<int, P>{}), ...);
-  (rest(std::integral_constant<int, P>{}), ...);
-  // (the packed words are formed here: left to itself the compiler carries
-  // the 32 halves into phase 2 and spills them)
+  auto cls = [](int p) { return 2 * p + 1 < RS ? 1 : 2 * p >= kFirstReread ? 3 : 2 * p >= RS ? 0 : 2; };
+  auto visit = [&](auto pc, auto kc) { if constexpr (cls(decltype(pc)::value) == decltype(kc)::value) one(pc); };
+  if constexpr (STAGED) {
+    (visit(std::integral_constant<int, P>{}, std::integral_constant<int, 0>{}), ...);
+  } else {
+    (visit(std::integral_constant<int, P>{}, std::integral_constant<int, 1>{}), ...);
+    (visit(std::integral_constant<int, P>{}, std::integral_constant<int, 2>{}), ...);
+    (visit(std::integral_constant<int, P>{}, std::integral_constant<int, 3>{}), ...);
+    // (the packed words are formed here: left to itself the compiler carries
+    // the 32 halves into phase 2 and spills them)
 #pragma unroll
-  for (int k = 0; k < kMaxSlots / 4; ++k) asm volatile("" : "+v"(bmp[k]));
-  return acc;
+    for (int k = 0; k < kMaxSlots / 4; ++k) asm volatile("" : "+v"(bmp[k]));
+  }
 }
 
 // Largest finite magnitude (16-bit pattern) over a lane's slots, read again
@@ -376,35 +368,30 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
 
   // ---------------- phase 1
   constexpr int kRegSlots = reg_slots<GUARD>();
+  constexpr int kScan = reread_slots<GUARD>();
   uint4 r[kRegSlots];
-  // (the full-workgroup variant issues every load unconditionally, back to back)
-  load_reg_slots<GUARD>(r, wg_x, wbase, lane, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
-  if constexpr (GUARD) {
-    for (int j = kRegSlots; j < kRegSlots + kLdsSlots && j < nres; ++j) {
-      const uint32_t ls0 = slot_of(wbase, j, 0);                           // first slot of this wave's row
-      if (ls0 < n_valid) {
-        // lane l lands at s_data[(j - kRegSlots) * kResThreads + wv * 64 + l]; a lane past
-        // the end re-reads the wave's first slot (in bounds) and is never used
-        const uint32_t ls = ls0 + (uint32_t)lane;
-        const uint32_t src = ls < n_valid ? ls : ls0;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wg_x + (size_t)src * 8u),
-                                         (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = kRegSlots; j < kRegSlots + kLdsSlots; ++j)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(slot_ptr(wg_x, slot_of(wbase, j, lane))),
-                                       (lds_void_t*)(&s_data[(j - kRegSlots) * kResThreads + wv * 64]), 16, 0, 0);
-  }
-  // the re-read slots: all loads in flight before the first use (with
-  // global->LDS loads in flight, the first use of a loaded register waits for
-  // every load issued)
   uint32_t acc = 0u;
   uint32_t bmp[kMaxSlots / 4];
+#pragma unroll
+  for (int k = 0; k < kMaxSlots / 4; ++k) bmp[k] = 0u;
   {
-    constexpr int kScan = reread_slots<GUARD>();
+    // The LDS-bound slots first, through VGPRs (a direct global->LDS load in
+    // flight would make the first use of any loaded register wait for every
+    // load issued), then the register slots, all back to back.
+    uint4 st[kLdsSlots];
+    load_slots<GUARD, kRegSlots>(st, wg_x, wbase, lane, nres, n_valid, std::make_integer_sequence<int, kLdsSlots>{});
+    load_slots<GUARD, 0>(r, wg_x, wbase, lane, nres, n_valid, std::make_integer_sequence<int, kRegSlots>{});
+    __builtin_amdgcn_sched_barrier(0);
     uint4 sc[kScan];
+    const Phase1Slots<kRegSlots, kScan> slots{r, st, sc};
+    const bool odd = (lane & 1) != 0;
+    block_maxima<kRegSlots, true>(slots, odd, bmp, acc, std::make_integer_sequence<int, kMaxSlots / 2>{});
+    // each lane's LDS entries are its own: phase 2 reads them back in program
+    // order, with no barrier
+#pragma unroll
+    for (int j = 0; j < kLdsSlots; ++j) s_data[j * kResThreads + tid] = st[j];
+    __builtin_amdgcn_sched_barrier(0);
+    // the re-read slots, into the registers the staged slots leave free
 #pragma unroll
     for (int k = 0; k < kScan; ++k) {
       const int j = kRegSlots + kLdsSlots + k;
@@ -418,13 +405,8 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
         sc[k] = make_uint4(a.x, a.y, a.z, a.w);
       }
     }
-    // (nothing scheduled above this point: an early use would stop the issue)
     __builtin_amdgcn_sched_barrier(0);
-    // a wave reads only the LDS entries its own loads wrote: the wait for its
-    // loads suffices
-    __builtin_amdgcn_s_waitcnt(0);
-    const Phase1Slots<GUARD, kRegSlots, kScan> slots{r, s_data, sc, wbase, lane, tid, nres, n_valid};
-    acc = block_maxima<kRegSlots>(slots, (lane & 1) != 0, bmp, std::make_integer_sequence<int, kMaxSlots / 2>{});
+    block_maxima<kRegSlots, false>(slots, odd, bmp, acc, std::make_integer_sequence<int, kMaxSlots / 2>{});
   }
   if (acc >= 0x7F80u) acc = lane_finite_max16(wg_x, wbase, lane, nres, n_valid);
   acc <<= 16;   // fp32 bit pattern

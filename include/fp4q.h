@@ -211,9 +211,10 @@ fp4q_status fp4q_dequantize(int32_t format, int64_t rows, int64_t cols, int32_t 
  * b_scales), exactly the planes fp4q_quantize_mxfp4 writes (B is the
  * [N][K] weight, so C = A B^T).  Products are exact; the sum is fp32 in the
  * matrix instructions' order.  C is dense [M][N] fp32 or bf16 (out_dtype,
- * rounded to nearest-even).  K must be a multiple of 128 (else UNSUPPORTED;
- * not a multiple of 32: INVALID_ARG); code planes 16-byte aligned, scale
- * planes and C 4-byte aligned.  A NaN scale (0xFF) makes its terms NaN. */
+ * rounded to nearest-even).  K must be a multiple of 128 and at most 2^23
+ * (else UNSUPPORTED; not a multiple of 32: INVALID_ARG); code planes 16-byte
+ * aligned, scale planes and C 4-byte aligned.  A NaN scale (0xFF) makes its
+ * terms NaN. */
 fp4q_status fp4q_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *a_codes, const uint8_t *a_scales,
                             const uint8_t *b_codes, const uint8_t *b_scales, int32_t out_dtype, void *c,
                             void *hip_stream);

@@ -159,6 +159,7 @@ def test_mxfp4_gemm_rejects():
     F = FAKE
     assert lib.fp4q_mxfp4_gemm(4, 4, 80, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_INVALID_ARG   # K % 32
     assert lib.fp4q_mxfp4_gemm(4, 4, 96, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_UNSUPPORTED   # K % 128
+    assert lib.fp4q_mxfp4_gemm(4, 4, (1 << 23) + 128, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_UNSUPPORTED
     assert lib.fp4q_mxfp4_gemm(-1, 4, 128, F, F, F, F, 0, F, None) == _lib.FP4Q_ERR_INVALID_ARG
     assert lib.fp4q_mxfp4_gemm(4, 4, 128, F, F, F, F, 7, F, None) == _lib.FP4Q_ERR_INVALID_ARG
     assert lib.fp4q_mxfp4_gemm(4, 4, 128, None, F, F, F, 0, F, None) == _lib.FP4Q_ERR_INVALID_ARG
