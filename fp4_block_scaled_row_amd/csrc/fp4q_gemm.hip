@@ -22,7 +22,9 @@
 // lets an LDS read wait only for the loads it depends on), into a ring of
 // four stage buffers kept three stages ahead of the one being multiplied;
 // one fence-free barrier per stage, the loads being waited for explicitly.
-// Buffer offsets are 32-bit: K is at most 2^23.  Workgroups are
+// Buffer offsets are 32-bit: K is at most 2^23.  A tile wholly inside C
+// (with 16-byte aligned rows) leaves through LDS as 16-byte row chunks; other
+// tiles store element by element.  Workgroups are
 // numbered so that each XCD walks a contiguous range of C tiles, in groups of
 // 8 tile rows traversed column by column, so that the workgroups resident on
 // one XCD at a time share both A row tiles and B column tiles in its L2.
@@ -197,6 +199,49 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
     if (st + 7 < nstage) step(st + 7, s_st3, s_st2);
   }
 
+  // A tile wholly inside C, with 16-byte aligned rows: each wave writes its
+  // quarter 32 rows at a time into its own stage buffer, in the accumulator
+  // layout, and stores it back as 16-byte row chunks.
+  const bool whole = m0 + kTile <= g.M && n0 + kTile <= g.N && g.N % 8 == 0 &&
+                     (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+  if (whole) {
+    __syncthreads();   // every wave is done with the stage buffers
+    uint8_t* band = wv == 0 ? s_st0 : wv == 1 ? s_st1 : wv == 2 ? s_st2 : s_st3;
+    const int64_t row0 = m0 + kWaveTile * wr, col0 = n0 + kWaveTile * wc;
+#pragma unroll
+    for (int i = 0; i < kSub; ++i) {
+      if constexpr (BF16OUT) {
+        constexpr int kStride = kWaveTile + 8;   // bf16 elements per band row (272 bytes)
+        __bf16* t = reinterpret_cast<__bf16*>(band);
+#pragma unroll
+        for (int j = 0; j < kSub; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            t[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kStride + 32 * j + (lane & 31)] = (__bf16)acc[i][j][r];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int rr = 4 * k + (lane >> 4), cc = (lane & 15) * 8;
+          const uint4 v = *reinterpret_cast<const uint4*>(t + rr * kStride + cc);
+          *reinterpret_cast<uint4*>(static_cast<__bf16*>(g.c) + (row0 + 32 * i + rr) * g.N + col0 + cc) = v;
+        }
+      } else {
+        constexpr int kStride = kWaveTile + 4;   // floats per band row (528 bytes)
+        float* t = reinterpret_cast<float*>(band);
+#pragma unroll
+        for (int j = 0; j < kSub; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            t[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kStride + 32 * j + (lane & 31)] = acc[i][j][r];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int rr = 2 * k + (lane >> 5), cc = (lane & 31) * 4;
+          const float4 v = *reinterpret_cast<const float4*>(t + rr * kStride + cc);
+          *reinterpret_cast<float4*>(static_cast<float*>(g.c) + (row0 + 32 * i + rr) * g.N + col0 + cc) = v;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kSub; ++i)
 #pragma unroll

@@ -844,9 +844,11 @@ def _gemm_check(c_gpu, c_ref, absc, K, extra_rel=0.0):
     return float(rel.max())
 
 
-# K covers 1 to 9 pipeline stages of 128 (the load ring runs three stages ahead)
+# K covers 1 to 9 pipeline stages of 128 (the load ring runs three stages ahead);
+# 256x256 tiles wholly inside C (N a multiple of 8) take the staged epilogue
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (33, 17, 128), (130, 257, 256), (300, 520, 384), (64, 64, 512),
-                                   (257, 129, 640), (256, 128, 1024), (40, 300, 1152), (97, 300, 4096), (5, 7, 0)])
+                                   (257, 129, 640), (256, 128, 1024), (40, 300, 1152), (97, 300, 4096), (5, 7, 0),
+                                   (512, 264, 256), (256, 256, 384), (256, 260, 128)])
 def test_mxfp4_gemm_small(M, N, K):
     a = make_input(M, K, "bf16", M * 7 + K) if K else np.zeros((M, 0), np.uint16)
     b = make_input(N, K, "f32", N * 11 + K) if K else np.zeros((N, 0), np.float32)
