@@ -62,6 +62,28 @@ def _check_input(x):
         raise ValueError("fp4q: rows must be contiguous (stride(1) == 1)")
 
 
+def _check_buf(t, shape, dtype, what):
+    """A buffer handed to the library: a contiguous GPU tensor of this shape
+    (None: any shape) and dtype, since the kernels write or read it densely."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("fp4q: %s must be a GPU tensor" % what)
+    if t.dtype != dtype:
+        raise ValueError("fp4q: %s must be %s, got %s" % (what, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("fp4q: %s must have shape %s, got %s" % (what, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("fp4q: %s must be contiguous" % what)
+
+
+def _check_mx_out(out, rows, cols):
+    _check_buf(out.codes, (rows, cols // 2), torch.uint8, "out.codes")
+    _check_buf(out.scales, (rows, cols // 32), torch.uint8, "out.scales")
+    if out.rotated is not None:
+        _check_buf(out.rotated, (rows, cols), torch.float32, "out.rotated")
+    if out.counters is not None:
+        _check_buf(out.counters, (3,), torch.int64, "out.counters")
+
+
 def _args(x, block, policy, manual_exponent, rounding, rotation, seed):
     a = _lib.QuantArgs()
     a.rows, a.cols = int(x.shape[0]), int(x.shape[1])
@@ -100,6 +122,7 @@ def quantize_mxfp4(x, *, policy="ocp", manual_exponent=0, rounding="rne", seed=0
         rot = torch.empty((rows, cols), dtype=torch.float32, device=dev) if return_rotated else None
         cnt = torch.empty(3, dtype=torch.int64, device=dev) if counters else None
         out = MxResult(codes, scales, rot, cnt)
+    _check_mx_out(out, rows, cols)
     o = _lib.Outputs(_ptr(out.codes), _ptr(out.scales), None, None, _ptr(out.rotated), _ptr(out.counters))
     _lib.check(_lib.load().fp4q_quantize_mxfp4(a, _ptr(x), o, None, 0, _stream()), "fp4q_quantize_mxfp4")
     return out
@@ -129,6 +152,17 @@ def quantize_nvfp4(x, *, policy="max6", rounding="rne", seed=0, rotation=None, g
         rot = torch.empty((rows, cols), dtype=torch.float32, device=dev) if return_rotated else None
         cnt = torch.empty(3, dtype=torch.int64, device=dev) if counters else None
         out = NvResult(codes, scales, gs, choice, rot, cnt)
+    _check_buf(out.codes, (rows, cols // 2), torch.uint8, "out.codes")
+    _check_buf(out.scales, (rows, cols // 16), torch.uint8, "out.scales")
+    _check_buf(out.global_scale, (1,), torch.float32, "out.global_scale")
+    if out.choice_bits is not None:
+        _check_buf(out.choice_bits, ((rows * (cols // 16) + 7) // 8,), torch.uint8, "out.choice_bits")
+    if out.rotated is not None:
+        _check_buf(out.rotated, (rows, cols), torch.float32, "out.rotated")
+    if out.counters is not None:
+        _check_buf(out.counters, (3,), torch.int64, "out.counters")
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("fp4q: the workspace must be a GPU tensor")
     if workspace is None and global_amax is None:
         workspace = torch.zeros(workspace_bytes(16), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -160,6 +194,7 @@ def silu_mul_fwht_mxfp4(gate, up, *, policy="ocp", manual_exponent=0, rounding="
         rot = torch.empty((rows, cols), dtype=torch.float32, device=dev) if return_rotated else None
         cnt = torch.empty(3, dtype=torch.int64, device=dev) if counters else None
         out = MxResult(codes, scales, rot, cnt)
+    _check_mx_out(out, rows, cols)
     o = _lib.Outputs(_ptr(out.codes), _ptr(out.scales), None, None, _ptr(out.rotated), _ptr(out.counters))
     _lib.check(_lib.load().fp4q_silu_mul_fwht_mxfp4(a, _ptr(gate), _ptr(up), o, _stream()),
                "fp4q_silu_mul_fwht_mxfp4")
@@ -173,6 +208,7 @@ def fwht(x, transform_size=None, random_signs=False, seed=0, out=None):
     rows, d = x.shape
     t = d if transform_size is None else int(transform_size)
     y = torch.empty((rows, d), dtype=torch.float32, device=x.device) if out is None else out
+    _check_buf(y, (rows, d), torch.float32, "out")
     stride = int(x.stride(0)) if rows > 1 else d
     _lib.check(_lib.load().fp4q_fwht(rows, d, stride, _in_dtype(x), _ptr(x), _ptr(y), t, int(bool(random_signs)),
                                      int(seed) & 0xFFFFFFFFFFFFFFFF, _stream()), "fp4q_fwht")
@@ -185,9 +221,15 @@ def dequantize(fmt, codes, scales, global_scale=None, out_dtype=torch.float32, o
     f = {"mxfp4": _lib.FP4Q_MXFP4, "nvfp4": _lib.FP4Q_NVFP4, "if4": _lib.FP4Q_IF4}[fmt]
     rows, half = codes.shape
     cols = half * 2
+    block = 32 if f == _lib.FP4Q_MXFP4 else 16
+    _check_buf(codes, None, torch.uint8, "codes")
+    _check_buf(scales, (rows, cols // block), torch.uint8, "scales")
+    if global_scale is not None:
+        _check_buf(global_scale, (1,), torch.float32, "global_scale")
     od = {torch.float32: _lib.FP4Q_F32, torch.bfloat16: _lib.FP4Q_BF16}[out_dtype]
     y = torch.empty((rows, cols), dtype=out_dtype, device=codes.device) if out is None else out
-    _lib.check(_lib.load().fp4q_dequantize(f, rows, cols, 32 if f == _lib.FP4Q_MXFP4 else 16, _ptr(codes),
+    _check_buf(y, (rows, cols), out_dtype, "out")
+    _lib.check(_lib.load().fp4q_dequantize(f, rows, cols, block, _ptr(codes),
                                            _ptr(scales), _ptr(global_scale), od, _ptr(y), _stream()),
                "fp4q_dequantize")
     return y
@@ -208,6 +250,7 @@ def mxfp4_gemm(a, b, out_dtype=torch.float32, out=None):
             raise ValueError("fp4q: GEMM operands must be contiguous uint8 GPU tensors")
     od = {torch.float32: _lib.FP4Q_F32, torch.bfloat16: _lib.FP4Q_BF16}[out_dtype]
     c = torch.empty((M, N), dtype=out_dtype, device=ac.device) if out is None else out
+    _check_buf(c, (M, N), out_dtype, "out")
     _lib.check(_lib.load().fp4q_mxfp4_gemm(M, N, K, _ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), od, _ptr(c),
                                            _stream()), "fp4q_mxfp4_gemm")
     return c

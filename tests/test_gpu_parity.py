@@ -865,6 +865,47 @@ def test_mxfp4_gemm_small(M, N, K):
     _gemm_check(c16, ref, absc, K, extra_rel=2.0 ** -8)
 
 
+def test_mxfp4_gemm_unaligned_out():
+    """C at a 4-byte but not 16-byte aligned address: whole tiles take the
+    element-wise epilogue, with the same bits as an aligned C."""
+    M, N, K = 512, 264, 256
+    qa = fq.quantize_mxfp4(to_dev(make_input(M, K, "bf16", 5)))
+    qb = fq.quantize_mxfp4(to_dev(make_input(N, K, "bf16", 6)))
+    for dt, off in ((torch.float32, 1), (torch.bfloat16, 2)):
+        want = host(fq.mxfp4_gemm(qa, qb, out_dtype=dt).view(torch.int32 if dt == torch.float32 else torch.int16))
+        buf = torch.zeros(M * N + 8, dtype=dt, device=gpu())
+        c = buf[off:off + M * N].view(M, N)
+        assert c.data_ptr() % 16 != 0 and c.data_ptr() % 4 == 0
+        fq.mxfp4_gemm(qa, qb, out_dtype=dt, out=c)
+        got = host(c.view(torch.int32 if dt == torch.float32 else torch.int16))
+        assert np.array_equal(got, want), dt
+        assert not host(buf[:off]).any() and not host(buf[off + M * N:]).any()   # nothing outside C
+
+
+def test_binding_rejects_bad_buffers():
+    """Buffers the kernels would write or read densely are checked in the
+    binding: wrong shape, dtype, device or layout raises before any launch."""
+    dev = gpu()
+    x = to_dev(make_input(4, 64, "bf16", 9))
+    q = fq.quantize_mxfp4(x)
+    with pytest.raises(ValueError):
+        fq.mxfp4_gemm(q, q, out=torch.empty((4, 5), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        fq.mxfp4_gemm(q, q, out=torch.empty((4, 4), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        fq.mxfp4_gemm(q, q, out=torch.empty((4, 8), dtype=torch.float32, device=dev)[:, ::2])
+    with pytest.raises(ValueError):
+        fq.quantize_mxfp4(x, out=fq.MxResult(q.codes[:2], q.scales, None, None))
+    with pytest.raises(ValueError):
+        fq.dequantize("mxfp4", q.codes.cpu(), q.scales)
+    with pytest.raises(ValueError):
+        fq.dequantize("mxfp4", q.codes, q.scales, out=torch.empty((4, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        fq.fwht(x, out=torch.empty((4, 64), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        fq.quantize_nvfp4(x, workspace=torch.zeros(fq.workspace_bytes(16), dtype=torch.uint8))
+
+
 def test_mxfp4_gemm_nan_scale_and_exact_case():
     M, N, K = 64, 64, 256
     ac = np.full((M, K // 2), 0x22, np.uint8)                   # all 1.0
