@@ -1,7 +1,7 @@
 """Benchmark: quantize GB/s and fraction of HBM peak, 8192x8192 bf16 -> NVFP4
 (headline) and MXFP4, one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
 
     python bench.py --profile-kernels   # a few launches of each kernel, for rocprofv3
 
@@ -11,7 +11,10 @@ E4M3 block scales and the fp32 tensor scale (one launch of the single-read
 kernel).  Inputs are resident in HBM before timing; the step cycles over 4
 replicas of the input (4 x 128 MiB) so every step reads an input the Infinity
 Cache no longer holds.  value = algorithmic bytes (read the input once, write
-every output once) x K / wall time of the K steps.
+every output once) x K / wall time of the K steps.  Before the W warmup steps
+the headline step runs back to back, untimed, for MS milliseconds (default
+50): the GPU clock idles low and needs ~30 ms of load to reach its sustained
+level, which a few warmup steps do not give.
 
 The same line carries the MXFP4 quantization of the same tensor and the
 NVFP4 dequantization back to bf16 as sub-objects, the roofline of the
@@ -97,7 +100,17 @@ def profile_kernels(dev, reps=5):
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
+    def settle(fn, seconds=0.04):
+        # back-to-back launches until the GPU clock is at its sustained level
+        # (it drops while the host prepares the next workload)
+        t = time.perf_counter()
+        while time.perf_counter() - t < seconds:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+
     def run(label, fn, nbytes):
+        settle(fn)
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -186,6 +199,7 @@ def profile_kernels(dev, reps=5):
     flops = 2.0 * 8192 ** 3
 
     def run_flops(label, fn):
+        settle(fn)
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -219,6 +233,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed back-to-back headline steps before the warmup steps, so that the GPU clock "
+                         "reaches its sustained level (it idles low and ramps within ~30 ms of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each kernel of the five workloads and of IF4 a few times (for rocprofv3) and print "
@@ -254,14 +271,21 @@ def main():
         fq.quantize_nvfp4(xs[k], out=nv_out[k], workspace=ws)
 
     def timed(fn, steps, warmup):
+        """(wall seconds per step, HIP-event seconds per step) of `steps` steps
+        after `warmup` untimed ones; the events bracket the timed steps on the
+        launch stream (torch's current stream, which the library launches on)."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t = time.perf_counter()
+        e0.record(st)
         for i in range(steps):
             fn(i)
+        e1.record(st)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t) / steps
+        return (time.perf_counter() - t) / steps, e0.elapsed_time(e1) / 1e3 / steps
 
     def event_avg(fn, steps, pre=None):
         """Average per-call GPU duration from HIP events on the launch stream
@@ -278,13 +302,22 @@ def main():
         torch.cuda.synchronize()
         return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps / 1e3
 
-    # ---- headline: NVFP4 quantize, K steps (one launch of nv_resident_kernel each)
-    sec = timed(nv_step, a.steps, a.warmup)
-    value = NV_BYTES / sec / 1e9
+    def settle(fn, ms):
+        n, t = 0, time.perf_counter()
+        while (time.perf_counter() - t) * 1e3 < ms:
+            for _ in range(50):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        return n
 
-    # ---- roofline of the dominant kernel: the single-read NVFP4 kernel, the
-    # only launch of a step, timed with events around each call
-    call_sec = event_avg(nv_step, a.steps)
+    # ---- headline: NVFP4 quantize, K steps (one launch of nv_resident_kernel each)
+    settle_steps = settle(nv_step, a.settle_ms)
+    # roofline of the dominant kernel: the single-read NVFP4 kernel, the only
+    # launch of a step, so the events over the timed steps give its average
+    # launch duration (back-to-back launches: the gaps between them included)
+    sec, call_sec = timed(nv_step, a.steps, a.warmup)
+    value = NV_BYTES / sec / 1e9
     call_gbps = NV_BYTES / call_sec / 1e9
 
     # ---- the two-pass NVFP4 encode (used when the caller hands in the
@@ -305,15 +338,14 @@ def main():
     def mx_step(i):
         k = i % REPLICAS
         fq.quantize_mxfp4(xs[k], out=mx_out[k])
-    mx_sec = timed(mx_step, a.steps, a.warmup)
-    mx_ev = event_avg(mx_step, a.steps)
+    mx_sec, mx_ev = timed(mx_step, a.steps, a.warmup)
 
     # ---- NVFP4 dequantize back to bf16
     def dq_step(i):
         k = i % REPLICAS
         o = nv_out[k]
         fq.dequantize("nvfp4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=dq_out[k])
-    dq_sec = timed(dq_step, a.steps, a.warmup)
+    dq_sec = timed(dq_step, a.steps, a.warmup)[0]
 
     # ---- IF4 of the same tensor (amax pass + encode pass) and its dequantize
     if4_out = [fq.quantize_nvfp4(x, policy="if4", workspace=ws) for x in xs]
@@ -321,13 +353,13 @@ def main():
     def if4_step(i):
         k = i % REPLICAS
         fq.quantize_nvfp4(xs[k], policy="if4", out=if4_out[k], workspace=ws)
-    if4_sec = timed(if4_step, a.steps, a.warmup)
+    if4_sec = timed(if4_step, a.steps, a.warmup)[0]
 
     def if4_dq_step(i):
         k = i % REPLICAS
         o = if4_out[k]
         fq.dequantize("if4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=dq_out[k])
-    if4_dq_sec = timed(if4_dq_step, a.steps, a.warmup)
+    if4_dq_sec = timed(if4_dq_step, a.steps, a.warmup)[0]
     if4_int4_frac = float((if4_out[0].scales >= 0x80).float().mean())
 
     line = {
@@ -337,6 +369,8 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "settle_ms": a.settle_ms,
+        "settle_steps": settle_steps,
         "ms_per_step": round(sec * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
