@@ -19,7 +19,7 @@
 namespace fp4q {
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;   // tiles per wave step (8 measured ~2 % faster than 4 on bf16; 2 slower)
 
 template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL>
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(QuantLaunch q) {
