@@ -717,3 +717,46 @@ def test_bf16_cast_matches_torch():
     x[:4] = [np.inf, -np.inf, 3.4e38, -0.0]
     want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(f32_to_bf16_bits(x), want)
+
+
+# ---------------------------------------------------------------- frozen-order SSE (R-14, R-24)
+@pytest.mark.parametrize("kind", ["four_over_six", "if4"])
+def test_near_tie_choices_follow_frozen_fp32_order(kind):
+    """Four Over Six (transcript cue 10) and IF4 (cues 14 and 17) keep the
+    candidate with the lower block SSE; the pages fix no precision, and the
+    oracle follows one frozen fp32 order.  On blocks built so that this order
+    and exact arithmetic pick different candidates (tests/near_tie.py:
+    candidates from exact rationals, the order evaluated in numpy float32),
+    the oracle must pick what the frozen order picks, with the codes and
+    scale byte of that candidate.  The same blocks separate the frozen order
+    from two plausible slips (one 16-term sequential sum, a fused d*d + acc),
+    so either slip in the oracle would fail here."""
+    import near_tie as N
+    x, info = N.build(kind, 200, seed=7 if kind == N.FOS else 8)
+    n = x.shape[0] - 1
+    assert n >= 200
+    policy = 3 if kind == N.FOS else 4
+    c, s, g, choice, _ = oracle.quantize_nv(x, policy=policy)
+    assert g == N.global_scale(kind, x.max())
+    codes = codes_of(c)
+    if kind == N.FOS:
+        bits = np.unpackbits(choice, bitorder="little")[: x.shape[0]]
+    alt_frozen = differs_exact = 0
+    for r in range(1, x.shape[0]):
+        frozen, exact, (sa, ca, _, sb, cb, _) = info[r]
+        assert frozen != exact
+        differs_exact += 1
+        alt_frozen += frozen
+        if kind == N.FOS:
+            assert bool(bits[r]) == frozen, r
+            assert s[r, 0] == (sb if frozen else sa), r
+        else:
+            assert bool(s[r, 0] & 0x80) == frozen, r
+            assert s[r, 0] & 0x7F == sa, r
+        assert list(codes[r]) == (cb if frozen else ca), r
+    # both directions occur: exact keeps the alternative where the order keeps the default, and vice versa
+    assert 20 <= alt_frozen <= n - 20
+    for slip in ("seq16", "fma"):
+        changed = sum(bool(N.choice_f32(kind, x[r:r + 1], info[r][2], g, slip)[0]) != info[r][0]
+                      for r in range(1, x.shape[0]))
+        assert changed >= 10, (slip, changed)
