@@ -104,6 +104,25 @@ def workspace_bytes(block_size):
     return int(_lib.load().fp4q_workspace_bytes(a))
 
 
+# One zero-filled NVFP4 workspace per (device, stream), kept for the life of
+# the process: calls on one stream are ordered, which is all the library asks
+# of calls that share a workspace.
+_workspaces = {}
+
+
+def _default_workspace(dev):
+    stream = torch.cuda.current_stream(dev)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), stream.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("fp4q: no NVFP4 workspace exists yet for this stream; pass workspace= or make one "
+                               "call on the stream before capturing it")
+        ws = torch.zeros(workspace_bytes(16), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
 def quantize_mxfp4(x, *, policy="ocp", manual_exponent=0, rounding="rne", seed=0, rotation=None,
                    return_rotated=False, counters=False, out=None):
     """MXFP4-quantize a 2-D fp32/bf16 GPU tensor along its rows.
@@ -164,7 +183,7 @@ def quantize_nvfp4(x, *, policy="max6", rounding="rne", seed=0, rotation=None, g
     if workspace is not None and not workspace.is_cuda:
         raise ValueError("fp4q: the workspace must be a GPU tensor")
     if workspace is None and global_amax is None:
-        workspace = torch.zeros(workspace_bytes(16), dtype=torch.uint8, device=dev)
+        workspace = _default_workspace(dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if global_amax is not None and (global_amax.dtype != torch.float32 or not global_amax.is_cuda):
         raise TypeError("fp4q: global_amax must be a float32 GPU tensor")

@@ -50,12 +50,25 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
-    """Compile every HIP source for gfx950 and link libfp4q.so in place."""
+def _stale(src):
+    """True when the object of src is missing or older than src or any header."""
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
+    deps.append(os.path.join(ROOT, "include", "fp4q.h"))
+    return any(os.path.getmtime(d) > os.path.getmtime(obj) for d in deps)
+
+
+def build(verbose=False, jobs=None, incremental=False):
+    """Compile every HIP source for gfx950 and link libfp4q.so in place
+    (incremental: only the sources whose object is out of date)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
+    todo = [s for s in SOURCES if not incremental or _stale(s)]
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,4 +79,4 @@ def build(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

@@ -200,7 +200,8 @@ fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args* args, const void* x, cons
   const int64_t n = args->rows * args->cols;
   if (args->scale_policy == FP4Q_SCALE_FOUR_OVER_SIX && n > 0 && !out->choice_bits) return FP4Q_ERR_INVALID_ARG;
   if (!global_amax) {
-    if (!workspace || workspace_bytes < fp4q_workspace_bytes(args) || !aligned(workspace, 4))
+    // (8-byte aligned: the single-read kernel keeps 64-bit atomic words in it)
+    if (!workspace || workspace_bytes < fp4q_workspace_bytes(args) || !aligned(workspace, 8))
       return FP4Q_ERR_WORKSPACE;
   }
   QuantLaunch q = make_launch(args, x, out);

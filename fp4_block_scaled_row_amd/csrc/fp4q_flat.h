@@ -152,12 +152,24 @@ __device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float
   p[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Adds a thread's saturated, underflowed and non-finite counts to the three
+// global counters: wave sums, then the workgroup's sums in LDS, then one
+// atomic add per nonzero counter per workgroup.  Every thread of the
+// workgroup calls it (it synchronises).
 __device__ __forceinline__ void flush_counters(unsigned long long* c, uint32_t sat, uint32_t und, uint32_t nf) {
+  __shared__ unsigned long long s_cnt[3];
   const unsigned long long a = wave_sum_u64(sat), b = wave_sum_u64(und), d = wave_sum_u64(nf);
+  if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0ull;
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) {
-    if (a) atomicAdd(c + 0, a);
-    if (b) atomicAdd(c + 1, b);
-    if (d) atomicAdd(c + 2, d);
+    if (a) atomicAdd(s_cnt + 0, a);
+    if (b) atomicAdd(s_cnt + 1, b);
+    if (d) atomicAdd(s_cnt + 2, d);
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    const unsigned long long v = s_cnt[threadIdx.x];
+    if (v) atomicAdd(c + threadIdx.x, v);
   }
 }
 

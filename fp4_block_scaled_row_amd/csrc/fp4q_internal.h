@@ -34,8 +34,8 @@ struct QuantLaunch {
 
 constexpr int kAmaxPartialsMax = 1024;  // workgroups of the NV amax pass
 // NVFP4 workspace layout (bytes): [0, 64) header of the single-launch kernel
-// (word 2: wait limit override), [64, 64 + 8 * 1024) its
-// per-workgroup flags, [8256, 8256 + 4 * 1024) the amax partials of the
+// (u64 word 2: wait limit override, word 3: epoch word of captured launches), [64,
+// 64 + 8 * 1024) its per-workgroup flags, [8256, 8256 + 4 * 1024) the amax partials of the
 // two-pass kernels, [16384, 16384 + 4096 * 16) sixteen copies of the result
 // word of the single-launch kernel, 4 KiB apart.
 constexpr size_t kWsFlagsOffsetBytes = 64;

@@ -19,10 +19,14 @@
 namespace fp4q {
 namespace {
 
-constexpr int kUnroll = 8;   // tiles per wave step (8 measured ~2 % faster than 4 on bf16; 2 slower)
+// Tiles per wave step: 8 (measured ~2 % faster than 4 on bf16; 2 slower), or
+// 1 for tensors too small to give every SIMD a wave with 8 (1024 x 1024 is
+// 2048 tiles: 64 workgroups with 8, 512 with 1).
+constexpr int kUnroll = 8;
 
-template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL>
+template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL, int UNROLL>
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(QuantLaunch q) {
+  constexpr int kUnroll = UNROLL;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
@@ -96,10 +100,17 @@ __global__ void zero_counters_kernel(unsigned long long* c) {
 template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL>
 hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   const int64_t ntiles = (q.nslots + 63) >> 6;
-  const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t cus = device_cu_count();
+  const bool small = ntiles < cus * kWaves * kUnroll;   // fewer than one workgroup per CU with 8
+  const int unroll = small ? 1 : kUnroll;
+  const int64_t want = (ntiles + kWaves * unroll - 1) / (kWaves * unroll);
+  const int64_t cap = cus * 8;
   const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
-  hipLaunchKernelGGL((mx_quant_kernel<IN, ROT, SR, COUNT, CONTIG, MANUAL>), dim3(grid), dim3(kThreads), 0, st, q);
+  if (small)
+    hipLaunchKernelGGL((mx_quant_kernel<IN, ROT, SR, COUNT, CONTIG, MANUAL, 1>), dim3(grid), dim3(kThreads), 0, st, q);
+  else
+    hipLaunchKernelGGL((mx_quant_kernel<IN, ROT, SR, COUNT, CONTIG, MANUAL, kUnroll>), dim3(grid), dim3(kThreads), 0,
+                       st, q);
   return hipGetLastError();
 }
 

@@ -26,10 +26,22 @@
 //
 // The launch is an ordinary one with at most kResPerCu workgroups per CU.
 // Results never depend on the workgroups being resident together: every wait
-// is bounded in time, and a workgroup whose wait runs out takes the tensor
-// maximum from a scan of the whole input instead (same value, only slower).
-// The epoch is a per-call number from the host, so flags left by an earlier
-// call never match; the workspace must be zero-filled before its first use.
+// is bounded in time (1 ms), and a workgroup whose wait runs out takes the
+// tensor maximum from the flags already published, scanning itself only the
+// chunks whose flags are missing and publishing their maxima for the others
+// (same value, only slower: at worst one extra read of the tensor per
+// workgroup that times out).
+//
+// Every launch carries a fresh epoch, so that flags and result words left by
+// an earlier launch never pass for its own.  An ordinary launch takes it from
+// a host counter (1 .. 2^31 - 1) as a kernel argument.  A launch captured in
+// a HIP graph cannot (its arguments are frozen at capture), so it is preceded
+// by a one-thread kernel that advances an epoch word kept in the workspace
+// (2^31 .. 2^32 - 1, disjoint from the host's), and the kernel reads that word
+// as it starts: every replay gets a fresh epoch too.  (One atomic ticket per
+// workgroup on a shared word was measured instead: the 1024 atomics on one
+// address serialise, about 20 us per launch.)  The workspace must be
+// zero-filled before its first use.
 //
 // The 8192 x 8192 bf16 activation is 1024 x 256 x 32 slots on 256 CUs: 26 of
 // every 32 slots stay on chip.
@@ -295,23 +307,57 @@ __device__ __forceinline__ uint32_t lane_finite_max16(const uint16_t* wg_x, int 
   return acc;
 }
 
-// Tensor maximum (finite bf16 magnitudes, as an fp32 bit pattern) from a scan
-// of the whole input by one workgroup: the fallback of a wait that ran out.
-__device__ uint32_t scan_tensor_amax(const QuantLaunch& q, uint32_t* s_red) {
+// Tensor maximum (finite bf16 magnitudes, as an fp32 bit pattern) after a
+// wait ran out: the chunk maxima already published in the flags, and a scan
+// by this workgroup of every chunk whose flag is missing (its maximum is then
+// published in that chunk's flag, the value its owner publishes too, so that
+// other workgroups that time out need not scan it again).  Every thread of the
+// workgroup calls this.
+__device__ uint32_t fallback_tensor_amax(const QuantLaunch& q, uint64_t* flags, uint32_t epoch, int nres,
+                                         uint32_t* s_red, uint32_t* s_missing) {
   const uint16_t* x = static_cast<const uint16_t*>(q.x);
-  const int tid = threadIdx.x;
-  uint32_t acc = 0u;
-  for (int64_t sl = tid; sl < q.nslots; sl += kResThreads) {
-    const u32x4_t a = load16<false>(x + (sl << 3));
-    acc = max(acc, raw_finite_absmax(make_uint4(a.x, a.y, a.z, a.w)));
-  }
-  acc = wave_max_u32(acc);
+  const int tid = threadIdx.x, G = gridDim.x;
+  const int64_t chunk = (int64_t)kResThreads * nres;   // slots per workgroup
   __syncthreads();
-  if ((tid & 63) == 0) s_red[tid >> 6] = acc;
+  for (int w = tid; w < kAmaxPartialsMax / 32; w += kResThreads) s_missing[w] = 0u;
   __syncthreads();
   uint32_t m = 0u;
+  for (int i = tid; i < G; i += kResThreads) {
+    const uint64_t f = __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(f >> 32) == epoch) m = max(m, (uint32_t)f);
+    else atomicOr(s_missing + (i >> 5), 1u << (i & 31));
+  }
+  __syncthreads();
+  for (int w = 0; w < (G + 31) / 32; ++w) {
+    uint32_t bitsw = s_missing[w];   // (the same value in every thread)
+    while (bitsw != 0u) {
+      const int i = 32 * w + __builtin_ctz(bitsw);
+      bitsw &= bitsw - 1u;
+      const int64_t s0 = (int64_t)i * chunk;
+      const int64_t s1 = s0 + chunk < q.nslots ? s0 + chunk : q.nslots;
+      uint32_t c = 0u;
+      for (int64_t sl = s0 + tid; sl < s1; sl += kResThreads) {
+        const u32x4_t a = load16<false>(x + (sl << 3));
+        c = max(c, raw_finite_absmax(make_uint4(a.x, a.y, a.z, a.w)));
+      }
+      c = wave_max_u32(c);
+      if ((tid & 63) == 0) s_red[tid >> 6] = c;
+      __syncthreads();
+      c = 0u;
 #pragma unroll
-  for (int w = 0; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
+      for (int v = 0; v < kResThreads / 64; ++v) c = max(c, s_red[v]);
+      if (tid == 0)
+        __hip_atomic_store(flags + i, ((uint64_t)epoch << 32) | c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      m = max(m, c);
+      __syncthreads();
+    }
+  }
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  m = 0u;
+#pragma unroll
+  for (int v = 0; v < kResThreads / 64; ++v) m = max(m, s_red[v]);
   __syncthreads();
   return m;
 }
@@ -341,9 +387,11 @@ __device__ __forceinline__ bool wait_epoch(const uint64_t* p, uint32_t epoch, co
   return false;
 }
 
+// epoch: this launch's epoch, or 0 to read it from the workspace's epoch word
+// (a launch captured in a graph, after epoch_advance_kernel).
 template <bool GUARD>
 __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(QuantLaunch q, int nres, unsigned char* ws,
-                                                                     uint32_t epoch) {
+                                                                     uint32_t epoch_arg) {
   __shared__ uint4 s_data[kLdsSlots * kResThreads];   // 36,864 bytes (four workgroups per CU)
   __shared__ float2 s_adj[256];   // adjusted multiplier and flag per conversion byte
   __shared__ float2 s_br[128];    // brackets of 1 / (s g) per scale code
@@ -351,10 +399,12 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   __shared__ uint32_t s_red[kResThreads / 64];
   __shared__ uint32_t s_timeout;
   __shared__ uint32_t s_amax;
+  __shared__ uint32_t s_epoch;
+  __shared__ uint32_t s_missing[kAmaxPartialsMax / 32];   // fallback: chunks without a flag
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
   const int G = gridDim.x;
-  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);   // [2] wait limit override
+  uint64_t* hdr = reinterpret_cast<uint64_t*>(ws);   // [2] wait limit override, [3] graph epoch word
   uint64_t* flags = reinterpret_cast<uint64_t*>(ws + kWsFlagsOffsetBytes);   // one per workgroup
   constexpr int kResultWords = (int)(kWsResultStrideBytes / 8);
   uint64_t* results = reinterpret_cast<uint64_t*>(ws + kWsResultsOffsetBytes);   // kWsResultCopies copies
@@ -365,6 +415,10 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   const uint16_t* wg_x = static_cast<const uint16_t*>(q.x) + (base << 3);
   const int wbase = wv * 64 * nres;                                   // this wave's first slot
   if (tid == 0) s_timeout = 0u;
+  // (a captured launch reads its epoch as it starts; it is used after phase 1)
+  uint32_t epoch_word = epoch_arg;
+  if (epoch_arg == 0u && tid == 0)
+    epoch_word = (uint32_t)__hip_atomic_load(hdr + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---------------- phase 1
   constexpr int kRegSlots = reg_slots<GUARD>();
@@ -412,7 +466,9 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   acc <<= 16;   // fp32 bit pattern
   acc = wave_max_u32(acc);
   if (lane == 0) s_red[wv] = acc;
+  if (tid == 0) s_epoch = epoch_word;
   __syncthreads();
+  const uint32_t epoch = s_epoch;
 
   // ---------------- grid-wide exchange of the chunk maxima
   if (tid == 0) {
@@ -439,7 +495,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     m = 0u;
 #pragma unroll
     for (int w = 0; w < kResThreads / 64; ++w) m = max(m, s_red[w]);
-    if (s_timeout) m = scan_tensor_amax(q, s_red);
+    if (s_timeout) m = fallback_tensor_amax(q, flags, epoch, nres, s_red, s_missing);
     const uint64_t word = ((uint64_t)epoch << 32) | m;
     if (tid < kWsResultCopies)
       __hip_atomic_store(results + (size_t)tid * kResultWords, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -453,7 +509,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
       else s_timeout = 1u;
     }
     __syncthreads();
-    amax_bits = s_timeout ? scan_tensor_amax(q, s_red) : s_red[0];
+    amax_bits = s_timeout ? fallback_tensor_amax(q, flags, epoch, nres, s_red, s_missing) : s_red[0];
   }
 
   NvCtx cx;
@@ -526,18 +582,36 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
   }
 }
 
-// Per-call epoch: flags written by earlier calls never carry it (0 is the
-// value of a freshly zeroed workspace and is skipped).
+// Host epochs 1 .. 2^31 - 1 (0 never: it is the value of a zeroed workspace,
+// and it tells the kernel to read the workspace's word).
 uint32_t next_epoch() {
   static std::atomic<uint32_t> counter{0u};
-  uint32_t e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  if (e == 0u) e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  return e;
+  for (;;) {
+    const uint32_t e = (counter.fetch_add(1u, std::memory_order_relaxed) + 1u) & 0x7FFFFFFFu;
+    if (e != 0u) return e;
+  }
+}
+
+// Advances the workspace's epoch word within 2^31 .. 2^32 - 1 (graph launches).
+__global__ void epoch_advance_kernel(unsigned char* ws) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(ws) + 3;
+  const uint32_t e = (uint32_t)*w;
+  *w = (uint64_t)((((e + 1u) & 0x7FFFFFFFu) | 0x80000000u));
 }
 
 hipError_t launch_resident(const QuantLaunch& q, int grid, int nres, hipStream_t st) {
   unsigned char* ws = reinterpret_cast<unsigned char*>(q.partials);
-  const uint32_t epoch = next_epoch();
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t ce = hipStreamIsCapturing(st, &cs);
+  if (ce != hipSuccess) return ce;
+  uint32_t epoch = 0u;
+  if (cs == hipStreamCaptureStatusNone) {
+    epoch = next_epoch();
+  } else {
+    hipLaunchKernelGGL(epoch_advance_kernel, dim3(1), dim3(1), 0, st, ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // every workgroup full: kMaxSlots slot rows each and nothing left over
   const bool full = nres == kMaxSlots && q.nslots == (int64_t)grid * kResThreads * kMaxSlots;
   if (full) {

@@ -121,16 +121,18 @@ typedef struct {
 } fp4q_outputs;
 
 /* Bytes of device workspace a quantize call needs (0 if none).  The NVFP4
- * workspace (80 KiB) belongs to the caller, must be zero-filled before its
- * first use and is then kept consistent by the library; calls that share one
+ * workspace (80 KiB, 8-byte aligned) belongs to the caller, must be
+ * zero-filled before its first use and is then kept consistent by the
+ * library, also across launches captured in a HIP graph and replayed (a
+ * captured single-read launch takes its epoch from a word in the workspace,
+ * advanced by a one-thread kernel captured before it); calls that share one
  * workspace must be ordered (same stream, or synchronised).  Layout: bytes
- * [16, 24) an
- * optional wait limit of that kernel's grid-wide exchange in ticks of the
- * 100 MHz GPU clock (0: 1 ms; a small value makes every wait run out and the
- * kernel fall back to scanning the tensor itself, which tests use), [64,
- * 8256) per-workgroup flags, [8256, 12352) the per-workgroup maxima of the
- * two-pass kernels, [16384, 81920) sixteen copies of the single-read
- * kernel's result word, 4 KiB apart. */
+ * [16, 24) an optional wait limit of that kernel's grid-wide exchange in
+ * ticks of the 100 MHz GPU clock (0: 1 ms; a small value makes every wait
+ * run out, which tests use), [24, 32) the epoch word of captured launches,
+ * [64, 8256) per-workgroup flags, [8256,
+ * 12352) the per-workgroup maxima of the two-pass kernels, [16384, 81920)
+ * sixteen copies of the single-read kernel's result word, 4 KiB apart. */
 size_t fp4q_workspace_bytes(const fp4q_quant_args *args);
 
 /* MXFP4 quantization of x ([rows][in_row_stride] of in_dtype).  block_size
@@ -156,12 +158,19 @@ fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args *args, const void *x,
  * computed in the call (a first pass over x, after rotation) unless
  * `global_amax` (device pointer to one finite non-negative float) is given.
  * amax 0 gives g = 1; a nonzero amax whose g underflows gives g = 2^-149.
- * Needs fp4q_workspace_bytes() of workspace unless global_amax is given.
+ * Needs fp4q_workspace_bytes() of workspace (8-byte aligned, else
+ * FP4Q_ERR_WORKSPACE) unless global_amax is given.
  * Contiguous bf16 input with policy NV_MAX6, RNE, no rotation, no counters,
  * no global_amax and at most 32768 eight-element slots per CU (64 Mi
- * elements on 256 CUs) runs as one launch that reads most of x once (one
- * 1024-thread workgroup per CU); every other case runs an amax pass and an
- * encode pass.  Both give identical bytes. */
+ * elements on 256 CUs) runs as one launch that reads most of x once (four
+ * 256-thread workgroups per CU, which exchange their chunk maxima through the
+ * workspace); every other case runs an amax pass and an encode pass.  Both
+ * give identical bytes.  The single launch assumes its workgroups run
+ * together; when they cannot (another stream holding CUs, say), each
+ * workgroup whose wait for the tensor maximum runs out (after 1 ms) reads the
+ * chunk maxima already published and scans the chunks still missing itself:
+ * still the same bytes, at a cost of up to 1 ms plus up to one read of x per
+ * such workgroup. */
 fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args *args, const void *x,
                                 const float *global_amax, const fp4q_outputs *out,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);

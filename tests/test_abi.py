@@ -128,6 +128,8 @@ def test_nvfp4_needs_workspace_or_amax():
     assert lib.fp4q_quantize_nvfp4(a, FAKE, None, OUTS, FAKE, 16, None) == _lib.FP4Q_ERR_WORKSPACE
     o = _lib.Outputs(FAKE, FAKE, None, None, None, None)
     assert lib.fp4q_quantize_nvfp4(a, FAKE, None, o, FAKE, 1 << 20, None) == _lib.FP4Q_ERR_INVALID_ARG
+    # the single-read kernel keeps 64-bit atomic words in the workspace: 8-byte alignment
+    assert lib.fp4q_quantize_nvfp4(a, FAKE, None, OUTS, FAKE + 4, 1 << 20, None) == _lib.FP4Q_ERR_WORKSPACE
     a46 = _args(block=16, policy=_lib.FP4Q_SCALE_FOUR_OVER_SIX)
     o = _lib.Outputs(FAKE, FAKE, FAKE, None, None, None)
     assert lib.fp4q_quantize_nvfp4(a46, FAKE, None, o, FAKE, 1 << 20, None) == _lib.FP4Q_ERR_INVALID_ARG

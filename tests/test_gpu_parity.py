@@ -127,23 +127,75 @@ def test_fwht_mx_swiglu_16384x8192():
     assert rel_l2(rot[rows], ref) <= RTOL_ROT
 
 
-def test_four_over_six_weight_8192x28672_sampled_rows():
+def oracle_nv_all_rows(x, policy, amax, rows_per_chunk=128):
+    """The oracle's NVFP4 of every row of x, rows split over host threads
+    (the C oracle runs without the GIL); amax is the tensor amax, so every
+    chunk uses the tensor's g.  Returns codes, scales, g, choice bytes (or
+    None) and the summed counters."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    R, cols = x.shape
+    nbr = cols // 16
+    assert (rows_per_chunk * nbr) % 8 == 0          # chunk choice bits start on byte boundaries
+    chunks = [(r0, min(R, r0 + rows_per_chunk)) for r0 in range(0, R, rows_per_chunk)]
+    nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(nthreads) as ex:
+        parts = list(ex.map(lambda c: oracle.quantize_nv(x[c[0]:c[1]], policy=policy, global_amax=amax), chunks))
+    codes = np.concatenate([p[0] for p in parts])
+    scales = np.concatenate([p[1] for p in parts])
+    g = parts[0][2]
+    assert all(p[2] == g for p in parts)
+    choice = None
+    if parts[0][3] is not None:
+        bitsall = np.concatenate([np.unpackbits(p[3], bitorder="little")[:(c[1] - c[0]) * nbr]
+                                  for p, c in zip(parts, chunks)])
+        choice = np.packbits(bitsall, bitorder="little")
+    cnt = np.sum([p[4] for p in parts], axis=0).astype(np.uint64)
+    return codes, scales, g, choice, cnt
+
+
+# The three tests below share the 8192 x 28672 weight (generated once), every
+# row compared.
+def test_four_over_six_weight_8192x28672_all_rows():
     x = workload("weight_bf16_8192x28672")
-    r = fq.quantize_nvfp4(to_dev(x), policy="four_over_six", counters=True)
     amax = oracle.tensor_amax(x)
-    g_ref = np.float32(amax) / np.float32(1792)
-    assert host(r.global_scale)[0] == g_ref
-    codes, scales, choice = host(r.codes), host(r.scales), host(r.choice_bits)
-    nbr = x.shape[1] // 16
-    for r0 in (0, 4095, 8192 - 160):
-        r1 = r0 + 160
-        c, s, g, ch, _ = oracle.quantize_nv(x[r0:r1], policy=3, global_amax=amax)
-        assert g == g_ref
-        assert_same(codes[r0:r1], c, "codes rows %d-%d" % (r0, r1))
-        assert_same(scales[r0:r1], s, "scales rows %d-%d" % (r0, r1))
-        assert_same(choice_bits_rows(choice, r0, r1, nbr), np.unpackbits(ch, bitorder="little")[:(r1 - r0) * nbr],
-                    "choice bits rows %d-%d" % (r0, r1))
-    assert host(r.counters)[2] == 0
+    c, s, g, ch, cnt = oracle_nv_all_rows(x, 3, amax)
+    assert g == np.float32(amax) / np.float32(1792)
+    xd = to_dev(x)
+    for counters in (False, True):   # (without counters: the kernel the bench times)
+        r = fq.quantize_nvfp4(xd, policy="four_over_six", counters=counters)
+        assert host(r.global_scale)[0] == g
+        assert_same(host(r.scales), s, "scales (counters %s)" % counters)
+        assert_same(host(r.codes), c, "codes (counters %s)" % counters)
+        assert_same(host(r.choice_bits), ch, "choice bits (counters %s)" % counters)
+        if counters:
+            assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+        del r
+
+
+def test_if4_weight_8192x28672_all_rows():
+    x = workload("weight_bf16_8192x28672")
+    amax = oracle.tensor_amax(x)
+    c, s, g, _, cnt = oracle_nv_all_rows(x, 4, amax)
+    xd = to_dev(x)
+    for counters in (False, True):
+        _if4_check(fq.quantize_nvfp4(xd, policy="if4", counters=counters), c, s, g, cnt if counters else None)
+
+
+def test_nv_max6_weight_8192x28672_two_pass_all_rows():
+    """max->6, RNE, no counters, amax in the call, over 64 Mi elements: too
+    large for the single-read kernel, so the amax pass and the streaming
+    paired encode run on the per-workgroup partials in the workspace."""
+    x = workload("weight_bf16_8192x28672")
+    amax = oracle.tensor_amax(x)
+    c, s, g, _, cnt = oracle_nv_all_rows(x, 2, amax)
+    r = fq.quantize_nvfp4(to_dev(x))
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    r = fq.quantize_nvfp4(to_dev(x), counters=True)   # the two-pass kernel with counters: same bytes
+    assert_same(host(r.codes), c, "codes (counters)")
+    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
 
 
 def test_rht_sr_grad_8192():
@@ -177,11 +229,13 @@ def make_input(rows, cols, dtype, seed, dist="t", pad=0):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rounding", ["rne", "stochastic"])
 @pytest.mark.parametrize("rotation", [None, "rht16"])
-def test_mx_small(rows, cols, dtype, rounding, rotation):
+@pytest.mark.parametrize("counters", [True, False])
+def test_mx_small(rows, cols, dtype, rounding, rotation, counters):
+    # odd row counts read every row from a wider padded tensor (strided input)
     pad = 32 if rows % 2 else 0
     full = make_input(rows, cols, dtype, rows * 1000 + cols, pad=pad)
     xd = to_dev(full)[:, :cols]
-    r = fq.quantize_mxfp4(xd, rounding=rounding, seed=77, rotation=rotation, counters=True,
+    r = fq.quantize_mxfp4(xd, rounding=rounding, seed=77, rotation=rotation, counters=counters,
                           return_rotated=rotation is not None)
     if rotation is None:
         c, s, cnt = oracle.quantize_mx(full, cols=cols, rounding=int(rounding != "rne"), seed=77)
@@ -192,24 +246,28 @@ def test_mx_small(rows, cols, dtype, rounding, rotation):
         c, s, cnt = oracle.quantize_mx(rot, rounding=int(rounding != "rne"), seed=77)
     assert_same(host(r.codes), c, "codes")
     assert_same(host(r.scales), s, "scales")
-    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    if counters:
+        assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
 
 
 @pytest.mark.parametrize("rows,cols", SHAPES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("policy", ["max6", "four_over_six"])
 @pytest.mark.parametrize("rounding", ["rne", "stochastic"])
-def test_nv_small(rows, cols, dtype, policy, rounding):
+@pytest.mark.parametrize("counters", [True, False])
+def test_nv_small(rows, cols, dtype, policy, rounding, counters):
+    # odd row counts read every row from a wider padded tensor (strided input)
     pad = 16 if rows % 2 else 0
     full = make_input(rows, cols, dtype, rows * 7 + cols, pad=pad)
     xd = to_dev(full)[:, :cols]
-    r = fq.quantize_nvfp4(xd, policy=policy, rounding=rounding, seed=123, counters=True)
+    r = fq.quantize_nvfp4(xd, policy=policy, rounding=rounding, seed=123, counters=counters)
     c, s, g, ch, cnt = oracle.quantize_nv(full, cols=cols, policy=3 if policy == "four_over_six" else 2,
                                          rounding=int(rounding != "rne"), seed=123)
     assert host(r.global_scale)[0] == g
     assert_same(host(r.scales), s, "scales")
     assert_same(host(r.codes), c, "codes")
-    assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+    if counters:
+        assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
     if ch is not None:
         assert_same(host(r.choice_bits), ch, "choice bits")
 
@@ -481,6 +539,39 @@ def test_nv_single_read_workspace_reuse_and_fallback():
     _nv_single(workloads.random_tensor(300, 4096, "bf16", 7, scale=2.0), ws)
 
 
+def test_nv_single_read_graph_replay():
+    """The single-read kernel captured in a HIP graph and replayed on new
+    data: each replay takes its epoch from the workspace, so flags and result
+    words of the previous replay never pass for its own (the tensors differ
+    in amax, so a stale tensor scale would show)."""
+    dev = gpu()
+    rows, cols = 2048, 4096
+    xs = [workloads.random_tensor(rows, cols, "bf16", 40 + k, scale=sc, dist="t")
+          for k, sc in enumerate((2.0, 50.0, 0.01, 2.0))]
+    static_x = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        static_x.copy_(to_dev(xs[0]))
+        fq.quantize_nvfp4(static_x)                   # the stream's workspace exists before capture
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        out = fq.quantize_nvfp4(static_x)
+    for k in (1, 2, 0, 3, 1):
+        static_x.copy_(to_dev(xs[k]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        c, s, g, _, _ = oracle.quantize_nv(xs[k])
+        assert host(out.global_scale)[0] == g, k
+        assert_same(host(out.scales), s, "scales (replay of input %d)" % k)
+        assert_same(host(out.codes), c, "codes (replay of input %d)" % k)
+        with torch.cuda.stream(stream):               # eager work on the same stream and workspace
+            e = fq.quantize_nvfp4(static_x)
+        stream.synchronize()
+        assert_same(host(e.codes), c, "codes (eager call between replays)")
+
+
 # ------------------------------------------------------------------ exhaustive NVFP4 coverage
 def _e4m3_value(c):
     return c * 2.0 ** -9 if c < 8 else (1 + (c & 7) / 8.0) * 2.0 ** ((c >> 3) - 7)
@@ -597,6 +688,29 @@ def test_nv_fp32_decision_points(rounding, counters):
         assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
 
 
+@pytest.mark.parametrize("kind", ["four_over_six", "if4"])
+def test_near_tie_sse_choices(kind):
+    """Blocks on which the frozen fp32 order of the block SSE and exact
+    arithmetic pick different candidates (tests/near_tie.py, fp32 inputs; the
+    oracle is pinned to the frozen order on the same blocks): the kernels'
+    per-lane half sums must reproduce that order, with counters on and off."""
+    import near_tie as N
+    x, _ = N.build(kind, 200, seed=7 if kind == N.FOS else 8)
+    x = np.ascontiguousarray(np.concatenate([x, np.zeros((x.shape[0], 48), np.float32)], axis=1))  # 4 blocks a row
+    policy = 3 if kind == N.FOS else 4
+    c, s, g, ch, cnt = oracle.quantize_nv(x, policy=policy)
+    xd = to_dev(x)
+    for counters in (False, True):
+        r = fq.quantize_nvfp4(xd, policy=kind, counters=counters)
+        assert host(r.global_scale)[0] == g
+        assert_same(host(r.scales), s, "scales")
+        assert_same(host(r.codes), c, "codes")
+        if ch is not None:
+            assert_same(host(r.choice_bits), ch, "choice bits")
+        if counters:
+            assert_same(host(r.counters).astype(np.uint64), cnt, "counters")
+
+
 # ------------------------------------------------------------------ IF4
 def _if4_check(r, c, s, g, cnt=None):
     assert host(r.global_scale)[0] == g
@@ -702,21 +816,6 @@ def test_if4_rht_grad_8192():
     c, s, g, _, cnt = oracle.quantize_nv(rot, policy=4)
     _if4_check(r, c, s, g, cnt)
     assert np.count_nonzero(s & 0x80) > s.size // 4
-
-
-def test_if4_weight_8192x28672_sampled_rows():
-    x = workload("weight_bf16_8192x28672")
-    r = fq.quantize_nvfp4(to_dev(x), policy="if4")
-    amax = oracle.tensor_amax(x)
-    g_ref = np.float32(amax) / np.float32(2688)
-    assert host(r.global_scale)[0] == g_ref
-    codes, scales = host(r.codes), host(r.scales)
-    for r0 in (0, 4095, 8192 - 160):
-        r1 = r0 + 160
-        c, s, g, _, _ = oracle.quantize_nv(x[r0:r1], policy=4, global_amax=amax)
-        assert g == g_ref
-        assert_same(codes[r0:r1], c, "codes rows %d-%d" % (r0, r1))
-        assert_same(scales[r0:r1], s, "scales rows %d-%d" % (r0, r1))
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -920,6 +1019,28 @@ def test_mxfp4_gemm_nan_scale_and_exact_case():
     # row sums of B: every partial sum is a short dyadic number, exact in fp32
     ok = np.delete(np.arange(M), 3)
     assert np.array_equal(c[ok].astype(np.float64), ref[ok])
+
+
+@pytest.mark.parametrize("M,N", [(256, 256), (300, 520)])
+def test_mxfp4_gemm_exact_k8192(M, N):
+    """K = 8192 with every A and B scale byte 126 or 127 (exponents -1 and
+    0, varying per block): each product is a multiple of 2^-4 of magnitude at
+    most 36, so every partial sum is a multiple of 2^-4 below 36 * 8192 < 2^19,
+    i.e. fewer than 2^23 units: every summation order is exact in fp32.  The fp32 result equals the exact sum
+    and the bf16 result is its round-to-nearest-even."""
+    K = 8192
+    rng = np.random.default_rng(M + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asc = rng.integers(126, 128, (M, K // 32), dtype=np.uint8)
+    bsc = rng.integers(126, 128, (N, K // 32), dtype=np.uint8)
+    ref, absc = oracle.mx_gemm(ac, asc, bc, bsc)
+    assert np.abs(ref).max() < 2.0 ** 19                       # (2^23 units of 2^-4)
+    qa, qb = (to_dev(ac), to_dev(asc)), (to_dev(bc), to_dev(bsc))
+    c32 = host(fq.mxfp4_gemm(qa, qb)).astype(np.float64)
+    assert np.array_equal(c32, ref)
+    c16 = host(fq.mxfp4_gemm(qa, qb, out_dtype=torch.bfloat16))
+    assert_same(c16, f32_to_bf16_bits(ref.astype(np.float32)), "bf16 output")
 
 
 def test_mxfp4_gemm_8192_sampled_rows():
