@@ -19,7 +19,8 @@ FP4Q_ROUND_RNE, FP4Q_ROUND_STOCHASTIC = 0, 1
 FP4Q_ROT_NONE, FP4Q_ROT_FWHT_ROW, FP4Q_ROT_RHT16, FP4Q_ROT_FWHT128 = 0, 1, 2, 3
 
 EXPORTED = [
-    "fp4q_workspace_bytes", "fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_silu_mul_fwht_mxfp4", "fp4q_fwht",
+    "fp4q_workspace_bytes", "fp4q_quantize_mxfp4", "fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_noalloc",
+    "fp4q_silu_mul_fwht_mxfp4", "fp4q_fwht",
     "fp4q_dequantize", "fp4q_mxfp4_gemm", "fp4q_check_counters", "fp4q_status_string", "fp4q_version",
 ]
 
@@ -67,6 +68,8 @@ def load():
         lib.fp4q_quantize_mxfp4.restype = C.c_int
         lib.fp4q_quantize_nvfp4.argtypes = [C.POINTER(QuantArgs), vp, vp, C.POINTER(Outputs), vp, C.c_size_t, vp]
         lib.fp4q_quantize_nvfp4.restype = C.c_int
+        lib.fp4q_quantize_nvfp4_noalloc.argtypes = [C.POINTER(QuantArgs), vp, vp, C.POINTER(Outputs), vp]
+        lib.fp4q_quantize_nvfp4_noalloc.restype = C.c_int
         lib.fp4q_silu_mul_fwht_mxfp4.argtypes = [C.POINTER(QuantArgs), vp, vp, C.POINTER(Outputs), vp]
         lib.fp4q_silu_mul_fwht_mxfp4.restype = C.c_int
         lib.fp4q_fwht.argtypes = [i64, i64, i64, i32, vp, vp, i32, i32, u64, vp]

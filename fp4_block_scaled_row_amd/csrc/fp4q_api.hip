@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fp4q.h"
 #include "fp4q_common.h"
 #include "fp4q_internal.h"
@@ -28,7 +30,34 @@ int device_cu_count() {
 
 using namespace fp4q;
 
+// Scratch of fp4q_quantize_nvfp4_noalloc, for callers that cannot allocate:
+// the NVFP4 workspace as a file-scope device array, one copy on every GPU the
+// library runs on, held until the process ends.  It starts zeroed and needs
+// no clearing between calls (each single-read launch carries a fresh epoch;
+// the two-pass kernels write the partials they read).  In host code `scratch`
+// names a host-side stand-in: kernels get its device address from
+// hipGetSymbolAddress, kept per device (scratch_address).
+__device__ __align__(256) unsigned char scratch[kNvWorkspaceBytes];
+
 namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current.
+fp4q_status scratch_address(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP4Q_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return FP4Q_ERR_HIP;
+    g_scratch_dev[dev] = a;
+  }
+  *p = g_scratch_dev[dev];
+  return FP4Q_OK;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -208,6 +237,18 @@ fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args* args, const void* x, cons
   q.global_amax = global_amax;
   q.partials = static_cast<uint32_t*>(workspace);
   return hip_status(launch_nv_quant(q, static_cast<hipStream_t>(hip_stream)));
+}
+
+fp4q_status fp4q_quantize_nvfp4_noalloc(const fp4q_quant_args* args, const void* x, const float* global_amax,
+                                        const fp4q_outputs* out, void* hip_stream) {
+  if (!args) return FP4Q_ERR_INVALID_ARG;
+  // (the workspace an NVFP4 call needs does not grow with the tensor: the
+  // kernels cap their grids, so the scratch covers every size)
+  if (fp4q_workspace_bytes(args) > sizeof(scratch)) return FP4Q_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const fp4q_status st = scratch_address(&ws);
+  if (st != FP4Q_OK) return st;
+  return fp4q_quantize_nvfp4(args, x, global_amax, out, ws, sizeof(scratch), hip_stream);
 }
 
 fp4q_status fp4q_fwht(int64_t rows, int64_t d, int64_t in_row_stride, int32_t in_dtype, const void* x, float* y,

@@ -175,6 +175,24 @@ fp4q_status fp4q_quantize_nvfp4(const fp4q_quant_args *args, const void *x,
                                 const float *global_amax, const fp4q_outputs *out,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* fp4q_quantize_nvfp4 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, checks, results and
+ * errors as fp4q_quantize_nvfp4; the workspace is an 80 KiB scratch array
+ * that the library holds in device memory on every GPU it runs on until the
+ * process ends (its address is looked up on the first call made with that
+ * device current: the calling thread's current device must be the GPU of
+ * hip_stream).  It allocates nothing and frees nothing.  The scratch covers
+ * every tensor size (the NVFP4 workspace does not grow with the tensor); a
+ * workspace need above 80 KiB would be refused with FP4Q_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that overlap on one GPU (unordered streams, several
+ * host threads) race and must not be made; calls ordered on one stream, or
+ * synchronised, are safe.  Lookup failures return FP4Q_ERR_HIP. */
+fp4q_status fp4q_quantize_nvfp4_noalloc(const fp4q_quant_args *args, const void *x,
+                                        const float *global_amax, const fp4q_outputs *out,
+                                        void *hip_stream);
+
 /* Fused SwiGLU epilogue ("Sub-4-Bit Microscaling", section 3: the online
  * rotation inside the SiLU_and_Mul kernel right before down_proj): the
  * activation h = SiLU(gate) * up, SiLU(g) = g / (1 + e^-g), is formed in fp32
