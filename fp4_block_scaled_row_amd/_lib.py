@@ -9,7 +9,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfp4q.so")
+# FP4Q_LIB selects another build of the same sources (the sanitizer run of the
+# host-side tests loads a host-only AddressSanitizer/UBSan build this way)
+LIB_PATH = os.environ.get("FP4Q_LIB") or os.path.join(HERE, "libfp4q.so")
 
 FP4Q_OK, FP4Q_ERR_INVALID_ARG, FP4Q_ERR_UNSUPPORTED, FP4Q_ERR_WORKSPACE, FP4Q_ERR_NONFINITE, FP4Q_ERR_HIP = range(6)
 FP4Q_F32, FP4Q_BF16 = 0, 1

@@ -78,5 +78,34 @@ def build(verbose=False, jobs=None, incremental=False):
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD_DIR, "san", "libfp4q_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libsan",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized_host():
+    """A copy of the library whose host-side C ABI (fp4q_api.hip: argument
+    checks, workspace sizing, dispatch) is built with AddressSanitizer and
+    UBSan (host code only; the kernels' objects are those of build()), for
+    running the host-side tests under the sanitizers.  Needs build() first."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    api = os.path.join(os.path.dirname(SAN_LIB), "fp4q_api.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"] + SAN_FLAGS
+    r = subprocess.run([hipcc()] + flags + ["-c", os.path.join(CSRC, "fp4q_api.hip"), "-o", api],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc (sanitized) failed:\n%s" % r.stderr)
+    objs = [api] + [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "fp4q_api.hip"]
+    for o in objs[1:]:
+        if not os.path.exists(o):
+            raise RuntimeError("%s missing: run build() first" % o)
+    r = subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + SAN_FLAGS + ["-o", SAN_LIB] + objs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link (sanitized) failed:\n%s" % r.stderr)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True, incremental="--incremental" in sys.argv))

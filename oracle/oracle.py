@@ -13,7 +13,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "fp4_oracle.c")
-LIB = os.path.join(HERE, "libfp4oracle.so")
+# FP4Q_ORACLE_LIB selects another build of the same source (the sanitizer
+# run of the CPU tests loads an AddressSanitizer/UBSan build this way)
+LIB = os.environ.get("FP4Q_ORACLE_LIB") or os.path.join(HERE, "libfp4oracle.so")
 
 F32, BF16 = 0, 1
 MX, NV, IF4 = 0, 1, 2
@@ -33,11 +35,28 @@ def build(force=True):
     return LIB
 
 
+SAN_LIB = os.path.join(HERE, "libfp4oracle_san.so")
+
+
+def build_sanitized(cc="/opt/rocm/llvm/bin/clang"):
+    """The same source with AddressSanitizer and UBSan (clang, shared
+    sanitizer runtime, so that it can share a process with the sanitized
+    host build of the HIP library), for the sanitizer run of the CPU tests."""
+    tmp = SAN_LIB + ".tmp%d" % os.getpid()
+    cmd = [cc, "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan",
+           "-fno-omit-frame-pointer", SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            if not os.environ.get("FP4Q_ORACLE_LIB") and (not os.path.exists(LIB) or
+                                                          os.path.getmtime(LIB) < os.path.getmtime(SRC)):
                 build()
             lib = C.CDLL(LIB)
             i64, i32, u64, vp, dp = C.c_int64, C.c_int, C.c_uint64, C.c_void_p, C.c_double
