@@ -246,6 +246,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
 
     def timed(fn, n_calls=None):
         n = n_calls or steps
+        timer.settle(fn, 30)     # (the clock drops while the host prepares each workload)
         mean = timer.wall(fn, n, warmup)[1]
         return mean, timer.per_call(fn, n, 2)
 

@@ -104,21 +104,21 @@ def workspace_bytes(block_size):
     return int(_lib.load().fp4q_workspace_bytes(a))
 
 
-# One zero-filled NVFP4 workspace per (device, stream), kept for the life of
+# One zero-filled workspace per (format, device, stream), kept for the life of
 # the process: calls on one stream are ordered, which is all the library asks
 # of calls that share a workspace.
 _workspaces = {}
 
 
-def _default_workspace(dev):
+def _default_workspace(dev, block_size=16):
     stream = torch.cuda.current_stream(dev)
-    key = (dev.index if dev.index is not None else torch.cuda.current_device(), stream.cuda_stream)
+    key = (block_size, dev.index if dev.index is not None else torch.cuda.current_device(), stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None:
         if torch.cuda.is_current_stream_capturing():
-            raise RuntimeError("fp4q: no NVFP4 workspace exists yet for this stream; pass workspace= or make one "
+            raise RuntimeError("fp4q: no workspace exists yet for this stream; pass workspace= or make one "
                                "call on the stream before capturing it")
-        ws = torch.zeros(workspace_bytes(16), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(workspace_bytes(block_size), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -143,7 +143,10 @@ def quantize_mxfp4(x, *, policy="ocp", manual_exponent=0, rounding="rne", seed=0
         out = MxResult(codes, scales, rot, cnt)
     _check_mx_out(out, rows, cols)
     o = _lib.Outputs(_ptr(out.codes), _ptr(out.scales), None, None, _ptr(out.rotated), _ptr(out.counters))
-    _lib.check(_lib.load().fp4q_quantize_mxfp4(a, _ptr(x), o, None, 0, _stream()), "fp4q_quantize_mxfp4")
+    # (a counting call sums its counts through the workspace's counter slots)
+    ws = _default_workspace(dev, 32) if out.counters is not None and rows * cols > 0 else None
+    ws_bytes = 0 if ws is None else ws.numel()
+    _lib.check(_lib.load().fp4q_quantize_mxfp4(a, _ptr(x), o, _ptr(ws), ws_bytes, _stream()), "fp4q_quantize_mxfp4")
     return out
 
 

@@ -131,16 +131,18 @@ extern "C" {
 size_t fp4q_workspace_bytes(const fp4q_quant_args* args) {
   if (!args) return 0;
   if (args->block_size == 16) return kNvWorkspaceBytes;
+  if (args->block_size == 32) return kMxWorkspaceBytes;
   return 0;
 }
 
 fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args* args, const void* x, const fp4q_outputs* out,
                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   fp4q_status st = check_quant(args, x, out, FP4Q_MXFP4);
   if (st != FP4Q_OK) return st;
   if (args->rotation == FP4Q_ROT_FWHT128) return FP4Q_ERR_UNSUPPORTED;
+  // the workspace (optional) holds the counter slots of a counting call
+  if (workspace && (workspace_bytes < kMxWorkspaceBytes || !aligned(workspace, 8))) return FP4Q_ERR_WORKSPACE;
+  unsigned long long* slots = (workspace && out->counters) ? static_cast<unsigned long long*>(workspace) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const int64_t n = args->rows * args->cols;
   if (args->rotation == FP4Q_ROT_FWHT_ROW) {
@@ -164,14 +166,16 @@ fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args* args, const void* x, cons
     f.codes = out->codes;
     f.scales = out->scales;
     f.counters = reinterpret_cast<unsigned long long*>(out->counters);
-    if (f.counters) {
+    f.count_slots = slots;
+    if (f.counters && !slots) {
       hipError_t e = launch_zero_counters(f.counters, s);
       if (e != hipSuccess) return FP4Q_ERR_HIP;
     }
     return hip_status(launch_fwht(f, s));
   }
   QuantLaunch q = make_launch(args, x, out);
-  if (q.counters) {
+  q.count_slots = slots;
+  if (q.counters && (!slots || n == 0)) {
     hipError_t e = launch_zero_counters(q.counters, s);
     if (e != hipSuccess) return FP4Q_ERR_HIP;
   }

@@ -152,11 +152,14 @@ __device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float
   p[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Adds a thread's saturated, underflowed and non-finite counts to the three
-// global counters: wave sums, then the workgroup's sums in LDS, then one
-// atomic add per nonzero counter per workgroup.  Every thread of the
-// workgroup calls it (it synchronises).
-__device__ __forceinline__ void flush_counters(unsigned long long* c, uint32_t sat, uint32_t und, uint32_t nf) {
+// Adds a thread's saturated, underflowed and non-finite counts to the
+// counters: wave sums, then the workgroup's sums in LDS, then one atomic add
+// per nonzero count per workgroup -- into the workgroup's counter slot
+// (slots[3 (b % kCountSlots) + k], summed afterwards by count_reduce_kernel)
+// when slots is given, else straight into the three counters.  Every thread
+// of the workgroup calls it (it synchronises).
+__device__ __forceinline__ void flush_counters(unsigned long long* c, unsigned long long* slots, uint32_t sat,
+                                               uint32_t und, uint32_t nf) {
   __shared__ unsigned long long s_cnt[3];
   const unsigned long long a = wave_sum_u64(sat), b = wave_sum_u64(und), d = wave_sum_u64(nf);
   if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0ull;
@@ -169,7 +172,8 @@ __device__ __forceinline__ void flush_counters(unsigned long long* c, uint32_t s
   __syncthreads();
   if (threadIdx.x < 3) {
     const unsigned long long v = s_cnt[threadIdx.x];
-    if (v) atomicAdd(c + threadIdx.x, v);
+    unsigned long long* dst = slots ? slots + 3 * (blockIdx.x % kCountSlots) + threadIdx.x : c + threadIdx.x;
+    if (v) atomicAdd(dst, v);
   }
 }
 

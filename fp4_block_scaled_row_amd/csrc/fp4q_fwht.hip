@@ -161,7 +161,7 @@ __global__ __launch_bounds__(128) void fwht8192_kernel(FwhtLaunch f, float c) {
                                           n_sat, n_und, n_nf);
     }
   }
-  if constexpr (COUNT) flush_counters(f.counters, n_sat, n_und, n_nf);
+  if constexpr (COUNT) flush_counters(f.counters, f.count_slots, n_sat, n_und, n_nf);
 }
 
 // ---------------------------------------------------------------- generic LDS
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void fwht_lds_kernel(FwhtLaunch f, int lo
                                           n_sat, n_und, n_nf);
     }
   }
-  if constexpr (COUNT) flush_counters(f.counters, n_sat, n_und, n_nf);
+  if constexpr (COUNT) flush_counters(f.counters, f.count_slots, n_sat, n_und, n_nf);
 }
 
 // ---------------------------------------------------------------- t <= 16
@@ -324,7 +324,15 @@ hipError_t launch_small(const FwhtLaunch& f, hipStream_t st, float c) {
 
 }  // namespace
 
+hipError_t launch_fwht_rows(const FwhtLaunch& f, hipStream_t st);
+
 hipError_t launch_fwht(const FwhtLaunch& f, hipStream_t st) {
+  const hipError_t e = launch_fwht_rows(f, st);
+  if (e != hipSuccess || !f.quantize || !f.counters || !f.count_slots || f.rows == 0 || f.d == 0) return e;
+  return launch_count_reduce(f.count_slots, f.counters, st);
+}
+
+hipError_t launch_fwht_rows(const FwhtLaunch& f, hipStream_t st) {
   if (f.rows == 0 || f.d == 0) return hipSuccess;
   const float c = (float)(1.0 / sqrt((double)f.t));
   int log2t = 0;

@@ -30,6 +30,7 @@ struct QuantLaunch {
   unsigned long long* counters;
   const float* global_amax;  // NV: caller-supplied amax (device) or null
   uint32_t* partials;        // NV: per-workgroup amax partials (workspace)
+  unsigned long long* count_slots;  // counter slots in the workspace, or null (atomics into counters)
 };
 
 constexpr int kAmaxPartialsMax = 1024;  // workgroups of the NV amax pass
@@ -45,7 +46,20 @@ constexpr size_t kWsResultStrideBytes = 4096;
 constexpr int kWsResultCopies = 16;
 constexpr size_t kNvWorkspaceBytes = kWsResultsOffsetBytes + kWsResultStrideBytes * kWsResultCopies;
 
+// Counter slots: a counting kernel's workgroup b adds its three counts into
+// slot b % kCountSlots (few workgroups per address, unlike one set of three
+// global words), and a one-workgroup kernel sums the slots into the counters
+// and zeroes them again.  NV: at [12352, 15424) of the NV workspace; MX: at
+// the start of its own kMxWorkspaceBytes workspace.
+constexpr int kCountSlots = 128;
+constexpr size_t kCountSlotBytes = (size_t)kCountSlots * 3 * 8;
+constexpr size_t kWsCountOffsetBytes = kWsPartialsOffsetBytes + 4 * kAmaxPartialsMax;
+static_assert(kWsCountOffsetBytes + kCountSlotBytes <= kWsResultsOffsetBytes, "NV workspace layout");
+constexpr size_t kMxWorkspaceBytes = 4096;
+static_assert(kCountSlotBytes <= kMxWorkspaceBytes, "MX workspace layout");
+
 hipError_t launch_zero_counters(unsigned long long* counters, hipStream_t s);
+hipError_t launch_count_reduce(unsigned long long* slots, unsigned long long* counters, hipStream_t s);
 hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_nv_quant(const QuantLaunch& q, hipStream_t s);
 bool nv_resident_shape(const QuantLaunch& q, int* grid, int* nres);
@@ -70,6 +84,7 @@ struct FwhtLaunch {
   uint8_t* codes;
   uint8_t* scales;
   unsigned long long* counters;
+  unsigned long long* count_slots;   // counter slots in the workspace, or null
 };
 hipError_t launch_fwht(const FwhtLaunch& f, hipStream_t s);
 

@@ -90,11 +90,33 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(QuantLaunch q) {
       }
     }
   }
-  if constexpr (COUNT) flush_counters(q.counters, n_sat, n_und, n_nf);
+  if constexpr (COUNT) flush_counters(q.counters, q.count_slots, n_sat, n_und, n_nf);
 }
 
 __global__ void zero_counters_kernel(unsigned long long* c) {
   if (threadIdx.x < 3) c[threadIdx.x] = 0ull;
+}
+
+// counters[k] = sum of the slots' count k, by one wave: lane l reads slots
+// 2l and 2l+1 (six 8-byte words: the workspace is only 8-byte aligned), the
+// wave sums, lane 0 writes the counters; the slots are zeroed for the next
+// call.
+static_assert(kCountSlots == 128, "one wave, two slots per lane");
+__global__ __launch_bounds__(64) void count_reduce_kernel(unsigned long long* slots, unsigned long long* c) {
+  const int l = threadIdx.x;
+  unsigned long long* p = slots + 6 * l;
+  unsigned long long v[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) v[i] = p[i];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) p[i] = 0ull;
+  const unsigned long long k0 = wave_sum_u64(v[0] + v[3]), k1 = wave_sum_u64(v[1] + v[4]),
+                           k2 = wave_sum_u64(v[2] + v[5]);
+  if (l == 0) {
+    c[0] = k0;
+    c[1] = k1;
+    c[2] = k2;
+  }
 }
 
 template <int IN, int ROT, bool SR, bool COUNT, bool CONTIG, bool MANUAL>
@@ -144,9 +166,16 @@ hipError_t launch_zero_counters(unsigned long long* counters, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_count_reduce(unsigned long long* slots, unsigned long long* counters, hipStream_t st) {
+  hipLaunchKernelGGL(count_reduce_kernel, dim3(1), dim3(64), 0, st, slots, counters);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t st) {
   if (q.nslots == 0) return hipSuccess;
-  return q.in_dtype == kF32 ? dispatch_rot<kF32>(q, st) : dispatch_rot<kBF16>(q, st);
+  const hipError_t e = q.in_dtype == kF32 ? dispatch_rot<kF32>(q, st) : dispatch_rot<kBF16>(q, st);
+  if (e != hipSuccess || !q.counters || !q.count_slots) return e;
+  return launch_count_reduce(q.count_slots, q.counters, st);
 }
 
 }  // namespace fp4q

@@ -97,7 +97,6 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
     for (int w = 1; w < kWaves; ++w) m = max(m, s_red[w]);
     q.partials[blockIdx.x] = m;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 3 && q.counters) q.counters[threadIdx.x] = 0ull;
 }
 
 template <int IN, int ROT, bool SR, int POL, bool COUNT, bool CONTIG>
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       }
     }
   }
-  if constexpr (COUNT) flush_counters(q.counters, n_sat, n_und, n_nf);
+  if constexpr (COUNT) flush_counters(q.counters, q.count_slots, n_sat, n_und, n_nf);
 }
 
 // Streaming max->6 round-to-nearest encode of contiguous bf16 (no rotation,
@@ -375,7 +374,8 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
     hipLaunchKernelGGL((nv_amax_kernel<IN, ROT, CONTIG>), dim3(np), dim3(kThreads), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-  } else if (q.counters) {
+  }
+  if (q.counters && !q.count_slots) {
     hipError_t e = launch_zero_counters(q.counters, st);
     if (e != hipSuccess) return e;
   }
@@ -389,7 +389,9 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, POL, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !COUNT || !q.count_slots) return e;
+  return launch_count_reduce(q.count_slots, q.counters, st);
 }
 
 template <int IN, int ROT, bool SR, int POL, bool COUNT>
@@ -434,7 +436,11 @@ hipError_t launch_nv_quant(const QuantLaunch& q0, hipStream_t st) {
   QuantLaunch q = q0;
   int grid = 0, nres = 0;
   if (q.partials && nv_resident_shape(q, &grid, &nres)) return launch_nv_resident(q, grid, nres, st);
-  if (q.partials) q.partials += kWsPartialsOffsetBytes / sizeof(uint32_t);
+  if (q.partials) {
+    unsigned char* ws = reinterpret_cast<unsigned char*>(q.partials);
+    if (q.counters) q.count_slots = reinterpret_cast<unsigned long long*>(ws + kWsCountOffsetBytes);
+    q.partials = reinterpret_cast<uint32_t*>(ws + kWsPartialsOffsetBytes);
+  }
   // (an empty tensor still runs both passes: g = 1 is reported, counters zeroed)
   return q.in_dtype == kF32 ? d_rot<kF32>(q, st) : d_rot<kBF16>(q, st);
 }

@@ -120,7 +120,12 @@ typedef struct {
                            /* [2] non-finite inputs                                           */
 } fp4q_outputs;
 
-/* Bytes of device workspace a quantize call needs (0 if none).  The NVFP4
+/* Bytes of device workspace a quantize call uses.  MXFP4 (block 32): 4 KiB,
+ * optional, 8-byte aligned, zero-filled before its first use: a counting call
+ * given one sums its counts through 128 slots in it (one atomic add per
+ * count per workgroup into slot b mod 128, then a one-workgroup kernel that
+ * writes the counters and clears the slots) instead of adding every
+ * workgroup's counts into the three counters directly.  The NVFP4
  * workspace (80 KiB, 8-byte aligned) belongs to the caller, must be
  * zero-filled before its first use and is then kept consistent by the
  * library, also across launches captured in a HIP graph and replayed (a
@@ -139,7 +144,9 @@ size_t fp4q_workspace_bytes(const fp4q_quant_args *args);
  * 32, policy OCP_MAX or MANUAL, rotation NONE / FWHT_ROW (cols a power of two
  * between 32 and 16384) / RHT16, rounding RNE or STOCHASTIC.  The fp32
  * rotated values are what gets quantized; `rotated`, when given, receives
- * them.  Sources: audit page sections cited above. */
+ * them.  workspace may be NULL; when given it must hold
+ * fp4q_workspace_bytes() bytes, 8-byte aligned (else FP4Q_ERR_WORKSPACE).
+ * Sources: audit page sections cited above. */
 fp4q_status fp4q_quantize_mxfp4(const fp4q_quant_args *args, const void *x,
                                 const fp4q_outputs *out, void *workspace,
                                 size_t workspace_bytes, void *hip_stream);

@@ -62,6 +62,8 @@ def test_workspace_bytes():
     a.block_size = 16
     assert lib.fp4q_workspace_bytes(a) == 80 * 1024   # the layout include/fp4q.h documents
     a.block_size = 32
+    assert lib.fp4q_workspace_bytes(a) == 4096                 # counter slots (optional)
+    a.block_size = 8
     assert lib.fp4q_workspace_bytes(a) == 0
 
 
@@ -98,6 +100,13 @@ OUTS = _lib.Outputs(FAKE, FAKE, FAKE, FAKE, None, None)
 def test_mxfp4_rejects(kwargs, status):
     lib = _lib_or_skip()
     assert lib.fp4q_quantize_mxfp4(_args(**kwargs), FAKE, OUTS, None, 0, None) == status
+
+
+def test_mxfp4_workspace_checked_when_given():
+    lib = _lib_or_skip()
+    o = _lib.Outputs(FAKE, FAKE, None, None, None, FAKE)
+    assert lib.fp4q_quantize_mxfp4(_args(), FAKE, o, FAKE, 64, None) == _lib.FP4Q_ERR_WORKSPACE      # too small
+    assert lib.fp4q_quantize_mxfp4(_args(), FAKE, o, FAKE + 4, 4096, None) == _lib.FP4Q_ERR_WORKSPACE  # misaligned
 
 
 @pytest.mark.parametrize("kwargs,status", [

@@ -1053,3 +1053,27 @@ def test_mxfp4_gemm_8192_sampled_rows():
     for r0 in (0, 4093, 8192 - 3):
         ref, absc = oracle.mx_gemm(ac, asc, bc, bsc, rows=(r0, 3))
         _gemm_check(c[r0:r0 + 3], ref, absc, 8192)
+
+
+def test_mx_counters_without_workspace_through_the_abi():
+    """A counting MXFP4 call with no workspace adds each workgroup's counts
+    straight into the counters (the binding always passes its workspace, so
+    this path is driven through the C ABI)."""
+    from fp4_block_scaled_row_amd import _lib
+    lib = _lib.load()
+    x = workload("mx_f32_1024")
+    xd = to_dev(x)
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=xd.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=xd.device)
+    cnt = torch.full((3,), 12345, dtype=torch.int64, device=xd.device)
+    a = _lib.QuantArgs()
+    a.rows, a.cols, a.in_row_stride = rows, cols, cols
+    a.in_dtype, a.block_size, a.scale_policy = _lib.FP4Q_F32, 32, _lib.FP4Q_SCALE_OCP_MAX
+    o = _lib.Outputs(codes.data_ptr(), scales.data_ptr(), None, None, None, cnt.data_ptr())
+    for _ in range(2):                       # counters start from zero on every call
+        st = lib.fp4q_quantize_mxfp4(a, xd.data_ptr(), o, None, 0, torch.cuda.current_stream().cuda_stream)
+        assert st == _lib.FP4Q_OK
+        c, s, ref = oracle.quantize_mx(x)
+        assert_same(host(codes), c, "codes")
+        assert_same(host(cnt).astype(np.uint64), ref, "counters")
