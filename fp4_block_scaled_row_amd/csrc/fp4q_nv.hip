@@ -358,6 +358,219 @@ __global__ __launch_bounds__(kThreads) void nv_fast_kernel(QuantLaunch q, int np
   }
 }
 
+// Half of a block's SSE (half_sse's frozen fp32 order) with the scale value
+// sd given instead of its code.
+__device__ __forceinline__ float half_sse_sd(const float v[8], uint32_t codes, float sd, float g) {
+#pragma clang fp contract(off)
+  const float one = e8m0_operand(127u);
+  float val[8];
+  float2_t p;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0); val[0] = p.x; val[1] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1); val[2] = p.x; val[3] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2); val[4] = p.x; val[5] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3); val[6] = p.x; val[7] = p.y;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float vs = val[i] * sd;
+    const float dq = vs * g;
+    const float d = v[i] - dq;
+    const float sq = d * d;
+    acc = acc + sq;
+  }
+  return acc;
+}
+
+// Four Over Six of one 16-block held by a lane pair (8 values v per lane,
+// the even lane elements 0..7), by the exact general steps: both scale
+// bytes, both candidates by bracketed products with exact decisions, the
+// frozen-order SSEs summed over the pair (S_lo + S_hi), max->4 kept iff its
+// SSE is lower; a block holding a non-finite value gets codes 0, scale 0x7F,
+// max->6.  Both lanes of the pair must run it together.
+__device__ __forceinline__ void fos_block_exact(const float v[8], bool odd, const NvCtx& cx, const float2* s_br,
+                                                uint32_t& codes, uint32_t& sbyte, bool& pick4) {
+  uint32_t bm = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bm = max(bm, as_u(v[i]) & 0x7FFFFFFFu);
+  bm = max(bm, dpp_u32<kQuadXor1>(bm));
+  const bool nonfinite = bm >= 0x7F800000u;
+  const float bamax = as_f(bm);
+  const U4 none = {0u, 0u, 0u, 0u};
+  uint32_t sat;
+  const uint32_t c6 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all, 6.0f, cx.g);
+  const uint32_t c4 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv4_lo, cx.inv4_hi, cx.inv4, cx.mg4, cx.exact_all, 4.0f, cx.g);
+  const uint32_t k6 = nv_encode<false, false>(v, c6, cx, s_br, none, sat);
+  const uint32_t k4 = nv_encode<false, false>(v, c4, cx, s_br, none, sat);
+  float e6 = half_sse(v, k6, c6, cx.g), e4 = half_sse(v, k4, c4, cx.g);
+  const float p6 = dpp_xor1_f(e6), p4 = dpp_xor1_f(e4);
+  e6 = odd ? (p6 + e6) : (e6 + p6);
+  e4 = odd ? (p4 + e4) : (e4 + p4);
+  pick4 = (e4 < e6) && !nonfinite;
+  codes = nonfinite ? 0u : (pick4 ? k4 : k6);
+  sbyte = nonfinite ? 0x7Fu : (pick4 ? c4 : c6);
+}
+
+// 32 choice bits of a 64-lane ballot taken on the even (SEL = 0) or odd
+// (SEL = 1) lanes: bit k = lane 2k + SEL.
+template <int SEL>
+__device__ __forceinline__ uint32_t pair_bits(uint64_t bal) {
+  bal = (bal >> SEL) & 0x5555555555555555ull;
+  bal = (bal | (bal >> 1)) & 0x3333333333333333ull;
+  bal = (bal | (bal >> 2)) & 0x0F0F0F0F0F0F0F0Full;
+  bal = (bal | (bal >> 4)) & 0x00FF00FF00FF00FFull;
+  bal = (bal | (bal >> 8)) & 0x0000FFFF0000FFFFull;
+  bal = (bal | (bal >> 16)) & 0x00000000FFFFFFFFull;
+  return (uint32_t)bal;
+}
+
+// Streaming Four Over Six of contiguous bf16 rounded to nearest, without
+// counters: the straight-line paired layout of nv_fast_kernel (lanes 2k and
+// 2k+1 hold block k of two tiles; the even lane works out the first tile's
+// block scales, the odd lane the second's, and they pass each other the
+// multipliers and scale values).  Per element: one product per candidate
+// with the adjusted multiplier of its scale byte (one table serves both, it
+// depends on s g only), the FP4 conversion, and the frozen-order SSE of each
+// candidate.  A block whose scale brackets disagree or whose byte is flagged
+// (in either candidate; non-finite blocks convert to a flagged NaN byte) is
+// redone by fos_block_exact, both lanes of its pair together; with
+// g < 2^-100 every block is.  Same bytes as nv_quant_kernel's Four Over Six.
+__global__ __launch_bounds__(kThreads) void nv_fos_fast_kernel(QuantLaunch q, int npartials) {
+  __shared__ float2 s_adj[256];
+  __shared__ float2 s_br[128];
+  __shared__ float4 s_eps[8];
+  __shared__ uint32_t s_red[kWaves];
+  const int lane = threadIdx.x & 63;
+  uint32_t amax_bits;
+  if (q.global_amax) {
+    amax_bits = as_u(fabsf(*q.global_amax));
+  } else {
+    uint32_t m = 0u;
+    for (int i = threadIdx.x; i < npartials; i += kThreads) m = max(m, q.partials[i]);
+    m = wave_max_u32(m);
+    if (lane == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, s_red[w]);
+    amax_bits = m;
+  }
+  NvCtx cx;
+  nv_context(as_f(amax_bits), true, cx);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
+  const bool exact_all = cx.exact_all;
+  nv_fill_adjusted_table<256>(s_adj, s_br, s_eps, cx, threadIdx.x);
+  __syncthreads();
+
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int64_t ntiles = (q.nslots + 63) >> 6;
+  const int64_t nblk = q.nslots >> 1;
+  const bool odd = (lane & 1) != 0;
+  const uint16_t* xs = static_cast<const uint16_t*>(q.x);
+  const float one = e8m0_operand(127u);
+  for (int64_t grp = wave; grp * 4 < ntiles; grp += nwaves) {
+    const int64_t t0 = grp * 4;
+    uint4 w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t s = ((t0 + r) << 6) + lane;
+      if (s < q.nslots) {
+        const u32x4_t a = load16<true>(xs + (s << 3));
+        w[r] = make_uint4(a.x, a.y, a.z, a.w);
+      } else {
+        w[r] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint4 w0 = w[2 * p], w1 = w[2 * p + 1];
+      const int64_t ta = t0 + 2 * p;              // tiles ta (this lane's w0) and ta + 1 (w1)
+      const int64_t s0 = (ta << 6) + lane, s1 = s0 + 64;
+      float xa[8] = {bf_lo(w0.x), bf_hi(w0.x), bf_lo(w0.y), bf_hi(w0.y), bf_lo(w0.z), bf_hi(w0.z), bf_lo(w0.w), bf_hi(w0.w)};
+      float xb[8] = {bf_lo(w1.x), bf_hi(w1.x), bf_lo(w1.y), bf_hi(w1.y), bf_lo(w1.z), bf_hi(w1.z), bf_lo(w1.w), bf_hi(w1.w)};
+      uint32_t ca = 0u, cb = 0u, sbyte = 0u;
+      bool pa = false, pb = false, need_a = true, need_b = true;
+      if (!exact_all) {
+        const uint32_t m0 = slot_max16(w0), m1 = slot_max16(w1);
+        const uint32_t own = odd ? m1 : m0, give = odd ? m0 : m1;
+        const float bamax = as_f(max(own, dpp_u32<kQuadXor1>(give)) << 16);
+        // both scale bytes of the block this lane works out, from their brackets
+        const uint32_t b6 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(bamax * cx.inv6_lo, bamax * cx.inv6_hi, 0, false);
+        const uint32_t b4 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(bamax * cx.inv4_lo, bamax * cx.inv4_hi, 0, false);
+        const float2 e6 = s_adj[b6 & 0xFFu], e4 = s_adj[b4 & 0xFFu];
+        const uint32_t need = (__builtin_amdgcn_alignbit(b6, b6, 9) ^ (b6 << 31)) | as_u(e6.y) |
+                              (__builtin_amdgcn_alignbit(b4, b4, 9) ^ (b4 << 31)) | as_u(e4.y);
+        const float sd6 = e4m3_value(b6 & 0x7Fu), sd4 = e4m3_value(b4 & 0x7Fu);
+        // block A (tile ta) was worked out by the even lane, block B by the odd one
+        const float ma6 = as_f(dpp_u32<kQuadEven>(as_u(e6.x))), mb6 = as_f(dpp_u32<kQuadOdd>(as_u(e6.x)));
+        const float ma4 = as_f(dpp_u32<kQuadEven>(as_u(e4.x))), mb4 = as_f(dpp_u32<kQuadOdd>(as_u(e4.x)));
+        const float sa6 = as_f(dpp_u32<kQuadEven>(as_u(sd6))), sb6 = as_f(dpp_u32<kQuadOdd>(as_u(sd6)));
+        const float sa4 = as_f(dpp_u32<kQuadEven>(as_u(sd4))), sb4 = as_f(dpp_u32<kQuadOdd>(as_u(sd4)));
+        need_a = (dpp_u32<kQuadEven>(need) >> 31) != 0u;
+        need_b = (dpp_u32<kQuadOdd>(need) >> 31) != 0u;
+        uint32_t a6 = 0u, a4 = 0u, c6 = 0u, c4 = 0u;
+#define FP4Q_FOS_WORD(K)                                                                            \
+  a6 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a6, xa[2 * K] * ma6, xa[2 * K + 1] * ma6, one, K);  \
+  a4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a4, xa[2 * K] * ma4, xa[2 * K + 1] * ma4, one, K);  \
+  c6 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c6, xb[2 * K] * mb6, xb[2 * K + 1] * mb6, one, K);  \
+  c4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c4, xb[2 * K] * mb4, xb[2 * K + 1] * mb4, one, K);
+        FP4Q_FOS_WORD(0)
+        FP4Q_FOS_WORD(1)
+        FP4Q_FOS_WORD(2)
+        FP4Q_FOS_WORD(3)
+#undef FP4Q_FOS_WORD
+        float ea6 = half_sse_sd(xa, a6, sa6, cx.g), ea4 = half_sse_sd(xa, a4, sa4, cx.g);
+        float eb6 = half_sse_sd(xb, c6, sb6, cx.g), eb4 = half_sse_sd(xb, c4, sb4, cx.g);
+        // S_lo (even lane) + S_hi (odd lane), the same sum on both lanes
+        {
+          const float q1 = dpp_xor1_f(ea6), q2 = dpp_xor1_f(ea4), q3 = dpp_xor1_f(eb6), q4 = dpp_xor1_f(eb4);
+          ea6 = odd ? (q1 + ea6) : (ea6 + q1);
+          ea4 = odd ? (q2 + ea4) : (ea4 + q2);
+          eb6 = odd ? (q3 + eb6) : (eb6 + q3);
+          eb4 = odd ? (q4 + eb4) : (eb4 + q4);
+        }
+        pa = ea4 < ea6;
+        pb = eb4 < eb6;
+        ca = pa ? a4 : a6;
+        cb = pb ? c4 : c6;
+        const bool pw = odd ? pb : pa;                       // the block this lane worked out
+        sbyte = pw ? (b4 & 0xFFu) : (b6 & 0xFFu);
+      }
+      if (need_a) {
+        uint32_t sba = 0u;
+        fos_block_exact(xa, odd, cx, s_br, ca, sba, pa);
+        if (!odd) sbyte = sba;
+      }
+      if (need_b) {
+        uint32_t sbb = 0u;
+        fos_block_exact(xb, odd, cx, s_br, cb, sbb, pb);
+        if (odd) sbyte = sbb;
+      }
+      if (s0 < q.nslots) __builtin_nontemporal_store(ca, reinterpret_cast<uint32_t*>(q.codes) + s0);
+      if (s1 < q.nslots) __builtin_nontemporal_store(cb, reinterpret_cast<uint32_t*>(q.codes) + s1);
+      const int64_t tb = ta + (odd ? 1 : 0);             // the block this lane worked out: tile tb, block lane / 2
+      if ((tb << 6) + (lane & ~1) < q.nslots) q.scales[(tb << 5) + (lane >> 1)] = (uint8_t)sbyte;
+      // choice bits of tiles ta and ta + 1: block k of a tile is bit k of its 32-bit word
+      const uint64_t bal = __ballot(odd ? pb : pa);
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t b0 = (ta + h) << 5;              // first block of the tile
+          if (b0 >= nblk) break;
+          const uint32_t bits = h ? pair_bits<1>(bal) : pair_bits<0>(bal);
+          const int64_t nb = (nblk - b0) < 32 ? (nblk - b0) : 32;
+          uint8_t* dst = q.choice_bits + (b0 >> 3);
+          if (nb == 32) {
+            *reinterpret_cast<uint32_t*>(dst) = bits;
+          } else {
+            for (int k = 0; k < (int)((nb + 7) >> 3); ++k) dst[k] = (uint8_t)(bits >> (8 * k));
+          }
+        }
+      }
+    }
+  }
+}
+
 int amax_grid(int64_t nslots) {
   const int64_t ntiles = (nslots + 63) >> 6;
   int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
@@ -386,6 +599,8 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   if constexpr (IN == kBF16 && ROT == kRotNone && !SR && POL == kPolMax6 && !COUNT && CONTIG) {
     static_assert(kUnroll == 4, "nv_fast_kernel takes four tiles per wave iteration");
     hipLaunchKernelGGL(nv_fast_kernel, dim3(grid), dim3(kThreads), 0, st, q, np);
+  } else if constexpr (IN == kBF16 && ROT == kRotNone && !SR && POL == kPolFos && !COUNT && CONTIG) {
+    hipLaunchKernelGGL(nv_fos_fast_kernel, dim3(grid), dim3(kThreads), 0, st, q, np);
   } else {
     hipLaunchKernelGGL((nv_quant_kernel<IN, ROT, SR, POL, COUNT, CONTIG>), dim3(grid), dim3(kThreads), 0, st, q, np);
   }

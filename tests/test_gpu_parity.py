@@ -370,6 +370,31 @@ def test_nv_tiny_and_huge_tensors(scale_exp):
         assert_same(bits(host(d)), bits(oracle.dequantize(oracle.NV, c, s, g)), "dequant fp32")
 
 
+@pytest.mark.parametrize("scale_exp", [None, -140, -101, -60, 0, 100, 120])
+def test_four_over_six_streaming_specials_tiny_huge(scale_exp):
+    """Four Over Six of contiguous bf16 without counters (the streaming
+    kernel): non-finite, zero and subnormal blocks, and tensors whose g is
+    below 2^-100 (every block on the exact path) or near the top of the range,
+    with ragged tile counts and a caller amax."""
+    if scale_exp is None:
+        x = _special_tensor("bf16")
+    else:
+        rng = np.random.default_rng(scale_exp + 700)
+        x = f32_to_bf16_bits(np.ldexp(rng.standard_t(4, (24, 96)), scale_exp).astype(np.float32))
+    c, s, g, ch, _ = oracle.quantize_nv(x, policy=3)
+    xd = to_dev(x)
+    r = fq.quantize_nvfp4(xd, policy="four_over_six")
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+    assert_same(host(r.choice_bits), ch, "choice bits")
+    amax = oracle.tensor_amax(x)
+    r = fq.quantize_nvfp4(xd, policy="four_over_six", global_amax=torch.tensor([amax], dtype=torch.float32,
+                                                                              device=xd.device))
+    assert_same(host(r.codes), c, "codes (caller amax)")
+    assert_same(host(r.choice_bits), ch, "choice bits (caller amax)")
+
+
 def test_nv_exact_ties_and_caller_amax():
     mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
     x = np.zeros((2, 64), np.float32)
@@ -621,13 +646,15 @@ def test_nv_exhaustive_scale_codes_and_magnitudes(amax):
     r = fq.quantize_nvfp4(xd, global_amax=amax_dev)             # caller amax, encode pass only
     assert_same(host(r.scales), s, "scales (caller amax)")
     assert_same(host(r.codes), c, "codes (caller amax)")
-    r = fq.quantize_nvfp4(xd, policy="four_over_six", counters=True)
     c4, s4, g4, ch4, cnt4 = oracle.quantize_nv(x, policy=3)
-    assert host(r.global_scale)[0] == g4
-    assert_same(host(r.scales), s4, "scales (four over six)")
-    assert_same(host(r.codes), c4, "codes (four over six)")
-    assert_same(host(r.choice_bits), ch4, "choice bits (four over six)")
-    assert_same(host(r.counters).astype(np.uint64), cnt4, "counters (four over six)")
+    for counters in (True, False):      # (without counters: the streaming Four Over Six kernel)
+        r = fq.quantize_nvfp4(xd, policy="four_over_six", counters=counters)
+        assert host(r.global_scale)[0] == g4
+        assert_same(host(r.scales), s4, "scales (four over six, counters %s)" % counters)
+        assert_same(host(r.codes), c4, "codes (four over six, counters %s)" % counters)
+        assert_same(host(r.choice_bits), ch4, "choice bits (four over six, counters %s)" % counters)
+        if counters:
+            assert_same(host(r.counters).astype(np.uint64), cnt4, "counters (four over six)")
     seed = 0xC0FFEE
     cs, ss, gs_, _, cnts = oracle.quantize_nv(x, rounding=1, seed=seed)
     r = fq.quantize_nvfp4(xd, rounding="stochastic", seed=seed, counters=True)
