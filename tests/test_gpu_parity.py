@@ -820,7 +820,9 @@ def test_if4_exhaustive_scale_codes_and_magnitudes(amax):
     c, s, g, _, cnt = oracle.quantize_nv(x, policy=4)
     if amax > 1.0:   # (at 2^-95 every squared error underflows in fp32: the SSEs tie and FP4 is kept)
         assert np.count_nonzero(s & 0x80) > 0
-    _if4_check(fq.quantize_nvfp4(to_dev(x), policy="if4", counters=True), c, s, g, cnt)
+    xd = to_dev(x)
+    _if4_check(fq.quantize_nvfp4(xd, policy="if4", counters=True), c, s, g, cnt)
+    _if4_check(fq.quantize_nvfp4(xd, policy="if4"), c, s, g)          # the streaming IF4 kernel
 
 
 def test_if4_specials_and_empty():
@@ -828,6 +830,12 @@ def test_if4_specials_and_empty():
         x = _special_tensor(dtype)
         c, s, g, _, cnt = oracle.quantize_nv(x, policy=4)
         _if4_check(fq.quantize_nvfp4(to_dev(x), policy="if4", counters=True), c, s, g, cnt)
+        _if4_check(fq.quantize_nvfp4(to_dev(x), policy="if4"), c, s, g)
+    rng = np.random.default_rng(77)
+    for e in (-140, -101, 100):           # g below 2^-100 (every block exact) and near the top
+        x = f32_to_bf16_bits(np.ldexp(rng.standard_t(4, (24, 96)), e).astype(np.float32))
+        c, s, g, _, _ = oracle.quantize_nv(x, policy=4)
+        _if4_check(fq.quantize_nvfp4(to_dev(x), policy="if4"), c, s, g)
     e = fq.quantize_nvfp4(torch.empty((0, 64), dtype=torch.bfloat16, device=gpu()), policy="if4")
     assert host(e.global_scale)[0] == 1.0
     with pytest.raises(fq.Fp4qError):
