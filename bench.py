@@ -26,8 +26,11 @@ The same JSON line carries:
     encode pass with a caller amax, the 1024x1024 fp32 MXFP4 quantize and
     dequantize, FWHT-8192 + MXFP4 of 16384x8192, Four Over Six of the
     8192x28672 weight, RHT16 + stochastic-rounding NVFP4 of the gradient,
-    IF4, the per-head FWHT-128, the fused SwiGLU epilogue; each with GB/s,
-    elements/s, fraction of 8 TB/s and the median / p10 / p90 per call;
+    IF4 (and its dequantize) of both tensors, the per-head FWHT-128, the
+    fused SwiGLU epilogue; each with GB/s, elements/s, fraction of 8 TB/s and
+    the median / p10 / p90 per call, and an `alu` object: the VALU issue
+    quad-cycles per call (committed rocprofv3 SQ counters) over the call
+    time, against one quad-cycle per SIMD every 4 clocks at 2.4 GHz;
   * quality: NVFP4 and MXFP4 mean squared error on the headline tensor and
     their ratio, beside the pages' "~2.4x lower for NVFP4";
   * gemm: the MXFP4 GEMM 8192^3 with the bf16 and, when the box runs it, the
@@ -48,6 +51,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense fp4 matrix peak
+VALU_PEAK_TSLOTS = 256 * 4 * 2.4e9 / 4 * 64 / 1e12   # 39.32: VALU issue of 256 CUs x 4 SIMDs
 ROWS, COLS = 8192, 8192
 N = ROWS * COLS
 BYTES_IN = N * 2
@@ -89,10 +93,25 @@ def traffic_for(kernel, launch_units=1):
 
 
 def valu_for(workload):
-    """VALU roofline of a workload's kernels from the committed rocprofv3 SQ
-    counters (wave instructions per launch), or None when stale or absent."""
+    """VALU issue quad-cycles per call of a workload's kernels, from the
+    committed rocprofv3 SQ counters (ACTIVE_INST_VALU - ACTIVE_INST_VALU2: a
+    dual-issued pair counts once, a half-rate conversion twice), or None when
+    the kernels changed since the counters were taken."""
     t = _profile(PROFILE_VALU)
-    return t.get("workloads", {}).get(workload) if t else None
+    w = t.get("workloads", {}).get(workload) if t else None
+    return int(w["valu_issue_quad_cycles_per_call"]) if w else None
+
+
+def alu_roofline(quad_cycles, seconds):
+    """VALU issue roofline: one quad-cycle (a 64-lane wave instruction at full
+    rate) per SIMD every 4 clocks, 256 CUs x 4 SIMDs at 2.4 GHz, in 64-lane
+    slots per second."""
+    if quad_cycles is None:
+        return None
+    achieved = quad_cycles * 64 / seconds / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 2), "peak": round(VALU_PEAK_TSLOTS, 2),
+            "unit": "T lane-slots/s", "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+            "valu_issue_quad_cycles_per_call": quad_cycles}
 
 
 def cpu_info():
@@ -220,6 +239,9 @@ def summary(timing, nbytes, nelems, kernels, **extra):
          "us_median": round(pct(times, 0.5) * 1e6, 3), "us_p10": round(pct(times, 0.1) * 1e6, 3),
          "us_p90": round(pct(times, 0.9) * 1e6, 3),
          "bytes_per_call": int(nbytes), "kernels": kernels}
+    valu = extra.pop("valu", None)
+    if valu is not None:
+        d["alu"] = alu_roofline(valu, mean)
     d.update(extra)
     return d
 
@@ -253,7 +275,8 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     # ---- H2: MXFP4 of the headline tensor
     mx_out = [fq.quantize_mxfp4(x) for x in xs_act]
     t = timed(lambda i: fq.quantize_mxfp4(xs_act[i % REPLICAS], out=mx_out[i % REPLICAS]))
-    rep["H2_mxfp4_bf16_8192"] = summary(t, MX_BYTES, N, "mx_quant_kernel", traffic=traffic_for("mx_quant_kernel"))
+    rep["H2_mxfp4_bf16_8192"] = summary(t, MX_BYTES, N, "mx_quant_kernel", traffic=traffic_for("mx_quant_kernel"),
+                                        valu=valu_for("H2_mxfp4_bf16_8192"))
 
     # ---- NVFP4 dequantize -> bf16, and the encode pass with a caller amax
     dq_out = [torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=dev) for _ in range(REPLICAS)]
@@ -262,11 +285,13 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
         o = nv_out[i % REPLICAS]
         fq.dequantize("nvfp4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=dq_out[i % REPLICAS])
     rep["C2_dequant_nvfp4_to_bf16"] = summary(timed(dq), DQ_BYTES, N, "dequant_kernel",
-                                              traffic=traffic_for("dequant_kernel"))
+                                              traffic=traffic_for("dequant_kernel"),
+                                              valu=valu_for("C2_dequant_nvfp4_to_bf16"))
     amax_dev = [torch.max(torch.abs(x.float())).reshape(1) for x in xs_act]
     t = timed(lambda i: fq.quantize_nvfp4(xs_act[i % REPLICAS], out=nv_out[i % REPLICAS],
                                           global_amax=amax_dev[i % REPLICAS]))
-    rep["C2_nvfp4_encode_given_amax"] = summary(t, NV_BYTES, N, "nv_fast_kernel", traffic=traffic_for("nv_fast_kernel"))
+    rep["C2_nvfp4_encode_given_amax"] = summary(t, NV_BYTES, N, "nv_fast_kernel", traffic=traffic_for("nv_fast_kernel"),
+                                                valu=valu_for("C2_nvfp4_encode_given_amax"))
 
     # ---- IF4 of the headline tensor and its dequantize
     if4_out = [fq.quantize_nvfp4(x, policy="if4", workspace=ws) for x in xs_act]
@@ -298,7 +323,8 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     xs1 = replicas(x1, k1)
     o1 = [fq.quantize_mxfp4(x, counters=True) for x in xs1]
     t = timed(lambda i: fq.quantize_mxfp4(xs1[i % k1], counters=True, out=o1[i % k1]))
-    rep["C1_mxfp4_f32_1024_counters"] = summary(t, b1, n1, "zero_counters_kernel + mx_quant_kernel", replicas=k1)
+    rep["C1_mxfp4_f32_1024_counters"] = summary(t, b1, n1, "mx_quant_kernel + count_reduce_kernel", replicas=k1,
+                                                valu=valu_for("C1_mxfp4_f32_1024_counters"))
     y1 = [torch.empty_like(x) for x in xs1]
     t = timed(lambda i: fq.dequantize("mxfp4", o1[i % k1].codes, o1[i % k1].scales, out_dtype=torch.float32,
                                       out=y1[i % k1]))
@@ -340,7 +366,8 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     t = timed(lambda i: fq.silu_mul_fwht_mxfp4(xgd[i % 2][:, :d], xgd[i % 2][:, d:], out=og[i % 2]),
               max(20, steps // 2))
     rep["F2_silu_mul_fwht8192_mxfp4_bf16_16384x8192"] = summary(t, 2 * ng * 2 + ng // 2 + ng // 32, ng,
-                                                                "fwht8192_kernel (SwiGLU + MXFP4)")
+                                                                "fwht8192_kernel (SwiGLU + MXFP4)",
+                                                                valu=valu_for("F2_silu_mul_fwht8192_mxfp4_bf16_16384x8192"))
     del xgd, og
     torch.cuda.empty_cache()
 
@@ -361,8 +388,17 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     oi = [fq.quantize_nvfp4(x, policy="if4", workspace=ws) for x in xs4]
     t = timed(lambda i: fq.quantize_nvfp4(xs4[i % 2], policy="if4", out=oi[i % 2], workspace=ws), max(20, steps // 2))
     rep["IF4_bf16_8192x28672"] = summary(t, n4 * 2 + n4 // 2 + n4 // 16 + 4, n4,
-                                         "nv_amax_kernel + nv_quant_kernel (IF4)")
-    del xs4, oi
+                                         "nv_amax_kernel + nv_quant_kernel (IF4)",
+                                         valu=valu_for("IF4_bf16_8192x28672"))
+    yi = [torch.empty_like(xs4[0]) for _ in range(2)]
+
+    def if4dq4(i):
+        o = oi[i % 2]
+        fq.dequantize("if4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=yi[i % 2])
+    rep["IF4_dequant_to_bf16_8192x28672"] = summary(timed(if4dq4, max(20, steps // 2)),
+                                                    n4 // 2 + n4 // 16 + 4 + n4 * 2, n4, "dequant_kernel (IF4)",
+                                                    valu=valu_for("IF4_dequant_to_bf16_8192x28672"))
+    del xs4, oi, yi
     torch.cuda.empty_cache()
     return rep
 
@@ -638,7 +674,8 @@ def main():
                      "launch_us_p10": round(pct(per_launch, 0.1) * 1e6, 3),
                      "launch_us_p90": round(pct(per_launch, 0.9) * 1e6, 3),
                      "bytes_per_launch": NV_BYTES,
-                     "traffic": traffic_for("nv_resident_kernel")},
+                     "traffic": traffic_for("nv_resident_kernel"),
+                     "alu": alu_roofline(valu_for("headline_nvfp4_bf16_8192"), call_sec)},
         "kernel_source_sha": kernel_source_sha(),
     }
     if not a.no_report:
