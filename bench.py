@@ -33,7 +33,7 @@ The same JSON line carries:
     time, against one quad-cycle per SIMD every 4 clocks at 2.4 GHz;
   * quality: NVFP4 and MXFP4 mean squared error on the headline tensor and
     their ratio, beside the pages' "~2.4x lower for NVFP4";
-  * gemm: the MXFP4 GEMM 8192^3 with the bf16 and, when the box runs it, the
+  * gemm: the MXFP4 GEMM 8192^3 with the bf16 and, where torch runs it, the
     fp8 matmul of the library routine, beside the pages' "FP4 ~2x FP8";
   * cpu_baseline: the CPU oracle on the host's cores (all threads it can use,
     and one), with the core count and CPU model.
@@ -141,7 +141,7 @@ def cpu_baseline(x_np, min_cpu_seconds=10.0):
 
     import oracle
     model, nproc, usable = cpu_info()
-    threads = max(1, min(16, usable))      # (a GPU machine gives one GPU's share of its cores: 16)
+    threads = max(1, min(16, usable))      # at most 16 threads: one GPU's share of a multi-GPU host's cores
     chunk = 256
     starts = list(range(0, ROWS, chunk))
 
@@ -426,7 +426,7 @@ def quality(xs_act, nv_out):
 
 def gemm_context(dev, timer, reps=10):
     """MXFP4 GEMM 8192^3 (this library) beside the library matmul in bf16 and,
-    if the box runs it, fp8 (e4m3, per-tensor scales)."""
+    where torch runs it, fp8 (e4m3, per-tensor scales)."""
     import numpy as np
     import torch
 

@@ -136,8 +136,10 @@ typedef struct {
  * ticks of the 100 MHz GPU clock (0: 1 ms; a small value makes every wait
  * run out, which tests use), [24, 32) the epoch word of captured launches,
  * [64, 8256) per-workgroup flags, [8256,
- * 12352) the per-workgroup maxima of the two-pass kernels, [16384, 81920)
- * sixteen copies of the single-read kernel's result word, 4 KiB apart. */
+ * 12352) the per-workgroup maxima of the two-pass kernels, [12352, 15424)
+ * the 128 counter slots (three 64-bit counts each) of a counting call,
+ * [16384, 81920) sixteen copies of the single-read kernel's result word,
+ * 4 KiB apart. */
 size_t fp4q_workspace_bytes(const fp4q_quant_args *args);
 
 /* MXFP4 quantization of x ([rows][in_row_stride] of in_dtype).  block_size
