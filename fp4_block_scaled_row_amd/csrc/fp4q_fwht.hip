@@ -68,8 +68,15 @@ __device__ __forceinline__ void load8(const FwhtLaunch& f, int64_t off, float v[
 }
 
 // ---------------------------------------------------------------- d = 8192
+// LDS word index of element i.  gfx950 serves 4-byte accesses half a wave at
+// a time over 32 banks (word bits 0-4) and 16-byte accesses 16 lanes at a
+// time over 64 banks.  Layout M reads and writes 4 bytes per lane with lane
+// bits 1-3 on word bits 0-2 and lane bits 0 and 4 on element bits 12 and 9,
+// which the XOR moves onto word bits 4 and 3: 32 banks per half wave.
+// Layout L moves 16 bytes per lane with lane bits on word bits 3-8 (the XOR
+// is uniform there) and bit 2 flipped by lane bit 3: 64 banks per 16 lanes.
 __device__ __forceinline__ int swz8192(int i) {
-  const int k = ((i >> 9) & 3) | (((i >> 12) & 1) << 2);
+  const int k = ((i >> 9) & 1) | (((i >> 12) & 1) << 1) | (((i >> 10) & 1) << 2);
   return i ^ (k << 3) ^ (((i >> 6) & 1) << 2);
 }
 

@@ -277,32 +277,21 @@ __device__ __forceinline__ uint32_t nv_scale_code(float bamax, float inv_lo, flo
   return cl == ch ? cl : resolve_e4m3(bamax, cl, ch, mult, g);
 }
 
-// Stochastic-rounding magnitude read off one product a ~ |q| (relative error
-// at most 1.5 * 2^-22).  Below 1 the sum a + 1 carries a's position in the
-// step-0.5 intervals [0, .5) and [.5, 1) in its mantissa; from 1 on a's own
-// mantissa does, the step being half the power of two below a.  Either way
-// the exponent with the top mantissa bit gives the interval and the low 22
-// bits the fraction f of the step in 2^-22 units, off by at most 7 units.
-// R-17 rounds up iff f exceeds u 2^-16, u << 6 units.  `near` keeps the
-// lane's minimum of f - (u << 6) + 16, below 32 within 16 units of the
-// threshold, and of 2^22 + 16 - f, below 32 within 16 units of the next
-// lattice point, where a and q may lie in different intervals (which leaves
-// the result unchanged unless u = 0).  A lane with near < 32 is decided
-// exactly.
-__device__ __forceinline__ uint32_t sr_mag_fast(float a, uint32_t u, uint32_t& near) {
-  const bool small = a < 1.0f;
-  const uint32_t b = as_u(small ? a + 1.0f : a);
-  const uint32_t fr = b & 0x3FFFFFu;
-  const int32_t d = (int32_t)fr - (int32_t)(u << 6);
-  near = min(near, min((uint32_t)d + 16u, 0x400010u - fr));
-  const uint32_t k = (b >> 22) - (small ? 254u : 252u) + (d > 0 ? 1u : 0u);
-  return min(k, 7u);   // a >= 6 (or an overflowed product) gives k >= 7
-}
+// Stochastic rounding from one product a ~ |q| (relative error at most
+// 1.5 * 2^-22).  Below 1 the sum a + 1 carries a's position in the step-0.5
+// intervals [0, .5) and [.5, 1) in its mantissa; from 1 on a's own mantissa
+// does, the step being half the power of two below a.  Either way the
+// exponent with the top mantissa bit gives the interval and the low 22 bits
+// the fraction fr of the step in 2^-22 units, off by at most 7 units.  R-17's
+// rule (round up iff the step fraction exceeds u 2^-16) is fr > u << 6 here.
+// Within 16 units of that threshold the product may decide wrongly, and so
+// it may when a and q lie on either side of a lattice point, which changes
+// the result only when u = 0; such lanes are decided exactly.
 
 // Codes of the 8 elements of a lane for E4M3 scale byte c.  Round to nearest:
 // the two bracket products of s_inv[c] rounded by the FP4 conversion; they
 // agree except within 2^-22 of a decision point.  Stochastic rounding: one
-// product (sr_mag_fast).  Elements left undecided take exact FMA-residual
+// product (above).  Elements left undecided take exact FMA-residual
 // decisions; a tensor with g < 2^-100 takes correctly rounded fp64 quotients.
 template <bool SR, bool COUNT>
 __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, const NvCtx& cx,
@@ -338,18 +327,40 @@ __device__ __forceinline__ uint32_t nv_encode(const float v[8], uint32_t c, cons
       redo |= r << i;
     }
   } else {
+    // The rule above in few steps.  t = med3(a, (a + 1) / 2, 6) has the bits
+    // of a + 1 (halved) below 1, of a from 1 to 6, and is 6 above.  With
+    // W = (u << 6) + 1 + (251 << 22), e = bits(t) - W borrows from bit 22
+    // exactly when the step fraction fr is at most u << 6, so e >> 22 is the
+    // magnitude code with its round-up; the low 22 bits of e + 17 are below
+    // 32 exactly when fr - (u << 6) lies in [-16, 15] modulo 2^22, which
+    // with u = 0 also takes in fr within 16 units under the next lattice
+    // point (the one case where a and q in different intervals can round
+    // differently).  The signs come from the RNE conversion of the signed
+    // products (which keeps the sign of zero).
+    const float one = e8m0_operand(127u);
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = v[i] * iv.x;
+    uint32_t sg = 0u;
+    sg = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(sg, p[0], p[1], one, 0);
+    sg = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(sg, p[2], p[3], one, 1);
+    sg = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(sg, p[4], p[5], one, 2);
+    sg = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(sg, p[6], p[7], one, 3);
     uint32_t near = ~0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float a = fabsf(v[i]) * iv.x;
-      const uint32_t mag = sr_mag_fast(a, draw16(rnd, i), near);
-      codes |= (mag | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+      const float a = fabsf(p[i]);
+      const float t = __builtin_amdgcn_fmed3f(a, __builtin_fmaf(a, 0.5f, 0.5f), 6.0f);
+      const uint32_t e = as_u(t) - ((draw16(rnd, i) << 6) + 0x3EC00001u);
+      near = min(near, (e << 10) + (17u << 10));
+      codes |= (e >> 22) << (4 * i);
       if constexpr (COUNT) {
         sat |= (a > 6.0f ? 1u : 0u) << i;
         redo |= (fabsf(a - 6.0f) <= 0x1p-17f ? 1u : 0u) << i;   // relative 2^-20 of 6
       }
     }
-    if (near < 32u) redo = 0xFFu;
+    codes |= sg & 0x88888888u;
+    if (near < (32u << 10)) redo = 0xFFu;
   }
   if (cx.exact_all) {
     // g < 2^-100: correctly rounded fp64 quotients for every element
