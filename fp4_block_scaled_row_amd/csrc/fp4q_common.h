@@ -46,9 +46,11 @@ constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kQuadEven = 0xA0;  // quad_perm [0,0,2,2]: each lane pair takes its even lane's value
 constexpr int kQuadOdd = 0xF5;   // quad_perm [1,1,3,3]: each lane pair takes its odd lane's value
 constexpr int kRowHalfMirror = 0x141;  // lane i of each 8-lane half-row <- lane 7 - i
+constexpr int kRowRor8 = 0x128;        // row_ror:8: lane i of each 16-lane row <- lane (i + 8) mod 16 = i ^ 8
 
 __device__ __forceinline__ float dpp_xor1_f(float v) { return as_f(dpp_u32<kQuadXor1>(as_u(v))); }
 __device__ __forceinline__ float dpp_xor2_f(float v) { return as_f(dpp_u32<kQuadXor2>(as_u(v))); }
+__device__ __forceinline__ float dpp_xor8_f(float v) { return as_f(dpp_u32<kRowRor8>(as_u(v))); }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -70,11 +70,9 @@ __device__ __forceinline__ void widen_slot(const SlotRaw<IN>& r, float v[8]) {
 // 16-point random Hadamard transform of the 16-block held by a lane pair:
 // y = (sigma * x) H16 / 4, natural order.  Butterfly stages h = 1, 2, 4 run in
 // registers, h = 8 between the two lanes (the even lane holds positions 0..7).
-// Sign flips and the final x0.25 are exact.
-__device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool odd_lane) {
-  const uint32_t sg = odd_lane ? (signs16 >> 8) : signs16;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = as_f(as_u(v[i]) ^ (((sg >> i) & 1u) << 31));
+// Sign flips and the final x0.25 are exact.  rht16_butterflies is the part
+// after the signs.
+__device__ __forceinline__ void rht16_butterflies(float v[8], bool odd_lane) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -94,21 +92,43 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool od
   for (int i = 0; i < 8; ++i) v[i] = fmaf(sg1, v[i], p[i]) * 0.25f;
 }
 
-// Partner value across lane bit 2 (xor 4) or bit 3 (xor 8) within a row of
-// 16 lanes: the upper half of each 2N-lane group reads lane - N (row_shr:N,
-// written to its banks only), the lower half lane + N (row_shl:N).
-template <int N>
-__device__ __forceinline__ float dpp_xor_hi_f(float v) {
-  constexpr int kShr = 0x110 + N, kShl = 0x100 + N;
-  constexpr int kUpper = N == 4 ? 0xA : 0xC, kLower = N == 4 ? 0x5 : 0x3;   // bank masks
-  const int up = __builtin_amdgcn_update_dpp(0, (int)as_u(v), kShr, 0xF, kUpper, false);
-  return as_f((uint32_t)__builtin_amdgcn_update_dpp(up, (int)as_u(v), kShl, 0xF, kLower, false));
+__device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool odd_lane) {
+  const uint32_t sg = odd_lane ? (signs16 >> 8) : signs16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = as_f(as_u(v[i]) ^ (((sg >> i) & 1u) << 31));
+  rht16_butterflies(v, odd_lane);
+}
+
+// Widening and RHT16 of a raw slot, the signs flipped in the raw words (a
+// bf16 word holds two positions, sign bits 15 and 31): the same values as
+// widen_slot then rht16_pair.
+template <int IN>
+__device__ __forceinline__ void widen_rht16(SlotRaw<IN> r, float v[8], uint32_t signs16, bool odd_lane) {
+  const uint32_t sg = odd_lane ? (signs16 >> 8) : signs16;
+  if constexpr (IN == kF32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.w[i] ^= ((sg >> i) & 1u) << 31;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] ^= (((sg >> (2 * i)) & 1u) << 15) | (((sg >> (2 * i + 1)) & 1u) << 31);
+  }
+  widen_slot<IN>(r, v);
+  rht16_butterflies(v, odd_lane);
+}
+
+// Partner value across lane bit 2 (xor 4) within a row of 16 lanes: lanes
+// 4-7 and 12-15 read lane - 4 (row_shr:4, written to those banks only),
+// lanes 0-3 and 8-11 lane + 4 (row_shl:4).  (Bit 3 is one row rotation.)
+__device__ __forceinline__ float dpp_xor4_f(float v) {
+  const int up = __builtin_amdgcn_update_dpp(0, (int)as_u(v), 0x114, 0xF, 0xA, false);
+  return as_f((uint32_t)__builtin_amdgcn_update_dpp(up, (int)as_u(v), 0x104, 0xF, 0x5, false));
 }
 
 // Normalised FWHT of each 128-element chunk held by 16 consecutive lanes, 8
 // consecutive elements each: the three butterfly stages of the element bits
 // run in registers, the four of the lane bits across lanes (quad
-// permutations for bits 0 and 1, bank-masked row shifts for bits 2 and 3);
+// permutations for bits 0 and 1, bank-masked row shifts for bit 2, a row
+// rotation by 8 for bit 3);
 // the upper member of a pair keeps a - b.  Scaled once by c = fl32(1/sqrt(128)).
 __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
 #pragma unroll
@@ -137,11 +157,11 @@ __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = fmaf(s1, v[i], p[i]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor_hi_f<4>(v[i]);
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor4_f(v[i]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = fmaf(s2, v[i], p[i]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor_hi_f<8>(v[i]);
+  for (int i = 0; i < 8; ++i) p[i] = dpp_xor8_f(v[i]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = fmaf(s3, v[i], p[i]) * c;
 }

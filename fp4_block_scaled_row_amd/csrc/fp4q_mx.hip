@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(QuantLaunch q) {
       constexpr bool kPackedBf16 = (IN == kBF16 && ROT == kRotNone && !SR && !COUNT);
       if constexpr (!kPackedBf16) {
         float v[8];
-        widen_slot<IN>(raw[u], v);
-        if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
+        if constexpr (ROT == kRotRht16) widen_rht16<IN>(raw[u], v, q.rht_signs, (lane & 1) != 0);
+        else widen_slot<IN>(raw[u], v);
         mx_encode_slot<SR, COUNT, MANUAL>(v, s, active, lane, q.manual_e, q.seed, q.codes, q.scales,
                                           n_sat, n_und, n_nf);
         if constexpr (ROT != kRotNone) {

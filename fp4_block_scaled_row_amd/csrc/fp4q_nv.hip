@@ -37,9 +37,12 @@ constexpr int kPolMax6 = 0, kPolFos = 1, kPolIf4 = 2;   // block scaling policie
 
 template <int IN, int ROT, bool CONTIG>
 __device__ __forceinline__ void load_values(const QuantLaunch& q, const SlotRaw<IN>& r, int lane, float v[8]) {
-  widen_slot<IN>(r, v);
-  if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
-  if constexpr (ROT == kRotFwht128) fwht128_lanes(v, lane, q.rot_scale);
+  if constexpr (ROT == kRotRht16) {
+    widen_rht16<IN>(r, v, q.rht_signs, (lane & 1) != 0);
+  } else {
+    widen_slot<IN>(r, v);
+    if constexpr (ROT == kRotFwht128) fwht128_lanes(v, lane, q.rot_scale);
+  }
 }
 
 // ---------------------------------------------------------------- pass 1

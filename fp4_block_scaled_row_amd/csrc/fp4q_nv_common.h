@@ -559,52 +559,6 @@ __device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t codes,
   return acc;
 }
 
-// The whole max->6 NVFP4 encoding of one slot of raw bf16 data (8 values at
-// flat slot s; the lane pair 2k, 2k+1 holds one 16-block and must execute
-// together): widen, optional RHT16, block amax, scale byte, codes, counters,
-// stores.
-template <int ROT, bool SR, bool COUNT>
-__device__ __forceinline__ void nv_encode_slot(const QuantLaunch& q, const NvCtx& cx, const float2* s_inv,
-                                               const uint4& w, int64_t s, bool active, int lane,
-                                               uint32_t& n_sat, uint32_t& n_und, uint32_t& n_nf) {
-  float v[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-  if constexpr (ROT == kRotRht16) rht16_pair(v, q.rht_signs, (lane & 1) != 0);
-  uint32_t bm = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) bm = max(bm, as_u(v[i]) & 0x7FFFFFFFu);
-  bm = max(bm, dpp_u32<kQuadXor1>(bm));
-  const bool nonfinite = bm >= 0x7F800000u;
-  const float bamax = as_f(bm);
-  U4 rnd = {0u, 0u, 0u, 0u};
-  if constexpr (SR) {
-    const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
-    rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
-  }
-  const uint32_t c = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all, 6.0f, cx.g);
-  uint32_t satm;
-  uint32_t codes = nv_encode<SR, COUNT>(v, c, cx, s_inv, rnd, satm);
-  if (nonfinite) codes = 0u;
-  if constexpr (COUNT) {
-    if (active) {
-      if (nonfinite) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) n_nf += ((as_u(v[i]) & 0x7FFFFFFFu) >= 0x7F800000u) ? 1u : 0u;
-      } else {
-        n_sat += __popc(satm);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) n_und += (v[i] != 0.0f && ((codes >> (4 * i)) & 7u) == 0u) ? 1u : 0u;
-      }
-    }
-  }
-  if (active) {
-    *reinterpret_cast<uint32_t*>(q.codes + (s << 2)) = codes;
-    if (!(lane & 1)) q.scales[s >> 1] = (uint8_t)(nonfinite ? 0x7Fu : c);
-    if constexpr (ROT != kRotNone) {
-      if (q.rotated) store_rotated(q.rotated, s, v);
-    }
-  }
-}
-
 // Exact max->6 round-to-nearest encoding of flat slot s of a contiguous bf16
 // tensor from its 16-block (a: first half, b: second half), by the brackets
 // and the exact decisions above; a block holding a non-finite value gets
