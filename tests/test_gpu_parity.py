@@ -352,6 +352,44 @@ def test_nonfinite_zero_subnormal_huge(dtype):
         fq.check_counters(n.counters)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rotation", ["none", "rht16"])
+@pytest.mark.parametrize("counters", [False, True])
+def test_nv_stochastic_signed_zeros_and_subnormal_elements(dtype, rotation, counters):
+    """Stochastic rounding keeps the sign of every code, zeros and underflows
+    included (R-5, R-17): 16-blocks whose maximum is a normal value and whose
+    other elements are +-0, subnormals of either sign and tiny normals, so
+    that the scaled products of the small ones are zero or subnormal."""
+    rng = np.random.default_rng(77)
+    rows, cols = 24, 128
+    x = np.empty((rows, cols), np.float32)
+    kinds = rng.integers(0, 5, (rows, cols))
+    x[kinds == 0] = 0.0
+    x[kinds == 1] = -0.0
+    sub = np.ldexp(rng.uniform(0.5, 1.0, (rows, cols)), rng.integers(-149, -127, (rows, cols)))
+    x[kinds == 2] = -sub[kinds == 2]
+    x[kinds == 3] = sub[kinds == 3]
+    tiny = np.ldexp(rng.uniform(-1, 1, (rows, cols)), -120)
+    x[kinds == 4] = tiny[kinds == 4]
+    x[:, ::16] = rng.choice([-1, 1], (rows, cols // 16)) * rng.uniform(0.5, 4.0, (rows, cols // 16))
+    x = x.astype(np.float32)
+    xin = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    rot = 1 if rotation == "rht16" else 0
+    n = fq.quantize_nvfp4(to_dev(xin), rotation=rotation, rounding="stochastic", seed=0x5EED, counters=counters,
+                          return_rotated=True)
+    if rot:
+        # codes against the oracle's NVFP4 of the GPU's own rotated values (as the other rotation tests)
+        xr = host(n.rotated)
+        c, s, g, _, cnt = oracle.quantize_nv(xr, rounding=1, seed=0x5EED)
+    else:
+        c, s, g, _, cnt = oracle.quantize_nv(xin, rounding=1, seed=0x5EED)
+    assert host(n.global_scale)[0] == g
+    assert_same(host(n.scales), s, "scales")
+    assert_same(host(n.codes), c, "codes")
+    if counters:
+        assert_same(host(n.counters).astype(np.uint64), cnt, "counters")
+
+
 @pytest.mark.parametrize("scale_exp", [-140, -120, -101, -60, 0, 100, 120])
 def test_nv_tiny_and_huge_tensors(scale_exp):
     """Tensors whose global scale is tiny take the all-fp64 path (g < 2^-100)."""
