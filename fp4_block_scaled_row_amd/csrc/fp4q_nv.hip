@@ -225,9 +225,10 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       }
       if constexpr (POL == kPolIf4) {
         uint32_t sati;
-        const uint32_t ci = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati);
+        const uint32_t mi = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati);
+        const uint32_t ci = mi | (codes & 0x88888888u);   // the signs of the FP4 codes
         float ef = half_sse(v, codes, c6, cx.g);
-        float ei = half_sse_int4(v, ci, s_dq + 8 * c6);
+        float ei = half_sse_int4(v, mi, s_dq + 8 * c6);
         const float pf = dpp_xor1_f(ef), pi = dpp_xor1_f(ei);
         ef = odd ? (pf + ef) : (ef + pf);   // S_lo + S_hi on both lanes
         ei = odd ? (pi + ei) : (ei + pi);

@@ -477,9 +477,11 @@ __device__ __forceinline__ void if4_fill_tables(float* s_i4, float* s_dq, const 
   }
 }
 
-// INT4 nibbles (and |q| > 7 saturation flags) of a lane's 8 elements under
-// scale byte c, q = 7 x / (6 s g) rounded to the nearest integer, ties to
-// even, |k| <= 7.  One product a = |x| * RN32(7 / (6 s g)) is within
+// INT4 magnitudes (and |q| > 7 saturation flags) of a lane's 8 elements
+// under scale byte c, q = 7 x / (6 s g) rounded to the nearest integer, ties
+// to even, |k| <= 7, in nibble i without its sign bit: an INT4 nibble has the
+// sign of its element, as the FP4 nibble of the same element has, so the
+// caller takes the sign bits from the FP4 codes.  One product a = |x| * RN32(7 / (6 s g)) is within
 // 2^-23 (relatively) of |q|, so rint(a) is the answer unless a lies within
 // 2^-19 of a half-integer (or, when counting, of 7); such a lane is decided
 // exactly: the sign of 7 |x| - (2k + 1) 3 s g is exact in one fp64 FMA
@@ -499,7 +501,7 @@ __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c
       const float a = fabsf(v[i]) * m;
       const float r = rintf(a);
       unsure |= fabsf(a - r) > 0.5f - 0x1p-19f;
-      codes |= ((uint32_t)fminf(r, 7.0f) | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+      codes |= (uint32_t)fminf(r, 7.0f) << (4 * i);
       if constexpr (COUNT) {
         sat |= (a > 7.0f ? 1u : 0u) << i;
         unsure |= fabsf(a - 7.0f) <= 0x1p-17f;
@@ -531,28 +533,24 @@ __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c
     for (int i = 0; i < 8; ++i) {
       const double q = 7.0 * (double)fabsf(v[i]) / den;
       const uint32_t k = q > 7.0 ? 7u : (uint32_t)rint(q);
-      codes |= (k | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+      codes |= k << (4 * i);
       sat |= (q > 7.0 ? 1u : 0u) << i;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) codes |= ((as_u(v[i]) >> 31) << 3) << (4 * i);
   }
   satmask = COUNT ? sat : 0u;
   return codes;
 }
 
 // Half of the INT4 candidate's block SSE in the order of half_sse, with
-// dq = +-s_dq[8 c + k] (dq_row = s_dq + 8 c).
-__device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t codes, const float* dq_row) {
+// dq = +-s_dq[8 c + k] (dq_row = s_dq + 8 c) of the element's sign, so that
+// d = x - dq is +-(|x| - s_dq[8 c + k]) and its square that of |x| - s_dq[..]
+// (mags: the magnitudes of if4_encode_int4).
+__device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t mags, const float* dq_row) {
 #pragma clang fp contract(off)
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t nib = (codes >> (4 * i)) & 15u;
-    const float m = dq_row[nib & 7u];
-    const float dq = (nib & 8u) ? -m : m;
-    const float d = v[i] - dq;
+    const float d = fabsf(v[i]) - dq_row[(mags >> (4 * i)) & 7u];
     const float sq = d * d;
     acc = acc + sq;
   }
