@@ -266,6 +266,31 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
             x0 = x0.view(torch.bfloat16)
         return [x0] + [x0.clone() for _ in range(k - 1)]
 
+    def graph_rate(fn, k, nbytes, replays=20):
+        """The same calls (k of them, one per replica) captured in a HIP graph and
+        replayed back to back: the GPU's time per call without the host's
+        dispatch of each launch, which bounds calls on tensors this small."""
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for i in range(k):
+                fn(i)           # (the binding keeps a workspace per stream: made here, outside capture)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(k):
+                fn(i)
+        timer.settle(lambda i: g.replay(), 20)
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(replays):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        per_call = e0.elapsed_time(e1) / 1e3 / (replays * k)
+        return {"us_per_call": round(per_call * 1e6, 3), "value": round(nbytes / per_call / 1e9, 2), "unit": "GB/s",
+                "calls_per_graph": k, "replays": replays}
+
     def timed(fn, n_calls=None):
         n = n_calls or steps
         timer.settle(fn, 30)     # (the clock drops while the host prepares each workload)
@@ -322,13 +347,15 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     k1 = n_replicas(x1.nbytes)
     xs1 = replicas(x1, k1)
     o1 = [fq.quantize_mxfp4(x, counters=True) for x in xs1]
-    t = timed(lambda i: fq.quantize_mxfp4(xs1[i % k1], counters=True, out=o1[i % k1]))
-    rep["C1_mxfp4_f32_1024_counters"] = summary(t, b1, n1, "mx_quant_kernel + count_reduce_kernel", replicas=k1,
-                                                valu=valu_for("C1_mxfp4_f32_1024_counters"))
+    q1 = lambda i: fq.quantize_mxfp4(xs1[i % k1], counters=True, out=o1[i % k1])
+    rep["C1_mxfp4_f32_1024_counters"] = summary(timed(q1), b1, n1, "mx_quant_kernel + count_reduce_kernel",
+                                                replicas=k1, valu=valu_for("C1_mxfp4_f32_1024_counters"),
+                                                graph_replay=graph_rate(q1, k1, b1))
     y1 = [torch.empty_like(x) for x in xs1]
-    t = timed(lambda i: fq.dequantize("mxfp4", o1[i % k1].codes, o1[i % k1].scales, out_dtype=torch.float32,
-                                      out=y1[i % k1]))
-    rep["C1_dequant_mxfp4_to_f32_1024"] = summary(t, b1, n1, "dequant_kernel", replicas=k1)
+    d1 = lambda i: fq.dequantize("mxfp4", o1[i % k1].codes, o1[i % k1].scales, out_dtype=torch.float32,
+                                 out=y1[i % k1])
+    rep["C1_dequant_mxfp4_to_f32_1024"] = summary(timed(d1), b1, n1, "dequant_kernel", replicas=k1,
+                                                  graph_replay=graph_rate(d1, k1, b1))
     del xs1, o1, y1
 
     # ---- C5: RHT16 + stochastic-rounding NVFP4 of the gradient
