@@ -92,6 +92,20 @@ def traffic_for(kernel, launch_units=1):
     return int(k["hbm_bytes_per_launch"]) * launch_units
 
 
+def traffic_for_workload(workload):
+    """HBM bytes per call of a workload's kernels (the sum over them) from the
+    committed rocprofv3 PMC summary, or None when stale or absent."""
+    t = _profile(PROFILE_TRAFFIC)
+    w = t.get("workloads", {}).get(workload) if t else None
+    return int(w["hbm_bytes_per_call"]) if w else None
+
+
+def profiled(workload):
+    """The counter-based fields of a report row: measured HBM bytes per call
+    and the VALU issue roofline (summary() turns `valu` into `alu`)."""
+    return {"traffic": traffic_for_workload(workload), "valu": valu_for(workload)}
+
+
 def valu_for(workload):
     """VALU issue quad-cycles per call of a workload's kernels, from the
     committed rocprofv3 SQ counters (ACTIVE_INST_VALU - ACTIVE_INST_VALU2: a
@@ -242,6 +256,8 @@ def summary(timing, nbytes, nelems, kernels, **extra):
     valu = extra.pop("valu", None)
     if valu is not None:
         d["alu"] = alu_roofline(valu, mean)
+    if extra.get("traffic") is not None:
+        d["traffic_over_algorithmic"] = round(extra["traffic"] / nbytes, 3)
     d.update(extra)
     return d
 
@@ -300,8 +316,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     # ---- H2: MXFP4 of the headline tensor
     mx_out = [fq.quantize_mxfp4(x) for x in xs_act]
     t = timed(lambda i: fq.quantize_mxfp4(xs_act[i % REPLICAS], out=mx_out[i % REPLICAS]))
-    rep["H2_mxfp4_bf16_8192"] = summary(t, MX_BYTES, N, "mx_quant_kernel", traffic=traffic_for("mx_quant_kernel"),
-                                        valu=valu_for("H2_mxfp4_bf16_8192"))
+    rep["H2_mxfp4_bf16_8192"] = summary(t, MX_BYTES, N, "mx_quant_kernel", **profiled("H2_mxfp4_bf16_8192"))
 
     # ---- NVFP4 dequantize -> bf16, and the encode pass with a caller amax
     dq_out = [torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=dev) for _ in range(REPLICAS)]
@@ -310,20 +325,19 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
         o = nv_out[i % REPLICAS]
         fq.dequantize("nvfp4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=dq_out[i % REPLICAS])
     rep["C2_dequant_nvfp4_to_bf16"] = summary(timed(dq), DQ_BYTES, N, "dequant_kernel",
-                                              traffic=traffic_for("dequant_kernel"),
-                                              valu=valu_for("C2_dequant_nvfp4_to_bf16"))
+                                              **profiled("C2_dequant_nvfp4_to_bf16"))
     amax_dev = [torch.max(torch.abs(x.float())).reshape(1) for x in xs_act]
     t = timed(lambda i: fq.quantize_nvfp4(xs_act[i % REPLICAS], out=nv_out[i % REPLICAS],
                                           global_amax=amax_dev[i % REPLICAS]))
-    rep["C2_nvfp4_encode_given_amax"] = summary(t, NV_BYTES, N, "nv_fast_kernel", traffic=traffic_for("nv_fast_kernel"),
-                                                valu=valu_for("C2_nvfp4_encode_given_amax"))
+    rep["C2_nvfp4_encode_given_amax"] = summary(t, NV_BYTES, N, "nv_fast_kernel",
+                                                **profiled("C2_nvfp4_encode_given_amax"))
 
     # ---- IF4 of the headline tensor and its dequantize
     if4_out = [fq.quantize_nvfp4(x, policy="if4", workspace=ws) for x in xs_act]
     t = timed(lambda i: fq.quantize_nvfp4(xs_act[i % REPLICAS], policy="if4", out=if4_out[i % REPLICAS], workspace=ws))
     frac = float((if4_out[0].scales >= 0x80).float().mean())
     rep["IF4_bf16_8192"] = summary(t, NV_BYTES, N, "nv_amax_kernel + nv_quant_kernel (IF4)",
-                                   int4_block_fraction=round(frac, 4), valu=valu_for("IF4_bf16_8192"))
+                                   int4_block_fraction=round(frac, 4), **profiled("IF4_bf16_8192"))
 
     def if4dq(i):
         o = if4_out[i % REPLICAS]
@@ -336,7 +350,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     t = timed(lambda i: fq.quantize_nvfp4(xs_act[i % REPLICAS], rotation="fwht128", out=h_out[i % REPLICAS],
                                           workspace=ws))
     rep["F4_fwht128_nvfp4_bf16_8192"] = summary(t, NV_BYTES, N, "nv_amax_kernel + nv_quant_kernel (FWHT-128)",
-                                                valu=valu_for("F4_fwht128_nvfp4_bf16_8192"))
+                                                **profiled("F4_fwht128_nvfp4_bf16_8192"))
     del h_out, amax_dev
     torch.cuda.empty_cache()
 
@@ -349,7 +363,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     o1 = [fq.quantize_mxfp4(x, counters=True) for x in xs1]
     q1 = lambda i: fq.quantize_mxfp4(xs1[i % k1], counters=True, out=o1[i % k1])
     rep["C1_mxfp4_f32_1024_counters"] = summary(timed(q1), b1, n1, "mx_quant_kernel + count_reduce_kernel",
-                                                replicas=k1, valu=valu_for("C1_mxfp4_f32_1024_counters"),
+                                                replicas=k1, **profiled("C1_mxfp4_f32_1024_counters"),
                                                 graph_replay=graph_rate(q1, k1, b1))
     y1 = [torch.empty_like(x) for x in xs1]
     d1 = lambda i: fq.dequantize("mxfp4", o1[i % k1].codes, o1[i % k1].scales, out_dtype=torch.float32,
@@ -367,7 +381,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     t = timed(lambda i: fq.quantize_nvfp4(xs5[i % REPLICAS], rotation="rht16", rounding="stochastic", seed=seed,
                                           out=o5[i % REPLICAS], workspace=ws))
     rep["C5_rht16_sr_nvfp4_bf16_8192"] = summary(t, NV_BYTES, N, "nv_amax_kernel + nv_quant_kernel (RHT16, SR)",
-                                                 valu=valu_for("C5_rht16_sr_nvfp4_bf16_8192"))
+                                                 **profiled("C5_rht16_sr_nvfp4_bf16_8192"))
     del xs5, o5
     torch.cuda.empty_cache()
 
@@ -379,7 +393,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
     o3 = [fq.quantize_mxfp4(x, rotation="fwht_row") for x in xs3]
     t = timed(lambda i: fq.quantize_mxfp4(xs3[i % 2], rotation="fwht_row", out=o3[i % 2]), max(20, steps // 2))
     rep["C3_fwht8192_mxfp4_bf16_16384x8192"] = summary(t, n3 * 2 + n3 // 2 + n3 // 32, n3, "fwht8192_kernel (+MXFP4)",
-                                                       valu=valu_for("C3_fwht8192_mxfp4_bf16_16384x8192"))
+                                                       **profiled("C3_fwht8192_mxfp4_bf16_16384x8192"))
     del xs3, o3
     torch.cuda.empty_cache()
 
@@ -394,7 +408,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
               max(20, steps // 2))
     rep["F2_silu_mul_fwht8192_mxfp4_bf16_16384x8192"] = summary(t, 2 * ng * 2 + ng // 2 + ng // 32, ng,
                                                                 "fwht8192_kernel (SwiGLU + MXFP4)",
-                                                                valu=valu_for("F2_silu_mul_fwht8192_mxfp4_bf16_16384x8192"))
+                                                                **profiled("F2_silu_mul_fwht8192_mxfp4_bf16_16384x8192"))
     del xgd, og
     torch.cuda.empty_cache()
 
@@ -410,13 +424,13 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
                                                       "nv_amax_kernel + nv_quant_kernel (Four Over Six)",
                                                       max4_block_fraction=round(float(np.unpackbits(
                                                           o4[0].choice_bits.cpu().numpy()).mean()), 4),
-                                                      valu=valu_for("C4_four_over_six_bf16_8192x28672"))
+                                                      **profiled("C4_four_over_six_bf16_8192x28672"))
     del o4
     oi = [fq.quantize_nvfp4(x, policy="if4", workspace=ws) for x in xs4]
     t = timed(lambda i: fq.quantize_nvfp4(xs4[i % 2], policy="if4", out=oi[i % 2], workspace=ws), max(20, steps // 2))
     rep["IF4_bf16_8192x28672"] = summary(t, n4 * 2 + n4 // 2 + n4 // 16 + 4, n4,
                                          "nv_amax_kernel + nv_quant_kernel (IF4)",
-                                         valu=valu_for("IF4_bf16_8192x28672"))
+                                         **profiled("IF4_bf16_8192x28672"))
     yi = [torch.empty_like(xs4[0]) for _ in range(2)]
 
     def if4dq4(i):
@@ -424,7 +438,7 @@ def report(dev, timer, steps, warmup, ws, xs_act, nv_out):
         fq.dequantize("if4", o.codes, o.scales, o.global_scale, out_dtype=torch.bfloat16, out=yi[i % 2])
     rep["IF4_dequant_to_bf16_8192x28672"] = summary(timed(if4dq4, max(20, steps // 2)),
                                                     n4 // 2 + n4 // 16 + 4 + n4 * 2, n4, "dequant_kernel (IF4)",
-                                                    valu=valu_for("IF4_dequant_to_bf16_8192x28672"))
+                                                    **profiled("IF4_dequant_to_bf16_8192x28672"))
     del xs4, oi, yi
     torch.cuda.empty_cache()
     return rep
