@@ -700,13 +700,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",     # the arithmetic: bf16 inputs are widened to fp32 (the tensor scale in fp64)
         "data": "synthetic (2*Student-t(4), seed 102, bf16)",
         "config": {"workload": "NVFP4 two-level quantize of bf16 8192x8192 (tensor amax computed in-call), "
                                "E4M3 16-blocks + fp32 tensor scale, RNE",
                    "rows": ROWS, "cols": COLS, "algorithmic_bytes_per_step": NV_BYTES,
                    "elements_per_s": round(N / sec, 1), "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-                   "input_replicas": REPLICAS},
+                   "input_replicas": REPLICAS, "input_dtype": "bf16"},
         "roofline": {"bound": "hbm", "kernel": "nv_resident_kernel",
                      "achieved": round(call_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / HBM_PEAK_GBPS, 4),
