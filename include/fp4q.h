@@ -46,8 +46,12 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, allocated and owned by the
- *    caller.  The library allocates no device memory and keeps no state
- *    between calls.  Tensors are row-major; blocks run along a row.
+ *    caller.  The library allocates no device memory (the scratch array of
+ *    fp4q_quantize_nvfp4_noalloc is part of its code object).  Between calls
+ *    it keeps only a per-process epoch counter of the single-read NVFP4
+ *    kernel and per-device caches (CU count, that kernel's co-resident
+ *    workgroups, the scratch address), all safe to use from several host
+ *    threads.  Tensors are row-major; blocks run along a row.
  *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
  *    default stream) and never synchronise.
  *  - Argument, shape and combination checks run on the host before anything
