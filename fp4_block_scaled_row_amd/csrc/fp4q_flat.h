@@ -71,7 +71,9 @@ __device__ __forceinline__ void widen_slot(const SlotRaw<IN>& r, float v[8]) {
 // y = (sigma * x) H16 / 4, natural order.  Butterfly stages h = 1, 2, 4 run in
 // registers, h = 8 between the two lanes (the even lane holds positions 0..7).
 // Sign flips and the final x0.25 are exact.  rht16_butterflies is the part
-// after the signs.
+// after the signs; SCALED = false leaves out the final x0.25 (the tensor
+// amax takes it once, on the maximum).
+template <bool SCALED = true>
 __device__ __forceinline__ void rht16_butterflies(float v[8], bool odd_lane) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
@@ -89,7 +91,7 @@ __device__ __forceinline__ void rht16_butterflies(float v[8], bool odd_lane) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = dpp_xor1_f(v[i]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(sg1, v[i], p[i]) * 0.25f;
+  for (int i = 0; i < 8; ++i) v[i] = SCALED ? fmaf(sg1, v[i], p[i]) * 0.25f : fmaf(sg1, v[i], p[i]);
 }
 
 __device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool odd_lane) {
@@ -102,7 +104,7 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool od
 // Widening and RHT16 of a raw slot, the signs flipped in the raw words (a
 // bf16 word holds two positions, sign bits 15 and 31): the same values as
 // widen_slot then rht16_pair.
-template <int IN>
+template <int IN, bool SCALED = true>
 __device__ __forceinline__ void widen_rht16(SlotRaw<IN> r, float v[8], uint32_t signs16, bool odd_lane) {
   const uint32_t sg = odd_lane ? (signs16 >> 8) : signs16;
   if constexpr (IN == kF32) {
@@ -113,7 +115,7 @@ __device__ __forceinline__ void widen_rht16(SlotRaw<IN> r, float v[8], uint32_t 
     for (int i = 0; i < 4; ++i) r.w[i] ^= (((sg >> (2 * i)) & 1u) << 15) | (((sg >> (2 * i + 1)) & 1u) << 31);
   }
   widen_slot<IN>(r, v);
-  rht16_butterflies(v, odd_lane);
+  rht16_butterflies<SCALED>(v, odd_lane);
 }
 
 // Partner value across lane bit 2 (xor 4) within a row of 16 lanes: lanes
@@ -129,7 +131,9 @@ __device__ __forceinline__ float dpp_xor4_f(float v) {
 // run in registers, the four of the lane bits across lanes (quad
 // permutations for bits 0 and 1, bank-masked row shifts for bit 2, a row
 // rotation by 8 for bit 3);
-// the upper member of a pair keeps a - b.  Scaled once by c = fl32(1/sqrt(128)).
+// the upper member of a pair keeps a - b.  Scaled once by c = fl32(1/sqrt(128))
+// (SCALED = false leaves the scaling out, for the tensor amax).
+template <bool SCALED = true>
 __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
@@ -163,7 +167,7 @@ __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = dpp_xor8_f(v[i]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(s3, v[i], p[i]) * c;
+  for (int i = 0; i < 8; ++i) v[i] = SCALED ? fmaf(s3, v[i], p[i]) * c : fmaf(s3, v[i], p[i]);
 }
 
 __device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float v[8]) {

@@ -45,15 +45,36 @@ __device__ __forceinline__ void load_values(const QuantLaunch& q, const SlotRaw<
   }
 }
 
+// Rotated values without the rotation's final scale c.
+template <int IN, int ROT>
+__device__ __forceinline__ void load_unscaled(const QuantLaunch& q, const SlotRaw<IN>& r, int lane, float v[8]) {
+  if constexpr (ROT == kRotRht16) {
+    widen_rht16<IN, false>(r, v, q.rht_signs, (lane & 1) != 0);
+  } else {
+    widen_slot<IN>(r, v);
+    fwht128_lanes<false>(v, lane, q.rot_scale);
+  }
+}
+
 // ---------------------------------------------------------------- pass 1
+//
+// Rotated values: the largest |y| is taken before the rotation's final scale
+// c (1/4 for RHT16, fl32(1/sqrt(128)) for FWHT-128; both below 1).  x ->
+// fl(c x) is monotone, finite for finite x, and keeps infinities and NaNs, so
+// the largest finite scaled value is fl(c * the largest finite unscaled one).
+// The maxima are float maxima of absolute values (two values per
+// instruction), which pass over NaNs; a wave whose maximum comes out infinite
+// scans its slots again with the scaled values, filtering each one.
 template <int IN, int ROT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
   __shared__ uint32_t s_red[kWaves];
+  constexpr bool kRot = ROT != kRotNone;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int64_t ntiles = (q.nslots + 63) >> 6;
   uint32_t acc = 0u;  // fp32 abs bit pattern of the running finite max
+  float mrot = 0.0f;  // rotated: the running max of |y| before the scale
   for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
     SlotRaw<IN> raw[kUnroll];
 #pragma unroll
@@ -80,6 +101,11 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
           }
         }
         acc = max(acc, mx << 16);
+      } else if constexpr (kRot) {
+        float v[8];
+        load_unscaled<IN, ROT>(q, raw[u], lane, v);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) mrot = fmaxf(mrot, fmaxf(fabsf(v[i]), fabsf(v[i + 1])));
       } else {
         float v[8];
         load_values<IN, ROT, CONTIG>(q, raw[u], lane, v);
@@ -87,6 +113,29 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
         for (int i = 0; i < 8; ++i) {
           const uint32_t a = as_u(v[i]) & 0x7FFFFFFFu;
           acc = max(acc, a < 0x7F800000u ? a : 0u);
+        }
+      }
+    }
+  }
+  if constexpr (kRot) {
+    if (__ballot(mrot == __builtin_inff()) == 0ull) {
+      acc = as_u(mrot * (ROT == kRotRht16 ? 0.25f : q.rot_scale));
+    } else {
+      // (the whole wave: the rotation exchanges values between lanes)
+      for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (g * kUnroll + u >= ntiles) break;
+          const int64_t s = ((g * kUnroll + u) << 6) + lane;
+          SlotRaw<IN> raw;
+          load_slot<IN, CONTIG, false>(q, s, s < q.nslots, raw);
+          float v[8];
+          load_values<IN, ROT, CONTIG>(q, raw, lane, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t a = as_u(v[i]) & 0x7FFFFFFFu;
+            acc = max(acc, a < 0x7F800000u ? a : 0u);
+          }
         }
       }
     }

@@ -353,6 +353,40 @@ def test_nonfinite_zero_subnormal_huge(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rotation,rounding", [("rht16", "rne"), ("rht16", "stochastic"), ("fwht128", "rne")])
+@pytest.mark.parametrize("kind", ["inf", "nan"])
+def test_nv_rotated_nonfinite_amax(dtype, rotation, rounding, kind):
+    """The tensor amax of rotated values is the largest finite rotated value.
+    'inf': an infinite input and a row of huge finite inputs whose rotated
+    sums overflow, next to ordinary rows (the amax pass then rescans with a
+    filter per value); 'nan': a NaN input only (the float maxima pass over
+    it).  Compared with the oracle on the GPU's rotated values."""
+    rng = np.random.default_rng(91)
+    x = (rng.standard_t(3, (8, 128)) * 2).astype(np.float32)
+    if kind == "inf":
+        x[1, 40] = np.inf
+        x[2, :] = rng.choice([-1.0, 1.0], 128) * np.float32(3.0e38)
+    else:
+        x[1, 40] = np.nan
+    x[3, :] = np.ldexp(rng.uniform(-1, 1, 128), -130).astype(np.float32)
+    x[4, :] *= 1e30
+    xin = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    r = fq.quantize_nvfp4(to_dev(xin), rotation=rotation, rounding=rounding, seed=0x77, return_rotated=True)
+    rot = host(r.rotated)
+    if kind == "inf":
+        assert np.isinf(rot).any() and np.isfinite(rot).any()
+    else:
+        assert np.isnan(rot).any() and not np.isinf(rot).any()
+    if rounding == "rne":
+        c, s, g, _, _ = oracle.quantize_nv(rot, policy=2)
+    else:
+        c, s, g, _, _ = oracle.quantize_nv(rot, policy=2, rounding=1, seed=0x77)
+    assert host(r.global_scale)[0] == g
+    assert_same(host(r.scales), s, "scales")
+    assert_same(host(r.codes), c, "codes")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rotation", ["none", "rht16"])
 @pytest.mark.parametrize("counters", [False, True])
 def test_nv_stochastic_signed_zeros_and_subnormal_elements(dtype, rotation, counters):
