@@ -239,14 +239,27 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         uint32_t codes4;
         if constexpr (kAdj) codes4 = nv_encode_adj<COUNT>(v, c4, cx, s_adj, s_inv, sat4);
         else codes4 = nv_encode<SR, COUNT>(v, c4, cx, s_inv, rnd, sat4);
-        float e6 = half_sse(v, codes, c6, cx.g);
-        float e4 = half_sse(v, codes4, c4, cx.g);
-        const float p6 = dpp_xor1_f(e6), p4 = dpp_xor1_f(e4);
-        // S_lo (even lane, elements 0..7) + S_hi (odd lane, 8..15); fp32
-        // addition is commutative so both lanes get the same sum.
-        e6 = odd ? (p6 + e6) : (e6 + p6);
-        e4 = odd ? (p4 + e4) : (e4 + p4);
-        pick4 = (e4 < e6) && !nonfinite;
+        // the FMA sums decide the block where they can (sse_decide), the
+        // frozen order where they cannot; S_lo (even lane, elements 0..7) +
+        // S_hi (odd lane, 8..15) either way, the same sum on both lanes (fp32
+        // addition is commutative)
+        const float h6 = e4m3_value(c6) * cx.g, h4 = e4m3_value(c4) * cx.g;
+        float f6 = half_sse_fma(v, codes, h6), f4 = half_sse_fma(v, codes4, h4);
+        {
+          const float p6 = dpp_xor1_f(f6), p4 = dpp_xor1_f(f4);
+          f6 = odd ? (p6 + f6) : (f6 + p6);
+          f4 = odd ? (p4 + f4) : (f4 + p4);
+        }
+        int dec = sse_decide(f6, f4, sse_bound(f6, 6.0f * h6), sse_bound(f4, 6.0f * h4));
+        if (dec < 0 && !nonfinite) {
+          float e6 = half_sse(v, codes, c6, cx.g);
+          float e4 = half_sse(v, codes4, c4, cx.g);
+          const float p6 = dpp_xor1_f(e6), p4 = dpp_xor1_f(e4);
+          e6 = odd ? (p6 + e6) : (e6 + p6);
+          e4 = odd ? (p4 + e4) : (e4 + p4);
+          dec = e4 < e6 ? 1 : 0;
+        }
+        pick4 = dec > 0 && !nonfinite;
         if (pick4) {
           codes = codes4;
           sbyte = c4;
@@ -276,12 +289,24 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         uint32_t sati;
         const uint32_t mi = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati);
         const uint32_t ci = mi | (codes & 0x88888888u);   // the signs of the FP4 codes
-        float ef = half_sse(v, codes, c6, cx.g);
-        float ei = half_sse_int4(v, mi, s_dq + 8 * c6);
-        const float pf = dpp_xor1_f(ef), pi = dpp_xor1_f(ei);
-        ef = odd ? (pf + ef) : (ef + pf);   // S_lo + S_hi on both lanes
-        ei = odd ? (pi + ei) : (ei + pi);
-        if (ei < ef) {
+        // (as for Four Over Six: the FMA sums where they can decide)
+        const float hf = e4m3_value(c6) * cx.g, h7 = s_dq[8 * c6 + 1];
+        float ff = half_sse_fma(v, codes, hf), fi = half_sse_int4_fma(v, mi, h7);
+        {
+          const float pf = dpp_xor1_f(ff), pi = dpp_xor1_f(fi);
+          ff = odd ? (pf + ff) : (ff + pf);
+          fi = odd ? (pi + fi) : (fi + pi);
+        }
+        int dec = sse_decide(ff, fi, sse_bound(ff, 6.0f * hf), sse_bound(fi, 7.0f * h7));
+        if (dec < 0 && !nonfinite) {
+          float ef = half_sse(v, codes, c6, cx.g);
+          float ei = half_sse_int4(v, mi, s_dq + 8 * c6);
+          const float pf = dpp_xor1_f(ef), pi = dpp_xor1_f(ei);
+          ef = odd ? (pf + ef) : (ef + pf);   // S_lo + S_hi on both lanes
+          ei = odd ? (pi + ei) : (ei + pi);
+          dec = ei < ef ? 1 : 0;
+        }
+        if (dec > 0) {
           codes = ci;
           sbyte = c6 | 0x80u;
           satm = sati;
@@ -572,18 +597,37 @@ __global__ __launch_bounds__(kThreads) void nv_fos_fast_kernel(QuantLaunch q, in
         FP4Q_FOS_WORD(2)
         FP4Q_FOS_WORD(3)
 #undef FP4Q_FOS_WORD
-        float ea6 = half_sse_sd(xa, a6, sa6, cx.g), ea4 = half_sse_sd(xa, a4, sa4, cx.g);
-        float eb6 = half_sse_sd(xb, c6, sb6, cx.g), eb4 = half_sse_sd(xb, c4, sb4, cx.g);
-        // S_lo (even lane) + S_hi (odd lane), the same sum on both lanes
+        // the FMA sums decide each block where they can (sse_decide), the
+        // frozen order where they cannot; S_lo (even lane) + S_hi (odd lane),
+        // the same sum on both lanes
+        const float ha6 = sa6 * cx.g, ha4 = sa4 * cx.g, hb6 = sb6 * cx.g, hb4 = sb4 * cx.g;
+        float fa6 = half_sse_fma(xa, a6, ha6), fa4 = half_sse_fma(xa, a4, ha4);
+        float fb6 = half_sse_fma(xb, c6, hb6), fb4 = half_sse_fma(xb, c4, hb4);
         {
-          const float q1 = dpp_xor1_f(ea6), q2 = dpp_xor1_f(ea4), q3 = dpp_xor1_f(eb6), q4 = dpp_xor1_f(eb4);
+          const float q1 = dpp_xor1_f(fa6), q2 = dpp_xor1_f(fa4), q3 = dpp_xor1_f(fb6), q4 = dpp_xor1_f(fb4);
+          fa6 = odd ? (q1 + fa6) : (fa6 + q1);
+          fa4 = odd ? (q2 + fa4) : (fa4 + q2);
+          fb6 = odd ? (q3 + fb6) : (fb6 + q3);
+          fb4 = odd ? (q4 + fb4) : (fb4 + q4);
+        }
+        int da = sse_decide(fa6, fa4, sse_bound(fa6, 6.0f * ha6), sse_bound(fa4, 6.0f * ha4));
+        int db = sse_decide(fb6, fb4, sse_bound(fb6, 6.0f * hb6), sse_bound(fb4, 6.0f * hb4));
+        if (da < 0) {
+          float ea6 = half_sse_sd(xa, a6, sa6, cx.g), ea4 = half_sse_sd(xa, a4, sa4, cx.g);
+          const float q1 = dpp_xor1_f(ea6), q2 = dpp_xor1_f(ea4);
           ea6 = odd ? (q1 + ea6) : (ea6 + q1);
           ea4 = odd ? (q2 + ea4) : (ea4 + q2);
+          da = ea4 < ea6 ? 1 : 0;
+        }
+        if (db < 0) {
+          float eb6 = half_sse_sd(xb, c6, sb6, cx.g), eb4 = half_sse_sd(xb, c4, sb4, cx.g);
+          const float q3 = dpp_xor1_f(eb6), q4 = dpp_xor1_f(eb4);
           eb6 = odd ? (q3 + eb6) : (eb6 + q3);
           eb4 = odd ? (q4 + eb4) : (eb4 + q4);
+          db = eb4 < eb6 ? 1 : 0;
         }
-        pa = ea4 < ea6;
-        pb = eb4 < eb6;
+        pa = da > 0;
+        pb = db > 0;
         ca = pa ? a4 : a6;
         cb = pb ? c4 : c6;
         const bool pw = odd ? pb : pa;                       // the block this lane worked out

@@ -557,6 +557,75 @@ __device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t mags, 
   return acc;
 }
 
+// ---------------------------------------------------------------- SSE decisions
+// Four Over Six and IF4 keep their alternative candidate iff its block SSE in
+// the frozen fp32 order of half_sse (S_lo + S_hi over the lane pair) is
+// lower; ties keep the default.  Most blocks are decided by cheaper sums:
+// d' = fma(-value, h, x) with h = fl(s g) (INT4: h = RN32(6 s g / 7) and the
+// integer k as the value), the squares accumulated by FMAs in element order,
+// A = A_lo + A_hi.  Error analysis, u = 2^-24, t_i = x_i - value_i s g
+// exactly, M = 6 s g (at least every |value_i s g|), no overflow: the frozen
+// d_i and d'_i both lie within u |t_i| + u (1 + u) M of t_i, and every square
+// reaches its sum through at most nine roundings, so
+//   |S - A| <= 22.2 u A + 16.2 u M sqrt(A) + 100 u^2 M^2
+//           <= 30.4 u A + 8.2 u M^2 + 100 u^2 M^2   (M sqrt(A) <= (M^2 + A) / 2).
+// Results rounded into the subnormal range add at most 2^-144 in all.
+// sse_bound gives more than twice that; sse_decide decides a block only when
+// its two sums are further apart than their bounds together, and sends
+// everything else (near ties, sums above 2^120, infinities, NaNs) to the
+// frozen order.
+
+// A_lo or A_hi of one candidate: codes as E2M1 nibbles (signs included),
+// h = fl(s g).
+__device__ __forceinline__ float half_sse_fma(const float v[8], uint32_t codes, float h) {
+  const float one = e8m0_operand(127u);
+  float val[8];
+  float2_t p;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0); val[0] = p.x; val[1] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1); val[2] = p.x; val[3] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2); val[4] = p.x; val[5] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3); val[6] = p.x; val[7] = p.y;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float d = fmaf(-val[i], h, v[i]);
+    acc = fmaf(d, d, acc);
+  }
+  return acc;
+}
+
+// The same for the INT4 candidate: mags the magnitudes k (nibbles, signs
+// apart), h7 = RN32(6 s g / 7); d' = |x| - k h7.
+__device__ __forceinline__ float half_sse_int4_fma(const float v[8], uint32_t mags, float h7) {
+  const uint32_t ev = mags & 0x0F0F0F0Fu, od = (mags >> 4) & 0x0F0F0F0Fu;   // k of even / odd elements, a byte each
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float k = (float)((((i & 1) ? od : ev) >> (8 * (i >> 1))) & 0xFFu);
+    const float d = fmaf(-k, h7, fabsf(v[i]));
+    acc = fmaf(d, d, acc);
+  }
+  return acc;
+}
+
+// Bound on |S - A| for a block sum A of a candidate with M = 6 s g:
+// 2^-18 A + 2^-19 M^2 + 2^-129 (64 u A + 32 u M^2 against the 30.4 u A +
+// 8.2 u M^2 + ... above).
+__device__ __forceinline__ float sse_bound(float a, float m) {
+  return fmaf(0x1p-18f, a, fmaf(0x1p-19f, m * m, 0x1p-129f));
+}
+
+// 1: keep the alternative (its frozen SSE is lower), 0: keep the default,
+// -1: the sums cannot tell; the frozen order must decide.  Both lanes of a
+// pair hold the same sums and get the same answer.
+__device__ __forceinline__ int sse_decide(float a_def, float a_alt, float e_def, float e_alt) {
+  if (!(fmaxf(a_def, a_alt) < 0x1p120f)) return -1;
+  const float gap = a_def - a_alt, et = e_def + e_alt;
+  if (gap > et) return 1;
+  if (-gap >= et) return 0;
+  return -1;
+}
+
 // Exact max->6 round-to-nearest encoding of flat slot s of a contiguous bf16
 // tensor from its 16-block (a: first half, b: second half), by the brackets
 // and the exact decisions above; a block holding a non-finite value gets
