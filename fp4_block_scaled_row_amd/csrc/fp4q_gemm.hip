@@ -17,11 +17,15 @@
 // four waves (one per SIMD) a 128x128 quarter: 4x4 instructions per 64-K
 // step on 256 accumulator registers, so every operand fetched from LDS feeds
 // four instructions.  K advances 128 per stage: the A and B tiles (256 rows x
-// 64 bytes) and their scale bytes are loaded straight into LDS (buffer loads
-// with the LDS destination: in that form, unlike the flat one, the compiler
-// lets an LDS read wait only for the loads it depends on), into a ring of
-// four stage buffers kept three stages ahead of the one being multiplied;
-// one fence-free barrier per stage, the loads being waited for explicitly.
+// 64 bytes) are loaded straight into LDS (buffer loads with the LDS
+// destination: in that form, unlike the flat one, the compiler lets an LDS
+// read wait only for the loads it depends on), into a ring of four stage
+// buffers kept three stages ahead of the one being multiplied; one fence-free
+// barrier per stage, the loads being waited for explicitly.  The scale bytes
+// go straight into registers, 16 bytes of a row (four stages) per load, one
+// group of four stages ahead: the load unit moves about one cache line a
+// clock per CU, and a 4-byte load per row and stage would cost a line for
+// every 4 bytes.
 // Buffer offsets are 32-bit: K is at most 2^23.  A tile wholly inside C
 // (with 16-byte aligned rows) leaves through LDS as 16-byte row chunks; other
 // tiles store element by element.  Workgroups are
@@ -48,26 +52,25 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // LDS stage buffer: A codes (256 rows x 64 bytes, the four 16-byte chunks of
-// a row permuted by (row >> 1) mod 4 to spread reads over the banks), B
-// codes, then the 4 scale bytes of each A row and of each B row.
+// a row permuted by (row >> 1) mod 4 to spread reads over the banks), then B
+// codes.
 constexpr int kCodeBytes = kTile * kRowBytes;               // 16 KiB
-constexpr int kStageBytes = 2 * kCodeBytes + 2 * kTile * 4;
-constexpr int kLoadsPerStage = 2 * (kCodeBytes / 1024 / 4) + 2;   // per lane: 4 + 4 codes, 1 + 1 scales
+constexpr int kStageBytes = 2 * kCodeBytes;
+constexpr int kLoadsPerStage = 2 * (kCodeBytes / 1024 / 4);   // per lane: 4 + 4 codes
+constexpr int kGroup = 4;                                     // stages per 16 scale bytes of a row
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int chunk_of(int row, int part) { return part ^ ((row >> 1) & 3); }
 
 // Direct-to-LDS loads through a buffer descriptor at base (bytes long), of 16
-// or 4 bytes per lane: lane l writes lds + 16 l (4 l); off is this lane's
-// byte offset from base.
+// bytes per lane: lane l writes lds + 16 l; off is this lane's byte offset
+// from base.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const uint8_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
                                            (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
 }
 __device__ __forceinline__ void buf_lds16(const uint8_t* base, int64_t bytes, lds_void_t* lds, int off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base, bytes), lds, 16, off, 0, 0, 0);
-}
-__device__ __forceinline__ void buf_lds4(const uint8_t* base, int64_t bytes, lds_void_t* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base, bytes), lds, 4, off, 0, 0, 0);
 }
 
 // s_waitcnt with vmcnt <= n (expcnt and lgkmcnt not waited for)
@@ -117,13 +120,29 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
       buf_lds16(a_c, na_c, (lds_void_t*)(buf + region * 1024), (int)(ra * kb + kbyte + part * 16));
       buf_lds16(b_c, nb_c, (lds_void_t*)(buf + kCodeBytes + region * 1024), (int)(rb * kb + kbyte + part * 16));
     }
-    const int row = wv * 64 + lane;
-    const int64_t ra = min(m0 + row, g.M - 1) - m0, rb = min(n0 + row, g.N - 1) - n0;
-    buf_lds4(a_s, na_s, (lds_void_t*)(buf + 2 * kCodeBytes + wv * 256), (int)(ra * ksb + (int64_t)st * 4));
-    buf_lds4(b_s, nb_s, (lds_void_t*)(buf + 2 * kCodeBytes + kTile * 4 + wv * 256), (int)(rb * ksb + (int64_t)st * 4));
+  };
+  // scale bytes of the four stages of group gi for this lane's 4 A rows and 4 B
+  // rows: 16 bytes a row, straight into registers (lanes l and l + 32 read the
+  // same row; bytes past a row's end, read for a last group of fewer than four
+  // stages, are never used)
+  const int wr = wv >> 1, wc = wv & 1;
+  int a_soff[kSub], b_soff[kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    const int r = kWaveTile * wr + 32 * u + (lane & 31), c = kWaveTile * wc + 32 * u + (lane & 31);
+    a_soff[u] = (int)((min(m0 + r, g.M - 1) - m0) * ksb);
+    b_soff[u] = (int)((min(n0 + c, g.N - 1) - n0) * ksb);
+  }
+  const __amdgpu_buffer_rsrc_t a_srs = buf_rsrc(a_s, na_s), b_srs = buf_rsrc(b_s, nb_s);
+  v4u_t sA[2][kSub], sB[2][kSub];
+  auto load_scales = [&](int gi, v4u_t (&da)[kSub], v4u_t (&db)[kSub]) {
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      da[u] = __builtin_amdgcn_raw_buffer_load_b128(a_srs, a_soff[u] + 16 * gi, 0, 0);
+      db[u] = __builtin_amdgcn_raw_buffer_load_b128(b_srs, b_soff[u] + 16 * gi, 0, 0);
+    }
   };
 
-  const int wr = wv >> 1, wc = wv & 1;
   v16f_t acc[kSub][kSub];
 #pragma unroll
   for (int i = 0; i < kSub; ++i)
@@ -135,9 +154,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
   // a stage's operands, both 64-K steps
   v8i_t a[2][kSub], b[2][kSub];
   int sa[2][kSub], sb[2][kSub];
-  auto read = [&](const uint8_t* buf) {
-    const uint32_t* sa_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes);
-    const uint32_t* sb_row = reinterpret_cast<const uint32_t*>(buf + 2 * kCodeBytes + kTile * 4);
+  auto read = [&](const uint8_t* buf, const v4u_t (&ra_)[kSub], const v4u_t (&rb_)[kSub], int sg) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int part = 2 * kk + (lane >> 5);   // this lane's 32 K positions of the 64-K step
@@ -146,11 +163,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
         const int arow = kWaveTile * wr + 32 * u + (lane & 31);
         const uint4 va = *reinterpret_cast<const uint4*>(buf + arow * kRowBytes + chunk_of(arow, part) * 16);
         a[kk][u] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-        sa[kk][u] = (int)((sa_row[arow] >> (8 * part)) & 0xFFu);
+        sa[kk][u] = (int)((ra_[u][sg] >> (8 * part)) & 0xFFu);
         const int brow = kWaveTile * wc + 32 * u + (lane & 31);
         const uint4 vb = *reinterpret_cast<const uint4*>(buf + kCodeBytes + brow * kRowBytes + chunk_of(brow, part) * 16);
         b[kk][u] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        sb[kk][u] = (int)((sb_row[brow] >> (8 * part)) & 0xFFu);
+        sb[kk][u] = (int)((rb_[u][sg] >> (8 * part)) & 0xFFu);
       }
     }
   };
@@ -163,40 +180,53 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmLaunch g, int tiles_m,
                                                                     sa[kk][i], 0, sb[kk][j]);
   };
   // one pipeline step: wait for this thread's loads of stage st (stages
-  // st + 1 and st + 2 stay in flight), one barrier -- after it every wave's
+  // st + 1 and st + 2, and the next scale group, stay in flight), one barrier -- after it every wave's
   // loads of stage st are in LDS and every wave is done with stage st - 1 --
   // then read stage st's operands, multiply the first 64-K step (its operands
   // arrive first), refill stage st - 1's buffer with stage st + 3 and
-  // multiply the second step.  Every LDS read of the step is issued before
-  // the refill, so none of them waits for it.  The barrier carries no memory
-  // fence: the loads are waited for explicitly.
-  auto step = [&](int st, uint8_t* cur, uint8_t* fill) {
-    if (st + 2 < nstage) wait_vm<2 * kLoadsPerStage>();
-    else if (st + 1 < nstage) wait_vm<kLoadsPerStage>();
+  // multiply the second step (the first step of a scale group also loads the
+  // next group's scales after the refill).  Every LDS read of the step is
+  // issued before the refill, so none of them waits for it.  The barrier
+  // carries no memory fence: the loads are waited for explicitly.  The wait
+  // counts the vm loads issued after stage st's refill, the moment step st
+  // begins: the
+  // refills of st + 1 and st + 2, and the scale group loaded by the first step
+  // of st's group when that step came after st's refill was issued (st not
+  // the first of its group)
+  auto step = [&](int st, uint8_t* cur, uint8_t* fill, const v4u_t (&ra_)[kSub], const v4u_t (&rb_)[kSub],
+                  v4u_t (&na_)[kSub], v4u_t (&nb_)[kSub]) {
+    const int sg = st % kGroup;
+    const int after = (st + 1 < nstage ? 1 : 0) + (st + 2 < nstage ? 1 : 0) +
+                      ((sg != 0 && st - sg + kGroup < nstage) ? 1 : 0);
+    if (after == 3) wait_vm<3 * kLoadsPerStage>();
+    else if (after == 2) wait_vm<2 * kLoadsPerStage>();
+    else if (after == 1) wait_vm<kLoadsPerStage>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    read(cur);
+    read(cur, ra_, rb_, sg);
     __builtin_amdgcn_sched_barrier(0);
     mma(0);
     __builtin_amdgcn_sched_barrier(0);
     if (st + 3 < nstage) issue(st + 3, fill);
+    if (sg == 0 && st + kGroup < nstage) load_scales(st / kGroup + 1, na_, nb_);
     __builtin_amdgcn_sched_barrier(0);
     mma(1);
   };
 
+  if (nstage > 0) load_scales(0, sA[0], sB[0]);
   if (nstage > 0) issue(0, s_st0);
   if (nstage > 1) issue(1, s_st1);
   if (nstage > 2) issue(2, s_st2);
-  // (unrolled over two rotations of the ring)
+  // (unrolled over two rotations of the ring, two scale groups)
   for (int st = 0; st < nstage; st += 8) {
-    step(st, s_st0, s_st3);
-    if (st + 1 < nstage) step(st + 1, s_st1, s_st0);
-    if (st + 2 < nstage) step(st + 2, s_st2, s_st1);
-    if (st + 3 < nstage) step(st + 3, s_st3, s_st2);
-    if (st + 4 < nstage) step(st + 4, s_st0, s_st3);
-    if (st + 5 < nstage) step(st + 5, s_st1, s_st0);
-    if (st + 6 < nstage) step(st + 6, s_st2, s_st1);
-    if (st + 7 < nstage) step(st + 7, s_st3, s_st2);
+    step(st, s_st0, s_st3, sA[0], sB[0], sA[1], sB[1]);
+    if (st + 1 < nstage) step(st + 1, s_st1, s_st0, sA[0], sB[0], sA[1], sB[1]);
+    if (st + 2 < nstage) step(st + 2, s_st2, s_st1, sA[0], sB[0], sA[1], sB[1]);
+    if (st + 3 < nstage) step(st + 3, s_st3, s_st2, sA[0], sB[0], sA[1], sB[1]);
+    if (st + 4 < nstage) step(st + 4, s_st0, s_st3, sA[1], sB[1], sA[0], sB[0]);
+    if (st + 5 < nstage) step(st + 5, s_st1, s_st0, sA[1], sB[1], sA[0], sB[0]);
+    if (st + 6 < nstage) step(st + 6, s_st2, s_st1, sA[1], sB[1], sA[0], sB[0]);
+    if (st + 7 < nstage) step(st + 7, s_st3, s_st2, sA[1], sB[1], sA[0], sB[0]);
   }
 
   // A tile wholly inside C, with 16-byte aligned rows: each wave writes its
