@@ -67,12 +67,41 @@ __device__ __forceinline__ void widen_slot(const SlotRaw<IN>& r, float v[8]) {
   }
 }
 
+// Cross-lane butterfly stages in one instruction per element.  A stage over
+// lane bit k pairs lane l (bit k clear, the lower member) with l ^ 2^k; the
+// butterfly gives the lower member a + b and the upper one a - b.  The form
+// used here is v <- p * s + v (v_fmac_f32_dpp: p is the partner's value read
+// through the DPP control, s = +1 on the lower lane and -1 on the upper), so
+// the upper lane gets b - a, the exact negative of a - b: the same rounded
+// magnitude, sign flipped.  Partners always carry the same accumulated sign
+// (it depends only on lane bits already processed), so the stages compose and
+// the caller applies the product of the signs once, with its final scale.
+// Only an output that is an exact zero can come out with the other sign.
+// A DPP read of a register needs two wait states after the VALU write of
+// it: each block opens with s_nop 1, and within a block every source was
+// written at least eight instructions earlier.
+#define FP4Q_FMAC_DPP(D, S, CTRL) "v_fmac_f32_dpp %" #D ", %" #D ", %" #S " " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define FP4Q_QX1 "quad_perm:[1,0,3,2]"
+#define FP4Q_QX2 "quad_perm:[2,3,0,1]"
+#define FP4Q_RX8 "row_ror:8"
+
+// v[i] <- p[i] * s + v[i] across the lane pair (lane bit 0), 8 registers.
+__device__ __forceinline__ void fmac_dpp_xor1_8(float v[8], float s) {
+  asm("s_nop 1\n\t"
+      FP4Q_FMAC_DPP(0, 8, FP4Q_QX1) FP4Q_FMAC_DPP(1, 8, FP4Q_QX1) FP4Q_FMAC_DPP(2, 8, FP4Q_QX1)
+      FP4Q_FMAC_DPP(3, 8, FP4Q_QX1) FP4Q_FMAC_DPP(4, 8, FP4Q_QX1) FP4Q_FMAC_DPP(5, 8, FP4Q_QX1)
+      FP4Q_FMAC_DPP(6, 8, FP4Q_QX1) FP4Q_FMAC_DPP(7, 8, FP4Q_QX1)
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+      : "v"(s));
+}
+
 // 16-point random Hadamard transform of the 16-block held by a lane pair:
 // y = (sigma * x) H16 / 4, natural order.  Butterfly stages h = 1, 2, 4 run in
 // registers, h = 8 between the two lanes (the even lane holds positions 0..7).
 // Sign flips and the final x0.25 are exact.  rht16_butterflies is the part
-// after the signs; SCALED = false leaves out the final x0.25 (the tensor
-// amax takes it once, on the maximum).
+// after the signs; SCALED = false leaves out the final x0.25 and the odd
+// lane's sign (the tensor amax takes the magnitudes, scaled once on the
+// maximum).
 template <bool SCALED = true>
 __device__ __forceinline__ void rht16_butterflies(float v[8], bool odd_lane) {
 #pragma unroll
@@ -85,13 +114,14 @@ __device__ __forceinline__ void rht16_butterflies(float v[8], bool odd_lane) {
       v[i + h] = a - b;
     }
   }
-  // (the even lane takes v + p, the odd lane p - v: one FMA with a sign)
+  // the odd lane holds the negated difference until the final scale
   const float sg1 = odd_lane ? -1.0f : 1.0f;
-  float p[8];
+  fmac_dpp_xor1_8(v, sg1);
+  if constexpr (SCALED) {
+    const float q = odd_lane ? -0.25f : 0.25f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor1_f(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = SCALED ? fmaf(sg1, v[i], p[i]) * 0.25f : fmaf(sg1, v[i], p[i]);
+    for (int i = 0; i < 8; ++i) v[i] *= q;
+  }
 }
 
 __device__ __forceinline__ void rht16_pair(float v[8], uint32_t signs16, bool odd_lane) {
@@ -118,21 +148,18 @@ __device__ __forceinline__ void widen_rht16(SlotRaw<IN> r, float v[8], uint32_t 
   rht16_butterflies<SCALED>(v, odd_lane);
 }
 
-// Partner value across lane bit 2 (xor 4) within a row of 16 lanes: lanes
-// 4-7 and 12-15 read lane - 4 (row_shr:4, written to those banks only),
-// lanes 0-3 and 8-11 lane + 4 (row_shl:4).  (Bit 3 is one row rotation.)
-__device__ __forceinline__ float dpp_xor4_f(float v) {
-  const int up = __builtin_amdgcn_update_dpp(0, (int)as_u(v), 0x114, 0xF, 0xA, false);
-  return as_f((uint32_t)__builtin_amdgcn_update_dpp(up, (int)as_u(v), 0x104, 0xF, 0x5, false));
-}
-
 // Normalised FWHT of each 128-element chunk held by 16 consecutive lanes, 8
 // consecutive elements each: the three butterfly stages of the element bits
-// run in registers, the four of the lane bits across lanes (quad
-// permutations for bits 0 and 1, bank-masked row shifts for bit 2, a row
-// rotation by 8 for bit 3);
-// the upper member of a pair keeps a - b.  Scaled once by c = fl32(1/sqrt(128))
-// (SCALED = false leaves the scaling out, for the tensor amax).
+// run in registers, the four of the lane bits across lanes in one block of
+// DPP instructions (fmac_dpp_xor1_8 above for the sign convention): lane bits
+// 0, 1 and 3 by v_fmac_f32_dpp (quad permutations, a row rotation by 8), lane
+// bit 2 by a bank-masked add (lanes 0-3 and 8-11 of each row, partner + 4)
+// and subtract (lanes 4-7 and 12-15, partner - 4) into fresh registers,
+// which keep the sign.  The accumulated sign is s0 s1 s3; scaled once by
+// c = fl32(1/sqrt(128)) with that sign folded in (SCALED = false leaves both
+// out, for the tensor amax, which takes magnitudes).
+#define FP4Q_ADD_X4(D, S) "v_add_f32_dpp %" #D ", %" #S ", %" #S " row_shl:4 row_mask:0xf bank_mask:0x5\n\t" \
+                          "v_sub_f32_dpp %" #D ", %" #S ", %" #S " row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
 template <bool SCALED = true>
 __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
 #pragma unroll
@@ -145,29 +172,32 @@ __device__ __forceinline__ void fwht128_lanes(float v[8], int lane, float c) {
       v[i + h] = a - b;
     }
   }
-  // the lower member of a pair takes v + p, the upper p - v: one FMA with a
-  // per-lane sign (s v is exact, so it rounds as the sum or difference);
-  // stage by stage over the 8 elements, so that no exchange waits on the
-  // element it follows
-  const float s0 = (lane & 1) ? -1.0f : 1.0f, s1 = (lane & 2) ? -1.0f : 1.0f;
-  const float s2 = (lane & 4) ? -1.0f : 1.0f, s3 = (lane & 8) ? -1.0f : 1.0f;
-  float p[8];
+  const float s0 = (lane & 1) ? -1.0f : 1.0f, s1 = (lane & 2) ? -1.0f : 1.0f, s3 = (lane & 8) ? -1.0f : 1.0f;
+  float t[8];
+  // t: operands 0-7, v: 8-15, s0, s1, s3: 16-18
+  asm("s_nop 1\n\t"
+      FP4Q_FMAC_DPP(8, 16, FP4Q_QX1) FP4Q_FMAC_DPP(9, 16, FP4Q_QX1) FP4Q_FMAC_DPP(10, 16, FP4Q_QX1)
+      FP4Q_FMAC_DPP(11, 16, FP4Q_QX1) FP4Q_FMAC_DPP(12, 16, FP4Q_QX1) FP4Q_FMAC_DPP(13, 16, FP4Q_QX1)
+      FP4Q_FMAC_DPP(14, 16, FP4Q_QX1) FP4Q_FMAC_DPP(15, 16, FP4Q_QX1)
+      FP4Q_FMAC_DPP(8, 17, FP4Q_QX2) FP4Q_FMAC_DPP(9, 17, FP4Q_QX2) FP4Q_FMAC_DPP(10, 17, FP4Q_QX2)
+      FP4Q_FMAC_DPP(11, 17, FP4Q_QX2) FP4Q_FMAC_DPP(12, 17, FP4Q_QX2) FP4Q_FMAC_DPP(13, 17, FP4Q_QX2)
+      FP4Q_FMAC_DPP(14, 17, FP4Q_QX2) FP4Q_FMAC_DPP(15, 17, FP4Q_QX2)
+      FP4Q_ADD_X4(0, 8) FP4Q_ADD_X4(1, 9) FP4Q_ADD_X4(2, 10) FP4Q_ADD_X4(3, 11)
+      FP4Q_ADD_X4(4, 12) FP4Q_ADD_X4(5, 13) FP4Q_ADD_X4(6, 14) FP4Q_ADD_X4(7, 15)
+      FP4Q_FMAC_DPP(0, 18, FP4Q_RX8) FP4Q_FMAC_DPP(1, 18, FP4Q_RX8) FP4Q_FMAC_DPP(2, 18, FP4Q_RX8)
+      FP4Q_FMAC_DPP(3, 18, FP4Q_RX8) FP4Q_FMAC_DPP(4, 18, FP4Q_RX8) FP4Q_FMAC_DPP(5, 18, FP4Q_RX8)
+      FP4Q_FMAC_DPP(6, 18, FP4Q_RX8) FP4Q_FMAC_DPP(7, 18, FP4Q_RX8)
+      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]),
+        "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+      : "v"(s0), "v"(s1), "v"(s3));
+  if constexpr (SCALED) {
+    const float cs = c * (s0 * s1 * s3);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor1_f(v[i]);
+    for (int i = 0; i < 8; ++i) v[i] = t[i] * cs;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(s0, v[i], p[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor2_f(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(s1, v[i], p[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor4_f(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(s2, v[i], p[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = dpp_xor8_f(v[i]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = SCALED ? fmaf(s3, v[i], p[i]) * c : fmaf(s3, v[i], p[i]);
+    for (int i = 0; i < 8; ++i) v[i] = t[i];
+  }
 }
 
 __device__ __forceinline__ void store_rotated(float* rot, int64_t s, const float v[8]) {

@@ -138,12 +138,24 @@ __global__ __launch_bounds__(128) void fwht8192_kernel(FwhtLaunch f, float c) {
           u[r] = a + b;
           u[r + h] = a - b;
         }
-    // (the even lane takes u + p, the odd lane p - u: one FMA with a sign)
     const float sg = (l & 1) ? -1.0f : 1.0f;
+    if constexpr ((IN & kSwiGlu) == 0) {
+      // one v_fmac_f32_dpp per element: the odd lane holds u - p, the
+      // negative of its p - u, until the scale by c, which takes the sign
+      const float cs = c * sg;
 #pragma unroll
-    for (int r = 0; r < 64; ++r) {
-      const float p = dpp_xor1_f(u[r]);
-      u[r] = fmaf(sg, u[r], p) * c;
+      for (int r = 0; r < 64; r += 8) fmac_dpp_xor1_8(u + r, sg);
+#pragma unroll
+      for (int r = 0; r < 64; ++r) u[r] *= cs;
+    } else {
+      // (the even lane takes u + p, the odd lane p - u: a move and an FMA;
+      // with the SwiGLU loads the DPP blocks above measured much slower, the
+      // compiler then placing the next barrier before the butterflies)
+#pragma unroll
+      for (int r = 0; r < 64; ++r) {
+        const float p = dpp_xor1_f(u[r]);
+        u[r] = fmaf(sg, u[r], p) * c;
+      }
     }
     // ---- transpose M -> L
     __syncthreads();

@@ -578,7 +578,8 @@ __global__ __launch_bounds__(kThreads) void nv_fos_fast_kernel(QuantLaunch q, in
         const float2 e6 = s_adj[b6 & 0xFFu], e4 = s_adj[b4 & 0xFFu];
         const uint32_t need = (__builtin_amdgcn_alignbit(b6, b6, 9) ^ (b6 << 31)) | as_u(e6.y) |
                               (__builtin_amdgcn_alignbit(b4, b4, 9) ^ (b4 << 31)) | as_u(e4.y);
-        const float sd6 = e4m3_value(b6 & 0x7Fu), sd4 = e4m3_value(b4 & 0x7Fu);
+        // (a NaN for byte 0x7F: such a block is flagged and redone exactly)
+        const float sd6 = e4m3_value_hw(b6 & 0x7Fu), sd4 = e4m3_value_hw(b4 & 0x7Fu);
         // block A (tile ta) was worked out by the even lane, block B by the odd one
         const float ma6 = as_f(dpp_u32<kQuadEven>(as_u(e6.x))), mb6 = as_f(dpp_u32<kQuadOdd>(as_u(e6.x)));
         const float ma4 = as_f(dpp_u32<kQuadEven>(as_u(e4.x))), mb4 = as_f(dpp_u32<kQuadOdd>(as_u(e4.x)));
@@ -587,16 +588,22 @@ __global__ __launch_bounds__(kThreads) void nv_fos_fast_kernel(QuantLaunch q, in
         need_a = (dpp_u32<kQuadEven>(need) >> 31) != 0u;
         need_b = (dpp_u32<kQuadOdd>(need) >> 31) != 0u;
         uint32_t a6 = 0u, a4 = 0u, c6 = 0u, c4 = 0u;
+        // (the old operand of the first conversion of each word only fills
+        // bytes that the next three overwrite: a dead value, no zeroing move)
+#define FP4Q_FOS_CVT(C, X, M, K)                                                                    \
+  {                                                                                                 \
+    const float lo = X[2 * K] * M, hi = X[2 * K + 1] * M;                                           \
+    C = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(K == 0 ? as_u(lo) : C, lo, hi, one, K);            \
+  }
 #define FP4Q_FOS_WORD(K)                                                                            \
-  a6 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a6, xa[2 * K] * ma6, xa[2 * K + 1] * ma6, one, K);  \
-  a4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a4, xa[2 * K] * ma4, xa[2 * K + 1] * ma4, one, K);  \
-  c6 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c6, xb[2 * K] * mb6, xb[2 * K + 1] * mb6, one, K);  \
-  c4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c4, xb[2 * K] * mb4, xb[2 * K + 1] * mb4, one, K);
+  FP4Q_FOS_CVT(a6, xa, ma6, K) FP4Q_FOS_CVT(a4, xa, ma4, K) FP4Q_FOS_CVT(c6, xb, mb6, K)            \
+  FP4Q_FOS_CVT(c4, xb, mb4, K)
         FP4Q_FOS_WORD(0)
         FP4Q_FOS_WORD(1)
         FP4Q_FOS_WORD(2)
         FP4Q_FOS_WORD(3)
 #undef FP4Q_FOS_WORD
+#undef FP4Q_FOS_CVT
         // the FMA sums decide each block where they can (sse_decide), the
         // frozen order where they cannot; S_lo (even lane) + S_hi (odd lane),
         // the same sum on both lanes
