@@ -52,6 +52,32 @@ __device__ __forceinline__ float dpp_xor1_f(float v) { return as_f(dpp_u32<kQuad
 __device__ __forceinline__ float dpp_xor2_f(float v) { return as_f(dpp_u32<kQuadXor2>(as_u(v))); }
 __device__ __forceinline__ float dpp_xor8_f(float v) { return as_f(dpp_u32<kRowRor8>(as_u(v))); }
 
+// max(m, |a|, |b|) in one v_max3_f32 with absolute-value modifiers.  It
+// passes over quiet NaNs as fmaxf does; callers give it arithmetic results,
+// which are never signalling NaNs, so the canonicalising max the compiler
+// puts before each fmaxf operand is not needed.
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+// Largest |v[i]| of 8 values as an fp32 bit pattern, the same value as the
+// integer maximum of the magnitude bits (as_u(v) & 0x7FFFFFFF) for every
+// input without a NaN; a NaN anywhere gives a NaN pattern, which like the
+// integer maximum is at least 0x7F800000.  Four v_maximum3_f32 (the IEEE
+// maximum, which propagates NaNs) with absolute-value modifiers, against
+// eight masks and four integer maxima.
+__device__ __forceinline__ uint32_t abs_max_bits8(const float v[8]) {
+  float m;
+  asm("v_maximum3_f32 %0, |%1|, |%2|, |%3|\n\t"
+      "v_maximum3_f32 %0, %0, |%4|, |%5|\n\t"
+      "v_maximum3_f32 %0, %0, |%6|, |%7|\n\t"
+      "v_maximum3_f32 %0, %0, |%8|, |%8|"
+      : "=&v"(m) : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+  return as_u(m);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {

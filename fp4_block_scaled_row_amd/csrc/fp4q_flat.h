@@ -244,9 +244,7 @@ __device__ __forceinline__ void mx_encode_slot(const float v[8], int64_t s, bool
                                                int manual_e, uint64_t seed, uint8_t* codes_out,
                                                uint8_t* scales_out, uint32_t& n_sat, uint32_t& n_und,
                                                uint32_t& n_nf) {
-  uint32_t amax = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = max(amax, as_u(v[i]) & 0x7FFFFFFFu);
+  uint32_t amax = abs_max_bits8(v);
   amax = max(amax, dpp_u32<kQuadXor1>(amax));
   amax = max(amax, dpp_u32<kQuadXor2>(amax));
   const bool nonfinite = amax >= 0x7F800000u;

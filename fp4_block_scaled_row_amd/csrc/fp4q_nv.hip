@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
         float v[8];
         load_unscaled<IN, ROT>(q, raw[u], lane, v);
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) mrot = fmaxf(mrot, fmaxf(fabsf(v[i]), fabsf(v[i + 1])));
+        for (int i = 0; i < 8; i += 2) mrot = max3_abs(mrot, v[i], v[i + 1]);
       } else {
         float v[8];
         load_values<IN, ROT, CONTIG>(q, raw[u], lane, v);
@@ -214,9 +214,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       float v[8];
       load_values<IN, ROT, CONTIG>(q, raw[u], lane, v);
 
-      uint32_t bm = 0u;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bm = max(bm, as_u(v[i]) & 0x7FFFFFFFu);
+      uint32_t bm = abs_max_bits8(v);
       bm = max(bm, dpp_u32<kQuadXor1>(bm));
       const bool nonfinite = bm >= 0x7F800000u;
       const float bamax = as_f(bm);
@@ -287,11 +285,12 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       }
       if constexpr (POL == kPolIf4) {
         uint32_t sati;
-        const uint32_t mi = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati);
+        float kf[8];
+        const uint32_t mi = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati, kf);
         const uint32_t ci = mi | (codes & 0x88888888u);   // the signs of the FP4 codes
         // (as for Four Over Six: the FMA sums where they can decide)
         const float hf = e4m3_value(c6) * cx.g, h7 = s_dq[8 * c6 + 1];
-        float ff = half_sse_fma(v, codes, hf), fi = half_sse_int4_fma(v, mi, h7);
+        float ff = half_sse_fma(v, codes, hf), fi = half_sse_int4_fma(v, kf, h7);
         {
           const float pf = dpp_xor1_f(ff), pi = dpp_xor1_f(fi);
           ff = odd ? (pf + ff) : (ff + pf);

@@ -488,25 +488,35 @@ __device__ __forceinline__ void if4_fill_tables(float* s_i4, float* s_dq, const 
 // (7 |x| and (2k + 1) 3 s have at most 27 and 10 significant bits), and
 // q > 7 is |x| > 6 s g, an exact fp32 FMA sign.  g < 2^-100 takes
 // correctly rounded fp64 quotients, which decide exactly.
+// kf (optional): the magnitudes k as floats, for the caller's SSE.
 template <bool COUNT>
 __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c, const NvCtx& cx,
-                                                   const float* s_i4, uint32_t& satmask) {
+                                                   const float* s_i4, uint32_t& satmask, float* kf = nullptr) {
   uint32_t codes = 0u, sat = 0u;
   const float sd = e4m3_value(c);
   if (!cx.exact_all) {
     const float m = s_i4[c];
+    // the largest |a - r| over the lane decides "unsure" once (a compare per
+    // element would accumulate in scalar registers)
+    float dmax = 0.0f;
     bool unsure = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a = fabsf(v[i]) * m;
-      const float r = rintf(a);
-      unsure |= fabsf(a - r) > 0.5f - 0x1p-19f;
-      codes |= (uint32_t)fminf(r, 7.0f) << (4 * i);
+    for (int i = 0; i < 8; i += 2) {
+      const float a0 = fabsf(v[i]) * m, a1 = fabsf(v[i + 1]) * m;
+      const float r0 = rintf(a0), r1 = rintf(a1);
+      dmax = max3_abs(dmax, a0 - r0, a1 - r1);
+      const float k0 = fminf(r0, 7.0f), k1 = fminf(r1, 7.0f);
+      if (kf) {
+        kf[i] = k0;
+        kf[i + 1] = k1;
+      }
+      codes |= ((uint32_t)k0 << (4 * i)) | ((uint32_t)k1 << (4 * i + 4));
       if constexpr (COUNT) {
-        sat |= (a > 7.0f ? 1u : 0u) << i;
-        unsure |= fabsf(a - 7.0f) <= 0x1p-17f;
+        sat |= ((a0 > 7.0f ? 1u : 0u) << i) | ((a1 > 7.0f ? 1u : 0u) << (i + 1));
+        unsure |= fabsf(a0 - 7.0f) <= 0x1p-17f || fabsf(a1 - 7.0f) <= 0x1p-17f;
       }
     }
+    unsure |= dmax > 0.5f - 0x1p-19f;
     if (unsure && c != 0u) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -525,16 +535,23 @@ __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c
         const uint32_t st = fmaf(-(6.0f * sd), cx.g, ax) > 0.0f ? 1u : 0u;
         codes = (codes & ~(7u << (4 * i))) | (k << (4 * i));
         sat = (sat & ~(1u << i)) | (st << i);
+        if (kf) kf[i] = (float)k;
       }
     }
-  } else if (c != 0u) {
-    const double den = 6.0 * (double)sd * cx.g64;
+  } else {
+    if (c != 0u) {
+      const double den = 6.0 * (double)sd * cx.g64;
 #pragma unroll 1
-    for (int i = 0; i < 8; ++i) {
-      const double q = 7.0 * (double)fabsf(v[i]) / den;
-      const uint32_t k = q > 7.0 ? 7u : (uint32_t)rint(q);
-      codes |= k << (4 * i);
-      sat |= (q > 7.0 ? 1u : 0u) << i;
+      for (int i = 0; i < 8; ++i) {
+        const double q = 7.0 * (double)fabsf(v[i]) / den;
+        const uint32_t k = q > 7.0 ? 7u : (uint32_t)rint(q);
+        codes |= k << (4 * i);
+        sat |= (q > 7.0 ? 1u : 0u) << i;
+      }
+    }
+    if (kf) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kf[i] = (float)((codes >> (4 * i)) & 7u);
     }
   }
   satmask = COUNT ? sat : 0u;
@@ -594,15 +611,13 @@ __device__ __forceinline__ float half_sse_fma(const float v[8], uint32_t codes, 
   return acc;
 }
 
-// The same for the INT4 candidate: mags the magnitudes k (nibbles, signs
-// apart), h7 = RN32(6 s g / 7); d' = |x| - k h7.
-__device__ __forceinline__ float half_sse_int4_fma(const float v[8], uint32_t mags, float h7) {
-  const uint32_t ev = mags & 0x0F0F0F0Fu, od = (mags >> 4) & 0x0F0F0F0Fu;   // k of even / odd elements, a byte each
+// The same for the INT4 candidate from its magnitudes k as floats (kf of
+// if4_encode_int4), h7 = RN32(6 s g / 7); d' = |x| - k h7.
+__device__ __forceinline__ float half_sse_int4_fma(const float v[8], const float kf[8], float h7) {
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float k = (float)((((i & 1) ? od : ev) >> (8 * (i >> 1))) & 0xFFu);
-    const float d = fmaf(-k, h7, fabsf(v[i]));
+    const float d = fmaf(-kf[i], h7, fabsf(v[i]));
     acc = fmaf(d, d, acc);
   }
   return acc;
