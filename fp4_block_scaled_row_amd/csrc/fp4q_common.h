@@ -112,6 +112,34 @@ __host__ __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t
   return c;
 }
 
+// The same rounds in a kernel whose key is uniform across the wave (a kernel
+// argument): each round's two three-way XORs (product high word, counter
+// word, key) are one v_bitop3_b32 each (truth table 0x96, the parity of its
+// three inputs) with the key in a scalar register, 4 instead of 6 vector
+// instructions per round (the compiler keeps the key XOR apart).  Same
+// outputs as philox4x32_10.
+__device__ __forceinline__ uint32_t xor3_uniform(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+__device__ __forceinline__ U4 philox4x32_10_uniform_key(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    U4 n;
+    n.x = xor3_uniform((uint32_t)(p1 >> 32), c.y, k0);
+    n.y = (uint32_t)p1;
+    n.z = xor3_uniform((uint32_t)(p0 >> 32), c.w, k1);
+    n.w = (uint32_t)p0;
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
 // Sixteen-bit draw for element (8*g + f) of a Philox output block.
 __device__ __forceinline__ uint32_t draw16(const U4& o, int f) {
   const uint32_t w = (f >> 1) == 0 ? o.x : (f >> 1) == 1 ? o.y : (f >> 1) == 2 ? o.z : o.w;

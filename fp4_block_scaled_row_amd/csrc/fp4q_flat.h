@@ -263,7 +263,7 @@ __device__ __forceinline__ void mx_encode_slot(const float v[8], int64_t s, bool
     codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[6], v[7], sc, 3);
   } else {
     const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
-    const U4 rnd = philox4x32_10(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const U4 rnd = philox4x32_10_uniform_key(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float qv = ldexpf(v[i], -e);

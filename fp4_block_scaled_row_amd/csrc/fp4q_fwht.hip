@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void fwht_lds_kernel(FwhtLaunch f, int lo
   if (f.random_signs) {
     for (int k = tid; k < (t + 127) / 128; k += kThreads) {
       const U4 ctr = {(uint32_t)k, 0u, 1u, 0u};
-      const U4 o = philox4x32_10(ctr, (uint32_t)f.seed, (uint32_t)(f.seed >> 32));
+      const U4 o = philox4x32_10_uniform_key(ctr, (uint32_t)f.seed, (uint32_t)(f.seed >> 32));
       sgn[4 * k] = o.x; sgn[4 * k + 1] = o.y; sgn[4 * k + 2] = o.z; sgn[4 * k + 3] = o.w;
     }
   }

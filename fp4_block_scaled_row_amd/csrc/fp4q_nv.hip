@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       U4 rnd = {0u, 0u, 0u, 0u};
       if constexpr (SR) {
         const U4 ctr = {(uint32_t)s, (uint32_t)((uint64_t)s >> 32), 0u, 0u};
-        rnd = philox4x32_10(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
+        rnd = philox4x32_10_uniform_key(ctr, (uint32_t)q.seed, (uint32_t)(q.seed >> 32));
       }
       const uint32_t c6 = nonfinite ? 0u : nv_scale_code(bamax, cx.inv6_lo, cx.inv6_hi, cx.inv6, cx.mg6, cx.exact_all, 6.0f, cx.g);
       uint32_t sat6;
