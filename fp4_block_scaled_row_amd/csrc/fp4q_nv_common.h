@@ -510,7 +510,9 @@ __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c
         kf[i] = k0;
         kf[i + 1] = k1;
       }
-      codes |= ((uint32_t)k0 << (4 * i)) | ((uint32_t)k1 << (4 * i + 4));
+      // byte i/2 = k0 + 16 k1 (exact small integers), one conversion per pair;
+      // the first one's old operand is a dead value (the others overwrite it)
+      codes = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(k1, 16.0f, k0), i >> 1, i == 0 ? as_u(k0) : codes);
       if constexpr (COUNT) {
         sat |= ((a0 > 7.0f ? 1u : 0u) << i) | ((a1 > 7.0f ? 1u : 0u) << (i + 1));
         unsure |= fabsf(a0 - 7.0f) <= 0x1p-17f || fabsf(a1 - 7.0f) <= 0x1p-17f;
