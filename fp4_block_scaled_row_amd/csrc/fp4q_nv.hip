@@ -199,10 +199,17 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   // tiles per iteration so its loads and its code/scale stores are contiguous
   for (int64_t grp = wave; grp * kUnroll < ntiles; grp += nwaves) {
     SlotRaw<IN> raw[kUnroll];
+    // (every slot of the group present, the common case: loads without a
+    // branch, so that the first tile waits for its own load only)
+    if (((grp + 1) * kUnroll << 6) <= q.nslots) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((grp * kUnroll + u) << 6) + lane;
-      load_slot<IN, CONTIG, true>(q, s, s < q.nslots, raw[u]);
+      for (int u = 0; u < kUnroll; ++u) load_slot<IN, CONTIG, true>(q, ((grp * kUnroll + u) << 6) + lane, true, raw[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t s = ((grp * kUnroll + u) << 6) + lane;
+        load_slot<IN, CONTIG, true>(q, s, s < q.nslots, raw[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
