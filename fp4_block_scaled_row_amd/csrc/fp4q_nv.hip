@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
       }
       if (active) {
         __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(q.codes + (f >> 1)));
-        if (!odd) q.scales[f >> 4] = (uint8_t)sbyte;
+        if (!odd) __builtin_nontemporal_store((uint8_t)sbyte, q.scales + (f >> 4));
         if constexpr (ROT != kRotNone) {
           if (q.rotated) store_rotated(q.rotated, s, v);
         }
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void nv_fast_kernel(QuantLaunch q, int np
         if (s1 < q.nslots) __builtin_nontemporal_store(c1, reinterpret_cast<uint32_t*>(q.codes) + s1);
         // the block this lane worked out: tile t0 + 2p + odd, block lane / 2
         const int64_t tb = t0 + 2 * p + (odd ? 1 : 0);
-        if ((tb << 6) + (lane & ~1) < q.nslots) q.scales[(tb << 5) + (lane >> 1)] = (uint8_t)sc;
+        if ((tb << 6) + (lane & ~1) < q.nslots) __builtin_nontemporal_store((uint8_t)sc, q.scales + (tb << 5) + (lane >> 1));
         mine |= (nd >> 31) << (2 * p);
       }
       // slot r of a lane belongs to the block its pair worked out in the even
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void nv_fos_fast_kernel(QuantLaunch q, in
       if (s0 < q.nslots) __builtin_nontemporal_store(ca, reinterpret_cast<uint32_t*>(q.codes) + s0);
       if (s1 < q.nslots) __builtin_nontemporal_store(cb, reinterpret_cast<uint32_t*>(q.codes) + s1);
       const int64_t tb = ta + (odd ? 1 : 0);             // the block this lane worked out: tile tb, block lane / 2
-      if ((tb << 6) + (lane & ~1) < q.nslots) q.scales[(tb << 5) + (lane >> 1)] = (uint8_t)sbyte;
+      if ((tb << 6) + (lane & ~1) < q.nslots) __builtin_nontemporal_store((uint8_t)sbyte, q.scales + (tb << 5) + (lane >> 1));
       // choice bits of tiles ta and ta + 1: block k of a tile is bit k of its 32-bit word
       const uint64_t bal = __ballot(odd ? pb : pa);
       if (lane == 0) {

@@ -683,7 +683,7 @@ __device__ __forceinline__ void nv_fix_slot_fma(const QuantLaunch& q, const NvCt
     scale = c;
   }
   __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(q.codes + (s << 2)));   // as the fast path
-  q.scales[s >> 1] = (uint8_t)scale;
+  __builtin_nontemporal_store((uint8_t)scale, q.scales + (s >> 1));   // as the fast paths
 }
 
 // Largest bf16 magnitude bit pattern of the 8 values of a raw slot (sign
