@@ -65,8 +65,10 @@ __device__ __forceinline__ void load_unscaled(const QuantLaunch& q, const SlotRa
 // The maxima are float maxima of absolute values (two values per
 // instruction), which pass over NaNs; a wave whose maximum comes out infinite
 // scans its slots again with the scaled values, filtering each one.
+// stream: non-temporal loads, for tensors too large to stay in the Infinity
+// Cache until pass 2 (otherwise the loads keep them there for pass 2).
 template <int IN, int ROT, bool CONTIG>
-__global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
+__global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q, bool stream) {
   __shared__ uint32_t s_red[kWaves];
   constexpr bool kRot = ROT != kRotNone;
   const int lane = threadIdx.x & 63;
@@ -77,10 +79,18 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(QuantLaunch q) {
   float mrot = 0.0f;  // rotated: the running max of |y| before the scale
   for (int64_t g = wave; g * kUnroll < ntiles; g += nwaves) {
     SlotRaw<IN> raw[kUnroll];
+    if (stream) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t s = ((g * kUnroll + u) << 6) + lane;
-      load_slot<IN, CONTIG, false>(q, s, s < q.nslots, raw[u]);   // kept in the caches for pass 2
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t s = ((g * kUnroll + u) << 6) + lane;
+        load_slot<IN, CONTIG, true>(q, s, s < q.nslots, raw[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t s = ((g * kUnroll + u) << 6) + lane;
+        load_slot<IN, CONTIG, false>(q, s, s < q.nslots, raw[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -694,7 +704,12 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   int np = 0;
   if (!q.global_amax) {
     np = amax_grid(q.nslots);
-    hipLaunchKernelGGL((nv_amax_kernel<IN, ROT, CONTIG>), dim3(np), dim3(kThreads), 0, st, q);
+    // (measured: cached loads for the 134 MB 8192^2 bf16 tensors, whose pass 2
+    // then finds them in the 256 MB Infinity Cache; non-temporal for the 470 MB
+    // 8192 x 28672 weight, C4 ~210 -> ~205 us)
+    const int64_t in_bytes = q.nslots * (IN == kF32 ? 32 : 16);
+    const bool stream = in_bytes > ((int64_t)192 << 20);
+    hipLaunchKernelGGL((nv_amax_kernel<IN, ROT, CONTIG>), dim3(np), dim3(kThreads), 0, st, q, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
