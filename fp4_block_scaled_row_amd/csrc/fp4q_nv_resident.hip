@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kResThreads, kResPerCu) void nv_resident_kernel(Qua
     for (int i = tid; i < G; i += kResThreads) {
       uint64_t f = 0;
       // (the master polls briskly: its wait is the critical path)
-      if (!wait_epoch<2>(flags + i, epoch, hdr + 2, f)) s_timeout = 1u;
+      if (!wait_epoch<1>(flags + i, epoch, hdr + 2, f)) s_timeout = 1u;
       m = max(m, (uint32_t)f);
     }
     m = wave_max_u32(m);
