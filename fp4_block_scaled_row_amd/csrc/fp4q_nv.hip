@@ -719,7 +719,7 @@ hipError_t launch_t(const QuantLaunch& q, hipStream_t st) {
   }
   const int64_t ntiles = (q.nslots + 63) >> 6;
   const int64_t want = (ntiles + kWaves * kUnroll - 1) / (kWaves * kUnroll);
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t cap = (int64_t)device_cu_count() * 16;   // (measured: 16 per CU against 4, 8, 32, 64)
   const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
   if constexpr (IN == kBF16 && ROT == kRotNone && !SR && POL == kPolMax6 && !COUNT && CONTIG) {
     static_assert(kUnroll == 4, "nv_fast_kernel takes four tiles per wave iteration");
