@@ -405,14 +405,24 @@ __global__ __launch_bounds__(kThreads) void nv_fast_kernel(QuantLaunch q, int np
   for (int64_t grp = wave; grp * 4 < ntiles; grp += nwaves) {
     const int64_t t0 = grp * 4;
     uint4 w[4];
+    // (every slot of the four tiles present, the common case: loads without a
+    // branch, so that the first pair waits for its own loads only)
+    if (((t0 + 4) << 6) <= q.nslots) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t s = ((t0 + r) << 6) + lane;
-      if (s < q.nslots) {
-        const u32x4_t a = load16<true>(xs + (s << 3));
+      for (int r = 0; r < 4; ++r) {
+        const u32x4_t a = load16<true>(xs + ((((t0 + r) << 6) + lane) << 3));
         w[r] = make_uint4(a.x, a.y, a.z, a.w);
-      } else {
-        w[r] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t s = ((t0 + r) << 6) + lane;
+        if (s < q.nslots) {
+          const u32x4_t a = load16<true>(xs + (s << 3));
+          w[r] = make_uint4(a.x, a.y, a.z, a.w);
+        } else {
+          w[r] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
     uint32_t redo = 0u;   // bit r: this lane's slot in tile t0 + r is redone
@@ -565,14 +575,23 @@ __global__ __launch_bounds__(kThreads) void nv_fos_fast_kernel(QuantLaunch q, in
   for (int64_t grp = wave; grp * 4 < ntiles; grp += nwaves) {
     const int64_t t0 = grp * 4;
     uint4 w[4];
+    // (as nv_fast_kernel: unconditional loads of a group of full tiles)
+    if (((t0 + 4) << 6) <= q.nslots) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t s = ((t0 + r) << 6) + lane;
-      if (s < q.nslots) {
-        const u32x4_t a = load16<true>(xs + (s << 3));
+      for (int r = 0; r < 4; ++r) {
+        const u32x4_t a = load16<true>(xs + ((((t0 + r) << 6) + lane) << 3));
         w[r] = make_uint4(a.x, a.y, a.z, a.w);
-      } else {
-        w[r] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t s = ((t0 + r) << 6) + lane;
+        if (s < q.nslots) {
+          const u32x4_t a = load16<true>(xs + (s << 3));
+          w[r] = make_uint4(a.x, a.y, a.z, a.w);
+        } else {
+          w[r] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
 #pragma unroll
