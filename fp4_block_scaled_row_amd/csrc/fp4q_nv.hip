@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   __shared__ float2 s_adj[kAdj ? 128 : 1];
   __shared__ float4 s_eps[8];
   __shared__ float s_i4[POL == kPolIf4 ? 128 : 1];
-  __shared__ float s_dq[POL == kPolIf4 ? 1024 : 1];
+  __shared__ float s_h7[POL == kPolIf4 ? 128 : 1];
   __shared__ uint32_t s_red[kWaves];
   const int lane = threadIdx.x & 63;
 
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
   nv_context(as_f(amax_bits), FOS, cx);
   if constexpr (kAdj) nv_fill_adjusted_table(s_adj, s_inv, s_eps, cx, threadIdx.x);
   else nv_fill_inverse_table(s_inv, cx, threadIdx.x, kThreads);
-  if constexpr (POL == kPolIf4) if4_fill_tables(s_i4, s_dq, cx, threadIdx.x, kThreads);
+  if constexpr (POL == kPolIf4) if4_fill_tables(s_i4, s_h7, cx, threadIdx.x, kThreads);
   if (blockIdx.x == 0 && threadIdx.x == 0 && q.global_scale) *q.global_scale = cx.g;
   __syncthreads();
 
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         const uint32_t mi = if4_encode_int4<COUNT>(v, c6, cx, s_i4, sati, kf);
         const uint32_t ci = mi | (codes & 0x88888888u);   // the signs of the FP4 codes
         // (as for Four Over Six: the FMA sums where they can decide)
-        const float hf = e4m3_value(c6) * cx.g, h7 = s_dq[8 * c6 + 1];
+        const float hf = e4m3_value(c6) * cx.g, h7 = s_h7[c6];
         float ff = half_sse_fma(v, codes, hf), fi = half_sse_int4_fma(v, kf, h7);
         {
           const float pf = dpp_xor1_f(ff), pi = dpp_xor1_f(fi);
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(QuantLaunch q, int n
         int dec = sse_decide(ff, fi, sse_bound(ff, 6.0f * hf), sse_bound(fi, 7.0f * h7));
         if (dec < 0 && !nonfinite) {
           float ef = half_sse(v, codes, c6, cx.g);
-          float ei = half_sse_int4(v, mi, s_dq + 8 * c6);
+          float ei = half_sse_int4(v, mi, c6, cx.g64);
           const float pf = dpp_xor1_f(ef), pi = dpp_xor1_f(ei);
           ef = odd ? (pf + ef) : (ef + pf);   // S_lo + S_hi on both lanes
           ei = odd ? (pi + ei) : (ei + pi);

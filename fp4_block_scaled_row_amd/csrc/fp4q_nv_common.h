@@ -464,16 +464,20 @@ __device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint
 // scale byte.  Nibbles are sign-magnitude like E2M1 codes.
 
 // s_i4[c] = RN32(7 / (6 s_c g)) (0 for c = 0; unused when exact_all),
-// s_dq[8 c + k] = RN32(k * 6 s_c g / 7): k * 6 * s_c * g is exact
+// if4_dq(k, c) = RN32(k * 6 s_c g / 7): k * 6 * s_c * g is exact
 // in fp64 (at most 33 significant bits) and the fp64 quotient is never
 // within 2^-33 (relatively) of an fp32 rounding boundary unless the exact
 // value lies on it, so converting it gives the single rounding.
-__device__ __forceinline__ void if4_fill_tables(float* s_i4, float* s_dq, const NvCtx& cx, int tid, int nthreads) {
-  for (int e = tid; e < 128 * 8; e += nthreads) {
-    const int c = e >> 3, k = e & 7;
+// s_h7[c] = if4_dq(1, c), the step of the INT4 grid, for every code; the
+// other multiples are computed where the rare frozen-order SSE needs them.
+__device__ __forceinline__ float if4_dq(uint32_t k, uint32_t c, double g64) {
+  return (float)((double)k * 6.0 * (double)e4m3_value(c) * g64 / 7.0);
+}
+__device__ __forceinline__ void if4_fill_tables(float* s_i4, float* s_h7, const NvCtx& cx, int tid, int nthreads) {
+  for (int c = tid; c < 128; c += nthreads) {
     const double sd = (double)e4m3_value((uint32_t)c);
-    s_dq[e] = (float)((double)k * 6.0 * sd * cx.g64 / 7.0);
-    if (k == 0) s_i4[c] = (c != 0 && c != 127 && !cx.exact_all) ? (float)(7.0 / (6.0 * sd * cx.g64)) : 0.0f;
+    s_h7[c] = if4_dq(1u, (uint32_t)c, cx.g64);
+    s_i4[c] = (c != 0 && c != 127 && !cx.exact_all) ? (float)(7.0 / (6.0 * sd * cx.g64)) : 0.0f;
   }
 }
 
@@ -561,15 +565,15 @@ __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c
 }
 
 // Half of the INT4 candidate's block SSE in the order of half_sse, with
-// dq = +-s_dq[8 c + k] (dq_row = s_dq + 8 c) of the element's sign, so that
-// d = x - dq is +-(|x| - s_dq[8 c + k]) and its square that of |x| - s_dq[..]
-// (mags: the magnitudes of if4_encode_int4).
-__device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t mags, const float* dq_row) {
+// dq = +-if4_dq(k, c) of the element's sign, so that d = x - dq is
+// +-(|x| - if4_dq(k, c)) and its square that of |x| - if4_dq(k, c) (mags: the
+// magnitudes of if4_encode_int4).
+__device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t mags, uint32_t c, double g64) {
 #pragma clang fp contract(off)
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float d = fabsf(v[i]) - dq_row[(mags >> (4 * i)) & 7u];
+    const float d = fabsf(v[i]) - if4_dq((mags >> (4 * i)) & 7u, c, g64);
     const float sq = d * d;
     acc = acc + sq;
   }
