@@ -470,8 +470,23 @@ __device__ __forceinline__ float half_sse(const float v[8], uint32_t codes, uint
 // value lies on it, so converting it gives the single rounding.
 // s_h7[c] = if4_dq(1, c), the step of the INT4 grid, for every code; the
 // other multiples are computed where the rare frozen-order SSE needs them.
+//
+// The fp64 quotient by 7 takes a product and two FMAs instead of a division:
+// q0 = RN(x y) with y = RN(1/7), the remainder r = x - 7 q0 (exact), then
+// RN(q0 + r y), which is Markstein's correction and gives RN(x / 7); checked
+// against the division for every integer x of 33 significant bits, which
+// covers every k * 6 s_c g here up to a power of two.  A non-finite x (an
+// infinite g) is passed through as the division would.
+__device__ __forceinline__ float if4_div7(double x) {
+  constexpr double y = 1.0 / 7.0;
+  const double q0 = x * y;
+  const double q1 = __builtin_fma(__builtin_fma(-q0, 7.0, x), y, q0);
+  return (float)(__builtin_isfinite(x) ? q1 : x);
+}
+// p6 = 6 s_c g (exact in fp64: at most 30 significant bits)
+__device__ __forceinline__ double if4_p6(uint32_t c, double g64) { return 6.0 * (double)e4m3_value(c) * g64; }
 __device__ __forceinline__ float if4_dq(uint32_t k, uint32_t c, double g64) {
-  return (float)((double)k * 6.0 * (double)e4m3_value(c) * g64 / 7.0);
+  return if4_div7((double)k * if4_p6(c, g64));
 }
 __device__ __forceinline__ void if4_fill_tables(float* s_i4, float* s_h7, const NvCtx& cx, int tid, int nthreads) {
   for (int c = tid; c < 128; c += nthreads) {
@@ -570,10 +585,11 @@ __device__ __forceinline__ uint32_t if4_encode_int4(const float v[8], uint32_t c
 // magnitudes of if4_encode_int4).
 __device__ __forceinline__ float half_sse_int4(const float v[8], uint32_t mags, uint32_t c, double g64) {
 #pragma clang fp contract(off)
+  const double p6 = if4_p6(c, g64);
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float d = fabsf(v[i]) - if4_dq((mags >> (4 * i)) & 7u, c, g64);
+    const float d = fabsf(v[i]) - if4_div7((double)((mags >> (4 * i)) & 7u) * p6);
     const float sq = d * d;
     acc = acc + sq;
   }
